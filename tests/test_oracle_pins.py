@@ -1,0 +1,423 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test checks one step (or the whole head) against a library routine that
+implements the same textbook operation independently (PyTorch fp64 modules,
+SciPy), a closed form, an invariant the pages fix, or the brute-force scalar
+evaluator on tiny inputs.  A plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand) fails at least one of them.
+"""
+import copy
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from conftest import table_reader, tiny_spec
+from oracle import head as O
+from structured_decision_head_amd import synth
+from brute import brute_record
+
+torch.set_default_dtype(torch.float64)
+
+
+def _rng(s=0):
+    return np.random.default_rng(s)
+
+
+# ----------------------------------------------------------------------------
+# elementary steps vs library routines / closed forms
+# ----------------------------------------------------------------------------
+def test_layer_norm_matches_torch():
+    r = _rng(1)
+    x = r.standard_normal((7, 96)) * 3 + 1.5
+    w, b = r.standard_normal(96), r.standard_normal(96)
+    ref = torch.nn.functional.layer_norm(torch.tensor(x), (96,), torch.tensor(w), torch.tensor(b), 1e-5)
+    np.testing.assert_allclose(O.layer_norm(x, w, b, 1e-5), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_layer_norm_closed_form():
+    # gamma = 1, beta = 0: every row has mean 0 and variance var / (var + eps).
+    r = _rng(2)
+    x = r.standard_normal((5, 64)) * np.array([[0.01], [0.1], [1.0], [10.0], [100.0]]) - 3.0
+    y = O.layer_norm(x, np.ones(64), np.zeros(64), 1e-5)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-10)
+
+
+def test_gelu_matches_torch_exact_erf():
+    x = np.linspace(-8, 8, 1001)
+    ref = torch.nn.functional.gelu(torch.tensor(x), approximate="none").numpy()
+    np.testing.assert_allclose(O.gelu(x), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_cosine_closed_forms_and_torch():
+    r = _rng(3)
+    a = r.standard_normal(50)
+    assert abs(O.cosine(a, 2.5 * a) - 1.0) < 1e-14
+    assert abs(O.cosine(a, -0.3 * a) + 1.0) < 1e-14
+    b = r.standard_normal(50)
+    b -= (a @ b) / (a @ a) * a
+    assert abs(O.cosine(a, b)) < 1e-13
+    A, Bm = r.standard_normal((9, 33)), r.standard_normal((9, 33))
+    ref = torch.nn.functional.cosine_similarity(torch.tensor(A), torch.tensor(Bm), dim=-1).numpy()
+    np.testing.assert_allclose(O.cosine(A, Bm), ref, rtol=1e-13)
+    # the zero vector is clamped, not divided by
+    assert O.cosine(np.zeros(5), np.ones(5)) == 0.0
+
+
+def test_softmax_matches_scipy():
+    s = _rng(4).standard_normal((3, 11)) * 20
+    np.testing.assert_allclose(O.softmax(s), scipy.special.softmax(s, axis=-1), rtol=1e-13)
+
+
+def _attn_params(r, D, F, prefix):
+    p = {}
+    for m in ("q", "k", "v", "o"):
+        p[f"{prefix}.{m}.w"] = r.standard_normal((D, D)) / math.sqrt(D)
+        p[f"{prefix}.{m}.b"] = r.standard_normal(D) / math.sqrt(D)
+    p[f"{prefix}.ln1.w"] = 1 + 0.1 * r.standard_normal(D)
+    p[f"{prefix}.ln1.b"] = 0.1 * r.standard_normal(D)
+    p[f"{prefix}.ln2.w"] = 1 + 0.1 * r.standard_normal(D)
+    p[f"{prefix}.ln2.b"] = 0.1 * r.standard_normal(D)
+    p[f"{prefix}.ffn1.w"] = r.standard_normal((F, D)) / math.sqrt(D)
+    p[f"{prefix}.ffn1.b"] = r.standard_normal(F) / math.sqrt(D)
+    p[f"{prefix}.ffn2.w"] = r.standard_normal((D, F)) / math.sqrt(F)
+    p[f"{prefix}.ffn2.b"] = r.standard_normal(D) / math.sqrt(F)
+    return p
+
+
+def _torch_mha(p, prefix, D, heads):
+    m = torch.nn.MultiheadAttention(D, heads, bias=True, batch_first=True)
+    with torch.no_grad():
+        m.in_proj_weight.copy_(torch.tensor(np.concatenate([p[f"{prefix}.{x}.w"] for x in "qkv"])))
+        m.in_proj_bias.copy_(torch.tensor(np.concatenate([p[f"{prefix}.{x}.b"] for x in "qkv"])))
+        m.out_proj.weight.copy_(torch.tensor(p[f"{prefix}.o.w"]))
+        m.out_proj.bias.copy_(torch.tensor(p[f"{prefix}.o.b"]))
+    return m
+
+
+def _torch_ln(p, key, D, eps):
+    ln = torch.nn.LayerNorm(D, eps=eps)
+    with torch.no_grad():
+        ln.weight.copy_(torch.tensor(p[key + ".w"]))
+        ln.bias.copy_(torch.tensor(p[key + ".b"]))
+    return ln
+
+
+def _torch_ffn(p, prefix, D, F):
+    l1, l2 = torch.nn.Linear(D, F), torch.nn.Linear(F, D)
+    with torch.no_grad():
+        l1.weight.copy_(torch.tensor(p[prefix + ".ffn1.w"]))
+        l1.bias.copy_(torch.tensor(p[prefix + ".ffn1.b"]))
+        l2.weight.copy_(torch.tensor(p[prefix + ".ffn2.w"]))
+        l2.bias.copy_(torch.tensor(p[prefix + ".ffn2.b"]))
+    return torch.nn.Sequential(l1, torch.nn.GELU(approximate="none"), l2)
+
+
+@pytest.mark.parametrize("n_mem,n_q", [(1, 3), (37, 5), (200, 1)])
+def test_routing_layer_matches_torch_modules(n_mem, n_q):
+    """Cross-attention + FFN, both pre-LN residual, vs torch.nn.MultiheadAttention,
+    LayerNorm, Linear and GELU in fp64; padding keys masked on the torch side."""
+    D, F, heads, eps = 64, 96, 4, 1e-5
+    r = _rng(10 + n_mem)
+    p = _attn_params(r, D, F, "route.0")
+    u = r.standard_normal((n_q, D))
+    mem = r.standard_normal((n_mem, D))
+    got = O.routing_layer(u, mem, p, "route.0", heads, eps)
+
+    pad = np.concatenate([mem, np.full((5, D), 1e3)], axis=0)          # extra masked keys
+    mask = torch.tensor([[False] * n_mem + [True] * 5])
+    mha, ln1, ln2 = _torch_mha(p, "route.0", D, heads), _torch_ln(p, "route.0.ln1", D, eps), \
+        _torch_ln(p, "route.0.ln2", D, eps)
+    ff = _torch_ffn(p, "route.0", D, F)
+    with torch.no_grad():
+        x = torch.tensor(u)[None]
+        a, _ = mha(ln1(x), torch.tensor(pad)[None], torch.tensor(pad)[None], key_padding_mask=mask,
+                   need_weights=False)
+        x = x + a
+        x = x + ff(ln2(x))
+    np.testing.assert_allclose(got, x[0].numpy(), rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("nf", [1, 4, 9])
+def test_field_layer_matches_transformer_encoder_layer(nf):
+    """Pre-LN self-attention + GELU FFN vs torch.nn.TransformerEncoderLayer(norm_first)."""
+    D, F, heads, eps = 64, 128, 4, 1e-5
+    r = _rng(20 + nf)
+    p = _attn_params(r, D, F, "field.0")
+    f = r.standard_normal((nf, D)) * 2
+    got = O.field_layer(f, p, "field.0", heads, eps)
+    layer = torch.nn.TransformerEncoderLayer(D, heads, F, dropout=0.0, activation="gelu",
+                                             layer_norm_eps=eps, batch_first=True, norm_first=True)
+    layer.train()   # dropout is 0; keeps the plain (non fused) path
+    with torch.no_grad():
+        sa = layer.self_attn
+        sa.in_proj_weight.copy_(torch.tensor(np.concatenate([p[f"field.0.{x}.w"] for x in "qkv"])))
+        sa.in_proj_bias.copy_(torch.tensor(np.concatenate([p[f"field.0.{x}.b"] for x in "qkv"])))
+        sa.out_proj.weight.copy_(torch.tensor(p["field.0.o.w"]))
+        sa.out_proj.bias.copy_(torch.tensor(p["field.0.o.b"]))
+        layer.linear1.weight.copy_(torch.tensor(p["field.0.ffn1.w"]))
+        layer.linear1.bias.copy_(torch.tensor(p["field.0.ffn1.b"]))
+        layer.linear2.weight.copy_(torch.tensor(p["field.0.ffn2.w"]))
+        layer.linear2.bias.copy_(torch.tensor(p["field.0.ffn2.b"]))
+        for i in (1, 2):
+            ln = getattr(layer, f"norm{i}")
+            ln.weight.copy_(torch.tensor(p[f"field.0.ln{i}.w"]))
+            ln.bias.copy_(torch.tensor(p[f"field.0.ln{i}.b"]))
+        ref = layer(torch.tensor(f)[None])[0].numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_attention_single_key_returns_projected_value():
+    # One memory row: every query gets W_O (W_V m + b_V) + b_O, whatever Q is.
+    D, heads = 32, 4
+    r = _rng(30)
+    p = _attn_params(r, D, 16, "x")
+    m = r.standard_normal((1, D))
+    q = r.standard_normal((6, D)) * 10
+    out = O.attention(q, m, p, "x", heads)
+    want = (m @ p["x.v.w"].T + p["x.v.b"]) @ p["x.o.w"].T + p["x.o.b"]
+    np.testing.assert_allclose(out, np.repeat(want, 6, axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_identical_keys_give_mean_free_value():
+    # Identical memory rows: attention weights are uniform, output = that row's value.
+    D, heads = 32, 4
+    r = _rng(31)
+    p = _attn_params(r, D, 16, "x")
+    m = np.repeat(r.standard_normal((1, D)), 9, axis=0)
+    out = O.attention(r.standard_normal((3, D)), m, p, "x", heads)
+    want = (m[:1] @ p["x.v.w"].T + p["x.v.b"]) @ p["x.o.w"].T + p["x.o.b"]
+    np.testing.assert_allclose(out, np.repeat(want, 3, axis=0), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# whole head
+# ----------------------------------------------------------------------------
+def _run(case, records=None):
+    return O.forward(case.weights, case.head, case.batch, table_reader(case), records=records)
+
+
+def _brute(case):
+    b = case.batch
+    ido = b.o_id_offsets()
+    L, P, A = [], [], []
+    for r in range(b.B):
+        n = int(b.lengths[r])
+        q0, q1 = int(b.q_offsets[r]), int(b.q_offsets[r + 1])
+        o0, o1 = int(b.o_offsets[q0]), int(b.o_offsets[q1])
+        rows = [case.table[b.o_ids[ido[k]: ido[k + 1]]] for k in range(o0, o1)]
+        lg, pr, am = brute_record(case.weights, case.head, b.hidden[r, :n], b.q_type[q0:q1],
+                                  b.q_span[q0:q1], b.o_offsets[q0: q1 + 1] - o0, b.o_span[o0:o1], rows)
+        L += lg
+        P += pr
+        A += am
+    return np.array(L), np.array(P), np.array(A)
+
+
+@pytest.mark.parametrize("seed,ln_random", [(7, False), (8, True), (9, True)])
+def test_oracle_matches_brute_force(seed, ln_random):
+    case = synth.make_case(tiny_spec(seed=seed, ln_random=ln_random))
+    lo, po, ao = _run(case)
+    lb, pb, ab = _brute(case)
+    np.testing.assert_allclose(lo, lb, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(po, pb, rtol=1e-10, atol=1e-12)
+    assert (ao == ab).all()
+
+
+def test_softmax_per_question_sums_to_one(tiny_case):
+    lg, pr, am = _run(tiny_case)
+    oo = tiny_case.batch.o_offsets
+    for i in range(len(oo) - 1):
+        seg = pr[oo[i]: oo[i + 1]]
+        assert abs(seg.sum() - 1.0) < 1e-12
+        assert (seg > 0).all() and (seg < 1).all()
+        np.testing.assert_allclose(seg, scipy.special.softmax(lg[oo[i]: oo[i + 1]]), rtol=1e-12)
+        assert am[i] == int(np.argmax(seg))
+
+
+def test_gate_zero_gives_lexical_prior_exactly():
+    """sigmoid(-inf) = 0, so logits equal the prior; the prior is recomputed here
+    with torch ops: layer_norm, span means, table-row means, cosine_similarity."""
+    case = synth.make_case(tiny_spec(seed=11, gate_logit=-math.inf, ln_random=True))
+    lg, _, _ = _run(case)
+    b, H = case.batch, case.head.hidden_size
+    ido = b.o_id_offsets()
+    want = []
+    for r in range(b.B):
+        n = int(b.lengths[r])
+        x = torch.tensor(O.from_bf16(b.hidden[r, :n]))
+        xh = torch.nn.functional.layer_norm(x, (H,), torch.tensor(O.from_bf16(case.weights["ln_in.w"])),
+                                            torch.tensor(O.from_bf16(case.weights["ln_in.b"])), 1e-5)
+        g = xh[n - 1]
+        for q in range(b.q_offsets[r], b.q_offsets[r + 1]):
+            qv = xh[b.q_span[q, 0]: b.q_span[q, 1]].mean(0)
+            for k in range(b.o_offsets[q], b.o_offsets[q + 1]):
+                e = torch.tensor(O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]])).mean(0)
+                want.append(float(torch.nn.functional.cosine_similarity(e, qv + g, dim=0)))
+    np.testing.assert_allclose(lg, want, rtol=1e-12, atol=1e-14)
+    assert (np.abs(lg) <= 1 + 1e-12).all()
+
+
+def test_joint_cosine_in_range_and_mlp_constant_when_w1_zero():
+    case = synth.make_case(tiny_spec(seed=12))
+    w = dict(case.weights)
+    w["score.w1"] = np.zeros_like(w["score.w1"])
+    p = O.load_params(w)
+    b = case.batch
+    ido = b.o_id_offsets()
+    n = int(b.lengths[0])
+    q1 = int(b.q_offsets[1])
+    o1 = int(b.o_offsets[q1])
+    tr = {}
+    O.forward_record(p, case.head, O.from_bf16(b.hidden[0, :n]), b.q_type[:q1], b.q_span[:q1],
+                     b.o_offsets[: q1 + 1], b.o_span[:o1],
+                     [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(o1)], trace=tr)
+    want = O.gelu(p["score.b1"]) @ p["score.w2"] + p["score.b2"][0]
+    np.testing.assert_allclose(tr["mlp"], want, rtol=1e-13)
+    assert (np.abs(tr["joint_cos"]) <= 1 + 1e-12).all()
+
+
+def test_pooling_special_cases(tiny_case):
+    b = tiny_case.batch
+    p = O.load_params(tiny_case.weights)
+    spec = tiny_spec(seed=13, instr_len=(1, 1), opt_len=(1, 1))
+    case = synth.make_case(spec)
+    b = case.batch
+    ido = b.o_id_offsets()
+    n = int(b.lengths[0])
+    q1 = int(b.q_offsets[1])
+    o1 = int(b.o_offsets[q1])
+    tr = {}
+    O.forward_record(O.load_params(case.weights), case.head, O.from_bf16(b.hidden[0, :n]),
+                     b.q_type[:q1], b.q_span[:q1], b.o_offsets[: q1 + 1], b.o_span[:o1],
+                     [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(o1)], trace=tr)
+    # length-1 spans return the LayerNorm-ed row itself; the global vector is the last valid row
+    for i in range(q1):
+        np.testing.assert_array_equal(tr["qbar"][i], tr["xh"][b.q_span[i, 0]])
+    for k in range(o1):
+        np.testing.assert_array_equal(tr["cbar"][k], tr["xh"][b.o_span[k, 0]])
+        np.testing.assert_array_equal(tr["ebar"][k], O.from_bf16(case.table[b.o_ids[ido[k]]]))
+    np.testing.assert_array_equal(tr["g"], tr["xh"][n - 1])
+
+
+def test_lexical_mean_of_repeated_id():
+    case = synth.make_case(tiny_spec(seed=14))
+    b = case.batch
+    b.o_ids[:] = 5
+    _, _, _ = _run(case)
+    p = O.load_params(case.weights)
+    tr = {}
+    n = int(b.lengths[0])
+    q1 = int(b.q_offsets[1])
+    o1 = int(b.o_offsets[q1])
+    ido = b.o_id_offsets()
+    O.forward_record(p, case.head, O.from_bf16(b.hidden[0, :n]), b.q_type[:q1], b.q_span[:q1],
+                     b.o_offsets[: q1 + 1], b.o_span[:o1],
+                     [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(o1)], trace=tr)
+    for k in range(o1):
+        np.testing.assert_allclose(tr["ebar"][k], O.from_bf16(case.table[5]), rtol=1e-15, atol=0)
+
+
+def test_batch_composition_and_padding_invariance():
+    case = synth.make_case(tiny_spec(seed=15, B=3, lengths=(12, 24)))
+    lg, pr, am = _run(case)
+    b = case.batch
+    oo = 0
+    qo = 0
+    for r in range(b.B):
+        sub = copy.copy(case)
+        sub.batch = b.record(r)
+        l1, p1, a1 = _run(sub)
+        np.testing.assert_array_equal(l1, lg[oo: oo + len(l1)])
+        np.testing.assert_array_equal(a1, am[qo: qo + len(a1)])
+        oo += len(l1)
+        qo += len(a1)
+    # NaN-poisoned extra padding changes nothing
+    padded = copy.copy(case)
+    pb = copy.copy(b)
+    pb.hidden = np.concatenate([b.hidden, np.full((b.B, 9, b.H), 0x7FC0, np.uint16)], axis=1)
+    for r in range(b.B):
+        pb.hidden[r, b.lengths[r]:] = 0x7FC0
+    padded.batch = pb
+    l2, p2, a2 = _run(padded)
+    np.testing.assert_array_equal(l2, lg)
+    assert np.isfinite(l2).all()
+
+
+def test_permuting_questions_and_options_permutes_outputs():
+    case = synth.make_case(tiny_spec(seed=16, B=1, lengths=(30, 30), field_range=(3, 3), choice_opts=(3, 3)))
+    lg, pr, am = _run(case)
+    b = case.batch
+    nq = b.NQ
+    ido = b.o_id_offsets()
+    r = _rng(17)
+    qperm = r.permutation(nq)
+    new_qt, new_qs, new_os, new_ids, counts, old_index = [], [], [], [], [], []
+    for q in qperm:
+        new_qt.append(b.q_type[q])
+        new_qs.append(b.q_span[q])
+        o0, o1 = int(b.o_offsets[q]), int(b.o_offsets[q + 1])
+        operm = r.permutation(o1 - o0) + o0
+        counts.append(o1 - o0)
+        for k in operm:
+            new_os.append(b.o_span[k])
+            new_ids.extend(b.o_ids[ido[k]: ido[k + 1]])
+            old_index.append(k)
+    pb = synth.Batch(hidden=b.hidden, lengths=b.lengths, q_offsets=b.q_offsets,
+                     q_type=np.array(new_qt, np.int32), q_span=np.array(new_qs, np.int32),
+                     o_offsets=np.concatenate([[0], np.cumsum(counts)]).astype(np.int32),
+                     o_span=np.array(new_os, np.int32), o_ids=np.array(new_ids, np.int32))
+    case2 = copy.copy(case)
+    case2.batch = pb
+    l2, p2, a2 = _run(case2)
+    np.testing.assert_allclose(l2, lg[old_index], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(p2, pr[old_index], rtol=1e-12, atol=1e-13)
+
+
+def test_argmax_first_index_on_exact_tie():
+    # Two options with the same span and ids have identical priors; with the gate
+    # closed (elementwise arithmetic only) the logits tie exactly and argmax is the first.
+    case = synth.make_case(tiny_spec(seed=18, B=1, lengths=(30, 30), fields="ordered",
+                                     ordered=((synth.CHOICE, 3),), gate_logit=-math.inf))
+    b = case.batch
+    ido = b.o_id_offsets()
+    # make option 2 a copy of option 1
+    b.o_span[2] = b.o_span[1]
+    ids = list(b.o_ids[: ido[2]]) + list(b.o_ids[ido[1]: ido[2]])
+    b.o_ids = np.array(ids, np.int32)
+    lg, pr, am = _run(case)
+    assert lg[1] == lg[2]
+    if lg[1] >= lg[0]:
+        assert am[0] == 1
+    # and with both tied options ahead of the rest
+    b.o_span[0] = b.o_span[1]
+    b.o_ids = np.array(list(b.o_ids[ido[1]: ido[2]]) * 3, np.int32)
+    lg, pr, am = _run(case)
+    assert lg[0] == lg[1] == lg[2] and am[0] == 0
+
+
+def test_single_option_question_summary_is_that_option():
+    case = synth.make_case(tiny_spec(seed=19, B=1, lengths=(30, 30), fields="ordered",
+                                     ordered=((synth.CHOICE, 1), (synth.NOUL, 2))))
+    b = case.batch
+    p = O.load_params(case.weights)
+    ido = b.o_id_offsets()
+    tr = {}
+    n = int(b.lengths[0])
+    lg, pr, am = O.forward_record(p, case.head, O.from_bf16(b.hidden[0, :n]), b.q_type, b.q_span,
+                                  b.o_offsets, b.o_span,
+                                  [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(b.NO)],
+                                  trace=tr)
+    assert pr[0] == 1.0 and am[0] == 0
+    # with zero field layers, f = qv + u + gp + type_emb exactly
+    h0 = synth.replace(case.head, layers=0)
+    tr0 = {}
+    O.forward_record(p, h0, O.from_bf16(b.hidden[0, :n]), b.q_type, b.q_span, b.o_offsets, b.o_span,
+                     [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(b.NO)], trace=tr0)
+    qv = tr0["qbar"][0] @ p["q_base.w"].T + p["q_base.b"]
+    gp = tr0["g"] @ p["glob.w"].T + p["glob.b"]
+    np.testing.assert_allclose(tr0["f"][0], qv + tr0["u"][0] + gp + p["type_emb"][1], rtol=1e-13, atol=1e-14)
