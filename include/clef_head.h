@@ -1,0 +1,187 @@
+/*
+ * libclefhead: JointSchemaHead forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The head turns a decision model's final-norm hidden states into one logit
+ * per option of every schema question, plus a softmax over each question's
+ * options, in one pass with no decoding loop.  Operation as the pages define
+ * it:
+ *   - "Cloudflare 发布 9B 多模态决策模型 Clef-Flash 完整解析" §三: pool the question
+ *     and option spans of the hidden states, route evidence with 2
+ *     cross-attention layers, score every option jointly; §四: logits, then a
+ *     softmax per question.
+ *   - "clef-4bit ... JointSchemaHead" §三 steps 1-4: question vector = mean of
+ *     the instruction span; option context = mean of the option span; option
+ *     lexical vector = mean of lm_head rows over the option's ids; option
+ *     query = sum of three projections; 2 routing layers (cross-attention over
+ *     the whole hidden memory + FFN, residual); field vector = question base +
+ *     option-weighted summary + global (last) vector + type embedding; 4
+ *     transformer layers across fields; logit = prior + gate * (joint_scale *
+ *     cosine + residual MLP over [f, o, f*o, |f-o|]).
+ *   - CoreML conversion metadata of clef-flash, "decision.head": LayerNorm over
+ *     the hidden width into memory, global vector = last token, spans pool the
+ *     LayerNorm-ed rows; "decision.spans": half-open [start, end) spans that
+ *     index the hidden rows; "question_types": noul 0, choice 1, score 2;
+ *     "option_order": noul options are [true, false]; "softmax": per question,
+ *     fp32, temperature 1.
+ *   - Head configuration (architecture page §3.2 table): width 1024, 16 heads,
+ *     routing_layers 2, layers 4, feedforward 4096; hidden_size 4096 (5120 for
+ *     the 27B variant, clef-4bit page §三).
+ *
+ * Conventions.
+ *   - Every entry point returns 0 (CLEF_OK) on success or a negative CLEF_E_*
+ *     code; clef_head_last_error() then holds a message (thread-local).
+ *   - All inputs are validated on the host BEFORE anything is launched; on an
+ *     error no output buffer is written.
+ *   - "HOST" pointers are ordinary CPU memory, read during the call and not
+ *     retained.  "DEVICE" pointers are HIP device memory on the current device.
+ *   - bf16 means IEEE bfloat16 bit patterns (uint16_t storage).
+ *   - No entry point is re-entrant for one handle; distinct handles may be
+ *     used from distinct threads.
+ */
+#ifndef CLEF_HEAD_H
+#define CLEF_HEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CLEF_API __attribute__((visibility("default")))
+
+/* status codes */
+#define CLEF_OK             0
+#define CLEF_E_ARG         -1  /* null pointer, bad config, missing / mis-sized weight */
+#define CLEF_E_LENGTH      -2  /* record length < 1 or > padded length; mask not a prefix mask */
+#define CLEF_E_SPAN        -3  /* empty span, span outside [0, n_b) */
+#define CLEF_E_ID          -4  /* token id outside [0, vocab_size) */
+#define CLEF_E_SCHEMA      -5  /* bad question type, question without options, noul without 2 options */
+#define CLEF_E_NOMEM       -6  /* device or pinned allocation failed */
+#define CLEF_E_HIP         -7  /* HIP runtime error (message in clef_head_last_error) */
+#define CLEF_E_UNSUPPORTED -8  /* configuration outside what the kernels are built for */
+
+/* weight element types */
+#define CLEF_BF16 1
+#define CLEF_F32  2
+
+/* batch layouts */
+#define CLEF_PADDED 0           /* hidden is [B, L, H]; key_mask gives the valid prefix of each row */
+#define CLEF_VARLEN 1           /* hidden is [T, H], records back to back; cu_seqlens gives them */
+
+typedef struct clef_head clef_head;   /* opaque handle */
+
+/* Head hyper-parameters (the keys of joint_head_config.json the pages list).
+ * The kernels are built for width 1024, 16 heads, feedforward 4096,
+ * num_types 3, hidden_size a multiple of 512 up to 8192; routing_layers and
+ * layers may be any count >= 0.  ln_eps is the epsilon of every LayerNorm. */
+typedef struct {
+  int32_t hidden_size, width, heads, routing_layers, layers, feedforward, vocab_size, num_types;
+  float ln_eps;
+} clef_head_config;
+
+/* One named head tensor in host memory.  Linear weights use the [out, in]
+ * layout.  Names (D = width, H = hidden_size, F = feedforward):
+ *   ln_in.{w,b}[H]; {mem,q_base,q_opt,opt_ctx,opt_lex,glob}.w[D,H], .b[D];
+ *   type_emb[num_types,D]; summary.w[D]; summary.b[1];
+ *   for P in route.0..route.{routing_layers-1}, field.0..field.{layers-1}:
+ *     P.ln1.{w,b}[D]; P.{q,k,v,o}.w[D,D], .b[D]; P.ln2.{w,b}[D];
+ *     P.ffn1.w[F,D], .b[F]; P.ffn2.w[D,F], .b[D];
+ *   score.w1[D,4D]; score.b1[D]; score.w2[D]; score.b2[1];
+ *   gate_logit[1] (CLEF_F32); joint_scale[1] (CLEF_F32).
+ * All others are CLEF_BF16.  clef_head_weight_name() enumerates them. */
+typedef struct {
+  const char *name;
+  const void *host_data;
+  int64_t numel;
+  int32_t dtype;
+} clef_head_weight;
+
+/* One batch of encoded records.  Spans are record-relative, half-open
+ * [start, end), and index the same positions as the hidden rows. */
+typedef struct {
+  int32_t layout;              /* CLEF_PADDED | CLEF_VARLEN */
+  int32_t num_records;         /* B >= 1 */
+  int32_t max_len;             /* L (CLEF_PADDED): row stride of hidden in rows */
+  const void *hidden;          /* DEVICE bf16 [B, L, H] (PADDED) or [T, H] (VARLEN); padding rows are never read */
+  const uint8_t *key_mask;     /* HOST [B, L], 1 = valid; each row must be a prefix mask (PADDED) */
+  const int32_t *cu_seqlens;   /* HOST [B+1], cu_seqlens[0] = 0, increasing (VARLEN) */
+  int32_t num_questions;       /* NQ >= 0 */
+  int32_t num_options;         /* NO */
+  const int32_t *q_offsets;    /* HOST [B+1]  records -> questions (CSR) */
+  const int32_t *q_type;       /* HOST [NQ]   0 noul, 1 choice, 2 score */
+  const int32_t *q_span;       /* HOST [NQ,2] instruction span [start, end) */
+  const int32_t *o_offsets;    /* HOST [NQ+1] questions -> options (CSR); option order as in the schema */
+  const int32_t *o_span;       /* HOST [NO,2] option description span [start, end) */
+  const int32_t *o_ids;        /* HOST [sum of option span lengths] token ids of every option span, in order */
+} clef_head_batch;
+
+/* Create a head on the current HIP device.  Weights are copied into
+ * handle-owned device memory (repacked bf16).  lexical_table is the DEVICE
+ * bf16 [vocab_size, hidden_size] untied lm_head.weight; it is borrowed and
+ * must outlive the handle.  On success *out receives the handle. */
+CLEF_API int clef_head_create(const clef_head_config *cfg, const clef_head_weight *weights, int32_t num_weights,
+                     const void *lexical_table, clef_head **out);
+
+/* Forward pass on hip_stream (a hipStream_t, or NULL for the default stream).
+ * Outputs (DEVICE, caller-owned): logits fp32 [NO], probs fp32 [NO] (softmax
+ * over each question's options), argmax int32 [NQ] (index of the first
+ * maximal logit within its question).  The host tables are copied before
+ * the call returns; outputs are ready when the stream reaches them.  The
+ * handle's workspace grows to the largest batch seen. */
+CLEF_API int clef_head_forward(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
+                      int32_t *argmax, void *hip_stream);
+
+/* Release everything the handle owns.  NULL is ignored. */
+CLEF_API void clef_head_destroy(clef_head *h);
+
+/* Message of the last failing call on this thread ("" if none). */
+CLEF_API const char *clef_head_last_error(void);
+
+/* Host-only validation of a batch against a configuration: the same checks
+ * clef_head_forward runs before launching.  Writes the total number of
+ * valid rows T to *num_rows when num_rows is not NULL.  Needs no GPU. */
+CLEF_API int clef_head_check_batch(const clef_head_config *cfg, const clef_head_batch *batch, int64_t *num_rows);
+
+/* Host-only: the pooled row ranges the library derives from a batch.  Writes
+ * int32 [NQ + NO + B][2] half-open ranges in packed row space (record b's
+ * rows start at the sum of the earlier records' lengths): the instruction
+ * span of every question, the description span of every option, then the
+ * global row [n_b - 1, n_b) of every record.  Needs no GPU. */
+CLEF_API int clef_head_span_rows(const clef_head_config *cfg, const clef_head_batch *batch, int32_t *rows);
+
+/* Host-only: number of named tensors the configuration expects, and the
+ * name, element count and dtype of the i-th one. */
+CLEF_API int32_t clef_head_weight_count(const clef_head_config *cfg);
+CLEF_API int clef_head_weight_info(const clef_head_config *cfg, int32_t i, char *name, int32_t name_cap,
+                          int64_t *numel, int32_t *dtype);
+
+/* Debug snapshots of intermediate results of the following forwards.
+ * enable != 0 keeps copies; clef_head_trace() copies one to host memory
+ * after synchronizing the last forward's stream.  Layouts:
+ *   CLEF_TRACE_POOLED  fp32 [NQ + NO + B, H]: question means, option-context means, global rows
+ *   CLEF_TRACE_LEXICAL fp32 [NO, H]           option lexical vectors
+ *   CLEF_TRACE_PRIOR   fp32 [NO]              lexical prior
+ *   CLEF_TRACE_MEMORY  bf16 [sum_b ceil(n_b/256)*256, D]: record b's rows start at
+ *                      the sum of the earlier records' rounded lengths
+ *   CLEF_TRACE_U + r   fp32 [NO, D]           option vectors after r routing layers (r = 0: queries)
+ *   CLEF_TRACE_F0      fp32 [NQ, D]           field vectors before the field layers
+ *   CLEF_TRACE_F       fp32 [NQ, D]           field vectors after the field layers
+ *   CLEF_TRACE_JCOS    fp32 [NO]              joint cosine
+ *   CLEF_TRACE_MLP     fp32 [NO]              residual MLP output
+ * bytes must equal the snapshot's size. */
+#define CLEF_TRACE_POOLED  1
+#define CLEF_TRACE_LEXICAL 2
+#define CLEF_TRACE_PRIOR   3
+#define CLEF_TRACE_MEMORY  4
+#define CLEF_TRACE_F0      5
+#define CLEF_TRACE_F       6
+#define CLEF_TRACE_JCOS    7
+#define CLEF_TRACE_MLP     8
+#define CLEF_TRACE_U       16
+CLEF_API int clef_head_set_trace(clef_head *h, int32_t enable);
+CLEF_API int clef_head_trace(clef_head *h, int32_t which, void *host_dst, int64_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CLEF_HEAD_H */

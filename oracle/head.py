@@ -194,8 +194,10 @@ def forward_record(p: Dict[str, np.ndarray], head, hidden: np.ndarray,
          + linear(qbar[opt_q], p["q_opt.w"], p["q_opt.b"]))
 
     # step 2: evidence routing
+    u_layers = [u]
     for r in range(head.routing_layers):
         u = routing_layer(u, memory, p, f"route.{r}", heads, eps)
+        u_layers.append(u)
 
     # step 3: field vectors, then the field transformer
     qv = linear(qbar, p["q_base.w"], p["q_base.b"])
@@ -206,6 +208,7 @@ def forward_record(p: Dict[str, np.ndarray], head, hidden: np.ndarray,
         o0, o1 = int(o_offsets[i]), int(o_offsets[i + 1])
         beta = softmax(s[o0:o1])
         f[i] = qv[i] + beta @ u[o0:o1] + gp + p["type_emb"][int(q_type[i])]
+    f0 = f.copy()
     for l in range(head.layers):
         f = field_layer(f, p, f"field.{l}", heads, eps)
 
@@ -225,7 +228,7 @@ def forward_record(p: Dict[str, np.ndarray], head, hidden: np.ndarray,
         amax[i] = int(np.argmax(logits[o0:o1]))
     if trace is not None:
         trace.update(xh=xh, memory=memory, qbar=qbar, cbar=cbar, g=g, ebar=ebar, prior=prior,
-                     u=u, f=f, joint_cos=joint_cos, mlp=mlp)
+                     u=u, u_layers=u_layers, f0=f0, f=f, joint_cos=joint_cos, mlp=mlp)
     return logits, probs, amax
 
 

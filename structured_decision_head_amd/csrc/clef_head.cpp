@@ -1,0 +1,923 @@
+// libclefhead host side: the C ABI, input validation, batch planning (packed
+// tables for the kernels), weight repacking, workspace management and the
+// launch sequence of the JointSchemaHead forward pass.
+//
+// Steps (clef-4bit page §三 steps 1-4; CoreML conversion metadata of
+// clef-flash, "decision.head" and "softmax"):
+//   1. LayerNorm statistics of every valid hidden row; span means of the
+//      LayerNorm-ed rows (questions, option contexts) and the last row
+//      (global); lexical gather-mean of lm_head rows and the cosine prior.
+//   2. memory = W_m LayerNorm(hidden) + b_m; per routing layer K, V of memory.
+//   3. option queries u = W_c c + W_l e + W_qo q (+ biases); 2 routing layers
+//      (pre-LN cross-attention over the record's memory + pre-LN GELU FFN).
+//   4. field vectors (question base + option-weighted summary + global +
+//      type embedding); 4 pre-LN self-attention + FFN layers across fields.
+//   5. logits = prior + sigmoid(gate) (joint_scale cos(u, f) + MLP[f, u, f*u,
+//      |f-u|]); softmax and argmax per question.
+#include "clef_head.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace clef;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCHK(x)                                                                              \
+  do {                                                                                         \
+    hipError_t e_ = (x);                                                                       \
+    if (e_ != hipSuccess) return fail(CLEF_E_HIP, "%s failed: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int D = 1024, F = 4096, NH = 16;
+constexpr int TILE = 256;     // row tile of the packed row space
+constexpr int KCH = 256;      // keys per routing-attention chunk
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+float bf16_to_f(uint16_t b) {
+  uint32_t u = uint32_t(b) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+uint16_t f_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// configuration and weight names
+// ---------------------------------------------------------------------------
+struct WSpec {
+  std::string name;
+  int64_t numel;
+  int32_t dtype;
+};
+
+std::vector<WSpec> weight_list(const clef_head_config& c) {
+  const int64_t H = c.hidden_size, d = c.width, f = c.feedforward;
+  std::vector<WSpec> s;
+  auto add = [&](const std::string& n, int64_t numel, int32_t dt = CLEF_BF16) { s.push_back({n, numel, dt}); };
+  add("ln_in.w", H);
+  add("ln_in.b", H);
+  for (const char* n : {"mem", "q_base", "q_opt", "opt_ctx", "opt_lex", "glob"}) {
+    add(std::string(n) + ".w", d * H);
+    add(std::string(n) + ".b", d);
+  }
+  add("type_emb", int64_t(c.num_types) * d);
+  add("summary.w", d);
+  add("summary.b", 1);
+  std::vector<std::string> stacks;
+  for (int r = 0; r < c.routing_layers; ++r) stacks.push_back("route." + std::to_string(r));
+  for (int l = 0; l < c.layers; ++l) stacks.push_back("field." + std::to_string(l));
+  for (auto& p : stacks) {
+    add(p + ".ln1.w", d);
+    add(p + ".ln1.b", d);
+    for (const char* m : {"q", "k", "v", "o"}) {
+      add(p + "." + m + ".w", d * d);
+      add(p + "." + m + ".b", d);
+    }
+    add(p + ".ln2.w", d);
+    add(p + ".ln2.b", d);
+    add(p + ".ffn1.w", f * d);
+    add(p + ".ffn1.b", f);
+    add(p + ".ffn2.w", d * f);
+    add(p + ".ffn2.b", d);
+  }
+  add("score.w1", d * 4 * d);
+  add("score.b1", d);
+  add("score.w2", d);
+  add("score.b2", 1);
+  add("gate_logit", 1, CLEF_F32);
+  add("joint_scale", 1, CLEF_F32);
+  return s;
+}
+
+int check_config(const clef_head_config* c) {
+  if (!c) return fail(CLEF_E_ARG, "config is NULL");
+  if (c->hidden_size <= 0 || c->width <= 0 || c->heads <= 0 || c->feedforward <= 0 || c->vocab_size <= 0 ||
+      c->num_types <= 0 || c->routing_layers < 0 || c->layers < 0 || !(c->ln_eps > 0.f))
+    return fail(CLEF_E_ARG, "config has a non-positive size or epsilon");
+  if (c->width != D || c->heads != NH || c->feedforward != F)
+    return fail(CLEF_E_UNSUPPORTED, "kernels are built for width 1024, 16 heads, feedforward 4096 (got %d, %d, %d)",
+                c->width, c->heads, c->feedforward);
+  if (c->hidden_size % 512 != 0 || c->hidden_size > 8192)
+    return fail(CLEF_E_UNSUPPORTED, "hidden_size must be a multiple of 512 up to 8192 (got %d)", c->hidden_size);
+  if (c->num_types < 3) return fail(CLEF_E_ARG, "num_types must cover noul, choice and score (>= 3)");
+  if (c->routing_layers > 64 || c->layers > 64) return fail(CLEF_E_UNSUPPORTED, "more than 64 layers in a stack");
+  return CLEF_OK;
+}
+
+// ---------------------------------------------------------------------------
+// batch plan
+// ---------------------------------------------------------------------------
+struct Plan {
+  int B = 0, NQ = 0, NO = 0, nact = 0;
+  int64_t T = 0, Tpad = 0, Ptot = 0, nids = 0;
+  int ntiles = 0, npool = 0, nitems = 0;
+  std::vector<int32_t> tab;   // all int32 tables, back to back
+  size_t off_rec = 0, off_tiles = 0, off_kvtiles = 0, off_pool = 0, off_lex = 0, off_ids = 0, off_optq = 0,
+         off_optrec = 0, off_qrec = 0, off_qtype = 0, off_ooff = 0, off_items = 0;
+  std::vector<int32_t> span_rows;   // [NQ + NO + B][2] packed-row ranges (for clef_head_span_rows)
+};
+
+int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, bool tables) {
+  if (!b) return fail(CLEF_E_ARG, "batch is NULL");
+  if (b->layout != CLEF_PADDED && b->layout != CLEF_VARLEN) return fail(CLEF_E_ARG, "unknown layout %d", b->layout);
+  const int B = b->num_records;
+  if (B < 1) return fail(CLEF_E_ARG, "num_records must be >= 1");
+  if (b->num_questions < 0 || b->num_options < 0) return fail(CLEF_E_ARG, "negative question / option count");
+  if (!b->q_offsets) return fail(CLEF_E_ARG, "q_offsets is NULL");
+  const int NQ = b->num_questions, NO = b->num_options;
+  if (NQ > 0 && (!b->q_type || !b->q_span || !b->o_offsets)) return fail(CLEF_E_ARG, "question tables are NULL");
+  if (NO > 0 && (!b->o_span || !b->o_ids)) return fail(CLEF_E_ARG, "option tables are NULL");
+
+  // record lengths and first hidden rows
+  std::vector<int64_t> len(B), src0(B);
+  if (b->layout == CLEF_PADDED) {
+    if (b->max_len < 1) return fail(CLEF_E_LENGTH, "max_len must be >= 1");
+    if (!b->key_mask) return fail(CLEF_E_ARG, "key_mask is NULL");
+    for (int r = 0; r < B; ++r) {
+      const uint8_t* m = b->key_mask + (size_t)r * b->max_len;
+      int n = 0;
+      while (n < b->max_len && m[n]) ++n;
+      for (int t = n; t < b->max_len; ++t)
+        if (m[t]) return fail(CLEF_E_LENGTH, "key_mask row %d is not a prefix mask", r);
+      if (n < 1) return fail(CLEF_E_LENGTH, "record %d has no valid token", r);
+      len[r] = n;
+      src0[r] = (int64_t)r * b->max_len;
+    }
+  } else {
+    if (!b->cu_seqlens) return fail(CLEF_E_ARG, "cu_seqlens is NULL");
+    if (b->cu_seqlens[0] != 0) return fail(CLEF_E_LENGTH, "cu_seqlens[0] must be 0");
+    for (int r = 0; r < B; ++r) {
+      const int64_t n = (int64_t)b->cu_seqlens[r + 1] - b->cu_seqlens[r];
+      if (n < 1) return fail(CLEF_E_LENGTH, "record %d has length %lld", r, (long long)n);
+      len[r] = n;
+      src0[r] = b->cu_seqlens[r];
+    }
+  }
+  if (!b->hidden) return fail(CLEF_E_ARG, "hidden is NULL");
+
+  // questions and options
+  if (b->q_offsets[0] != 0 || b->q_offsets[B] != NQ)
+    return fail(CLEF_E_SCHEMA, "q_offsets must start at 0 and end at num_questions");
+  for (int r = 0; r < B; ++r)
+    if (b->q_offsets[r + 1] < b->q_offsets[r]) return fail(CLEF_E_SCHEMA, "q_offsets decreases at record %d", r);
+  if (NQ > 0 && (b->o_offsets[0] != 0 || b->o_offsets[NQ] != NO))
+    return fail(CLEF_E_SCHEMA, "o_offsets must start at 0 and end at num_options");
+  if (NQ == 0 && NO != 0) return fail(CLEF_E_SCHEMA, "options without questions");
+  int64_t nids = 0;
+  for (int r = 0; r < B; ++r) {
+    for (int q = b->q_offsets[r]; q < b->q_offsets[r + 1]; ++q) {
+      const int t = b->q_type[q];
+      if (t < 0 || t > 2) return fail(CLEF_E_SCHEMA, "question %d has type %d (0 noul, 1 choice, 2 score)", q, t);
+      const int s = b->q_span[2 * q], e = b->q_span[2 * q + 1];
+      if (!(0 <= s && s < e && e <= len[r]))
+        return fail(CLEF_E_SPAN, "question %d span [%d, %d) outside record %d of length %lld", q, s, e, r,
+                    (long long)len[r]);
+      const int no = b->o_offsets[q + 1] - b->o_offsets[q];
+      if (no < 1) return fail(CLEF_E_SCHEMA, "question %d has no options", q);
+      if (t == 0 && no != 2) return fail(CLEF_E_SCHEMA, "noul question %d has %d options (needs true, false)", q, no);
+      if (no > kMaxOptions) return fail(CLEF_E_UNSUPPORTED, "question %d has more than %d options", q, kMaxOptions);
+      for (int k = b->o_offsets[q]; k < b->o_offsets[q + 1]; ++k) {
+        const int os = b->o_span[2 * k], oe = b->o_span[2 * k + 1];
+        if (!(0 <= os && os < oe && oe <= len[r]))
+          return fail(CLEF_E_SPAN, "option %d span [%d, %d) outside record %d of length %lld", k, os, oe, r,
+                      (long long)len[r]);
+        for (int i = 0; i < oe - os; ++i) {
+          const int id = b->o_ids[nids + i];
+          if (id < 0 || id >= c.vocab_size)
+            return fail(CLEF_E_ID, "option %d token id %d outside [0, %d)", k, id, c.vocab_size);
+        }
+        nids += oe - os;
+      }
+    }
+  }
+
+  p.B = B;
+  p.NQ = NQ;
+  p.NO = NO;
+  p.nids = nids;
+  int64_t T = 0;
+  for (int r = 0; r < B; ++r) T += len[r];
+  p.T = T;
+
+  // pooled row ranges in packed row space (independent of the device layout)
+  {
+    p.span_rows.assign((size_t)(NQ + NO + B) * 2, 0);
+    int64_t base = 0;
+    for (int r = 0; r < B; ++r) {
+      for (int q = b->q_offsets[r]; q < b->q_offsets[r + 1]; ++q) {
+        p.span_rows[2 * q] = int32_t(base + b->q_span[2 * q]);
+        p.span_rows[2 * q + 1] = int32_t(base + b->q_span[2 * q + 1]);
+        for (int k = b->o_offsets[q]; k < b->o_offsets[q + 1]; ++k) {
+          p.span_rows[2 * (NQ + k)] = int32_t(base + b->o_span[2 * k]);
+          p.span_rows[2 * (NQ + k) + 1] = int32_t(base + b->o_span[2 * k + 1]);
+        }
+      }
+      p.span_rows[2 * (NQ + NO + r)] = int32_t(base + len[r] - 1);
+      p.span_rows[2 * (NQ + NO + r) + 1] = int32_t(base + len[r]);
+      base += len[r];
+    }
+  }
+  if (!tables || NQ == 0) return CLEF_OK;
+
+  // active records (with questions), their padded row bases and chunking
+  std::vector<int32_t> rec, tiles, kvtiles, pool, lex, ids, optq, optrec, qrec, qtype, ooff, items;
+  std::vector<int> act_of(B, -1);
+  int64_t kv0 = 0, pbase = 0;
+  int nact = 0;
+  for (int r = 0; r < B; ++r) {
+    const int q0 = b->q_offsets[r], nq = b->q_offsets[r + 1] - q0;
+    if (nq == 0) continue;
+    const int o0 = b->o_offsets[q0], no = b->o_offsets[q0 + nq] - o0;
+    const int nc = (int)ceil_div(len[r], KCH);
+    act_of[r] = nact;
+    rec.insert(rec.end(), {int32_t(kv0), int32_t(len[r]), o0, no, int32_t(pbase), nc, q0, nq});
+    for (int64_t t0 = 0; t0 < len[r]; t0 += TILE) {
+      tiles.insert(tiles.end(), {int32_t(src0[r] + t0), int32_t(kv0 + t0), int32_t(std::min<int64_t>(TILE, len[r] - t0)), nact});
+      kvtiles.insert(kvtiles.end(), {int32_t(kv0 + t0), int32_t(kv0 + t0), TILE, nact});
+    }
+    for (int ch = 0; ch < nc; ++ch) items.insert(items.end(), {nact, ch});
+    kv0 += ceil_div(len[r], TILE) * TILE;
+    pbase += (int64_t)no * nc;
+    ++nact;
+  }
+  if (kv0 > INT32_MAX / 2 || pbase * 64 * NH > INT64_C(1) << 40)
+    return fail(CLEF_E_UNSUPPORTED, "batch too large for 32-bit row indices");
+  p.nact = nact;
+  p.Tpad = kv0;
+  p.Ptot = pbase;
+  p.ntiles = (int)tiles.size() / 4;
+  p.nitems = (int)items.size() / 2;
+
+  // pooling entries: questions, then options, then global rows; lexical entries per option
+  std::vector<int32_t> opool;
+  int64_t idoff = 0;
+  for (int r = 0; r < B; ++r) {
+    const int a = act_of[r];
+    if (a < 0) continue;
+    const int64_t kvb = rec[8 * a];
+    for (int q = b->q_offsets[r]; q < b->q_offsets[r + 1]; ++q) {
+      const int s = b->q_span[2 * q], e = b->q_span[2 * q + 1];
+      pool.insert(pool.end(), {int32_t(src0[r] + s), e - s, int32_t(kvb + s), q});
+      qrec.push_back(a);
+      qtype.push_back(b->q_type[q]);
+      for (int k = b->o_offsets[q]; k < b->o_offsets[q + 1]; ++k) {
+        const int os = b->o_span[2 * k], oe = b->o_span[2 * k + 1];
+        optq.push_back(q);
+        optrec.push_back(a);
+        opool.insert(opool.end(), {int32_t(src0[r] + os), oe - os, int32_t(kvb + os), NQ + k});
+        lex.insert(lex.end(), {int32_t(idoff), oe - os, q, NQ + NO + a});
+        idoff += oe - os;
+      }
+    }
+  }
+  pool.insert(pool.end(), opool.begin(), opool.end());
+  for (int r = 0; r < B; ++r) {
+    const int a = act_of[r];
+    if (a < 0) continue;
+    const int64_t kvb = rec[8 * a];
+    pool.insert(pool.end(), {int32_t(src0[r] + len[r] - 1), 1, int32_t(kvb + len[r] - 1), NQ + NO + a});
+  }
+  ids.assign(b->o_ids, b->o_ids + nids);
+  ooff.assign(b->o_offsets, b->o_offsets + NQ + 1);
+  p.npool = (int)pool.size() / 4;
+
+  auto put = [&](const std::vector<int32_t>& v) {
+    // keep every table 16-byte aligned (int4 loads)
+    while (p.tab.size() % 4) p.tab.push_back(0);
+    const size_t off = p.tab.size();
+    p.tab.insert(p.tab.end(), v.begin(), v.end());
+    return off;
+  };
+  p.tab.clear();
+  p.off_rec = put(rec);
+  p.off_tiles = put(tiles);
+  p.off_kvtiles = put(kvtiles);
+  p.off_pool = put(pool);
+  p.off_lex = put(lex);
+  p.off_ids = put(ids);
+  p.off_optq = put(optq);
+  p.off_optrec = put(optrec);
+  p.off_qrec = put(qrec);
+  p.off_qtype = put(qtype);
+  p.off_ooff = put(ooff);
+  p.off_items = put(items);
+  while (p.tab.size() % 4) p.tab.push_back(0);
+  return CLEF_OK;
+}
+
+// ---------------------------------------------------------------------------
+// device weights
+// ---------------------------------------------------------------------------
+struct Layer {
+  const float *ln1g, *ln1b, *ln2g, *ln2b, *bq, *bo, *b1, *b2, *bqkv;
+  const bf16_t *Wq, *Wo, *W1, *W2, *Wqkv;
+};
+
+struct Weights {
+  const float *lnin_g, *lnin_b, *cmem, *dmem, *ba7, *bqb, *bg, *temb, *sw, *bkv, *bs1, *ws2;
+  const bf16_t *Wmem, *Wa7, *Wqb, *Wg, *Wkv, *Ws1;
+  std::vector<Layer> route, field;
+  float sb, bs2, gate_logit, gate, lam;
+};
+
+}  // namespace
+
+struct clef_head {
+  clef_head_config cfg;
+  int device = 0;
+  const bf16_t* table = nullptr;
+  void* dweights = nullptr;
+  Weights w;
+  // workspace
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  void* pinned = nullptr;
+  size_t pinned_bytes = 0;
+  hipEvent_t staged = nullptr;
+  bool staged_pending = false;
+  // trace
+  bool trace = false;
+  void* tr = nullptr;
+  size_t tr_bytes = 0;
+  hipStream_t last_stream = nullptr;
+  int last_NQ = 0, last_NO = 0, last_B = 0;
+  int64_t last_Tpad = 0;
+  // workspace pointers of the last forward (for traces)
+  float *pooled = nullptr, *ebar = nullptr, *prior = nullptr;
+  bf16_t* mem = nullptr;
+  float *tr_u = nullptr, *tr_f0 = nullptr, *tr_f = nullptr, *tr_jcos = nullptr, *tr_mlp = nullptr;
+};
+
+namespace {
+
+struct Blob {
+  std::vector<uint8_t> host;
+  size_t add(const void* src, size_t bytes) {
+    const size_t off = align256(host.size());
+    host.resize(off + bytes);
+    if (src) memcpy(host.data() + off, src, bytes);
+    return off;
+  }
+  size_t add_f32(const std::vector<float>& v) { return add(v.data(), v.size() * 4); }
+};
+
+struct NamedW {
+  const void* p;
+  int64_t n;
+  int32_t dt;
+};
+
+int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
+  const clef_head_config& c = h->cfg;
+  const int H = c.hidden_size;
+  std::unordered_map<std::string, NamedW> m;
+  if (nw < 0 || (nw > 0 && !w)) return fail(CLEF_E_ARG, "weights array is NULL");
+  for (int i = 0; i < nw; ++i) {
+    if (!w[i].name || !w[i].host_data) return fail(CLEF_E_ARG, "weight %d has a NULL name or data", i);
+    if (m.count(w[i].name)) return fail(CLEF_E_ARG, "weight %s given twice", w[i].name);
+    m[w[i].name] = {w[i].host_data, w[i].numel, w[i].dtype};
+  }
+  const auto specs = weight_list(c);
+  for (auto& s : specs) {
+    auto it = m.find(s.name);
+    if (it == m.end()) return fail(CLEF_E_ARG, "missing weight %s", s.name.c_str());
+    if (it->second.n != s.numel || it->second.dt != s.dtype)
+      return fail(CLEF_E_ARG, "weight %s has %lld elements of dtype %d, expected %lld of dtype %d", s.name.c_str(),
+                  (long long)it->second.n, it->second.dt, (long long)s.numel, s.dtype);
+  }
+  if (m.size() != specs.size()) return fail(CLEF_E_ARG, "unexpected extra weights (%zu given, %zu expected)", m.size(), specs.size());
+
+  auto bf = [&](const std::string& n) { return static_cast<const uint16_t*>(m[n].p); };
+  auto tof = [&](const std::string& n) {
+    const auto& e = m[n];
+    std::vector<float> v(e.n);
+    const uint16_t* s = static_cast<const uint16_t*>(e.p);
+    for (int64_t i = 0; i < e.n; ++i) v[i] = bf16_to_f(s[i]);
+    return v;
+  };
+  auto scalar = [&](const std::string& n) { return *static_cast<const float*>(m[n].p); };
+
+  Blob blob;
+  struct Fix { size_t off; const void** dst; };
+  std::vector<std::pair<size_t, const void**>> fix;
+  auto put_bf = [&](const uint16_t* src, size_t n, const bf16_t** dst) { fix.push_back({blob.add(src, n * 2), (const void**)dst}); };
+  auto put_f = [&](const std::vector<float>& v, const float** dst) { fix.push_back({blob.add_f32(v), (const void**)dst}); };
+
+  Weights& W = h->w;
+  // input LayerNorm (pooling) and the memory projection with the LayerNorm folded in
+  const std::vector<float> g = tof("ln_in.w"), be = tof("ln_in.b");
+  put_f(g, &W.lnin_g);
+  put_f(be, &W.lnin_b);
+  {
+    const uint16_t* Wm = bf("mem.w");
+    const std::vector<float> bm = tof("mem.b");
+    std::vector<uint16_t> Wp((size_t)D * H);
+    std::vector<float> cm(D), dm(D);
+    for (int j = 0; j < D; ++j) {
+      double cs = 0, ds = bm[j];
+      for (int k = 0; k < H; ++k) {
+        const float wv = bf16_to_f(Wm[(size_t)j * H + k]);
+        const uint16_t wp = f_to_bf16(wv * g[k]);
+        Wp[(size_t)j * H + k] = wp;
+        cs += bf16_to_f(wp);
+        ds += (double)wv * be[k];
+      }
+      cm[j] = (float)cs;
+      dm[j] = (float)ds;
+    }
+    put_bf(Wp.data(), Wp.size(), &W.Wmem);
+    put_f(cm, &W.cmem);
+    put_f(dm, &W.dmem);
+  }
+  // option-query projection: [W_c | W_l | W_qo] along K, biases summed
+  {
+    std::vector<uint16_t> Wa((size_t)D * 3 * H);
+    const uint16_t* a = bf("opt_ctx.w");
+    const uint16_t* l = bf("opt_lex.w");
+    const uint16_t* q = bf("q_opt.w");
+    for (int j = 0; j < D; ++j) {
+      memcpy(&Wa[(size_t)j * 3 * H], a + (size_t)j * H, H * 2);
+      memcpy(&Wa[(size_t)j * 3 * H + H], l + (size_t)j * H, H * 2);
+      memcpy(&Wa[(size_t)j * 3 * H + 2 * H], q + (size_t)j * H, H * 2);
+    }
+    put_bf(Wa.data(), Wa.size(), &W.Wa7);
+    const auto b1 = tof("opt_ctx.b"), b2 = tof("opt_lex.b"), b3 = tof("q_opt.b");
+    std::vector<float> bs(D);
+    for (int j = 0; j < D; ++j) bs[j] = (float)((double)b1[j] + b2[j] + b3[j]);
+    put_f(bs, &W.ba7);
+  }
+  put_bf(bf("q_base.w"), (size_t)D * H, &W.Wqb);
+  put_f(tof("q_base.b"), &W.bqb);
+  put_bf(bf("glob.w"), (size_t)D * H, &W.Wg);
+  put_f(tof("glob.b"), &W.bg);
+  put_f(tof("type_emb"), &W.temb);
+  put_f(tof("summary.w"), &W.sw);
+  W.sb = bf16_to_f(bf("summary.b")[0]);
+
+  const int NR = c.routing_layers, NL = c.layers;
+  // K/V of every routing layer stacked: [K_0; V_0; K_1; V_1; ...] rows
+  {
+    std::vector<uint16_t> Wkv((size_t)NR * 2 * D * D);
+    std::vector<float> bkv((size_t)NR * 2 * D);
+    for (int r = 0; r < NR; ++r) {
+      const std::string p = "route." + std::to_string(r);
+      memcpy(&Wkv[(size_t)(2 * r) * D * D], bf(p + ".k.w"), (size_t)D * D * 2);
+      memcpy(&Wkv[(size_t)(2 * r + 1) * D * D], bf(p + ".v.w"), (size_t)D * D * 2);
+      const auto bk = tof(p + ".k.b"), bv = tof(p + ".v.b");
+      std::copy(bk.begin(), bk.end(), bkv.begin() + (size_t)(2 * r) * D);
+      std::copy(bv.begin(), bv.end(), bkv.begin() + (size_t)(2 * r + 1) * D);
+    }
+    if (NR > 0) {
+      put_bf(Wkv.data(), Wkv.size(), &W.Wkv);
+      put_f(bkv, &W.bkv);
+    } else {
+      W.Wkv = nullptr;
+      W.bkv = nullptr;
+    }
+  }
+  W.route.resize(NR);
+  W.field.resize(NL);
+  for (int s = 0; s < NR + NL; ++s) {
+    const bool route = s < NR;
+    const std::string p = route ? "route." + std::to_string(s) : "field." + std::to_string(s - NR);
+    Layer& L = route ? W.route[s] : W.field[s - NR];
+    put_f(tof(p + ".ln1.w"), &L.ln1g);
+    put_f(tof(p + ".ln1.b"), &L.ln1b);
+    put_f(tof(p + ".ln2.w"), &L.ln2g);
+    put_f(tof(p + ".ln2.b"), &L.ln2b);
+    if (route) {
+      put_bf(bf(p + ".q.w"), (size_t)D * D, &L.Wq);
+      put_f(tof(p + ".q.b"), &L.bq);
+      L.Wqkv = nullptr;
+      L.bqkv = nullptr;
+    } else {
+      std::vector<uint16_t> Wqkv((size_t)3 * D * D);
+      std::vector<float> bqkv((size_t)3 * D);
+      int i = 0;
+      for (const char* mname : {"q", "k", "v"}) {
+        memcpy(&Wqkv[(size_t)i * D * D], bf(p + "." + mname + ".w"), (size_t)D * D * 2);
+        const auto bb = tof(p + "." + mname + ".b");
+        std::copy(bb.begin(), bb.end(), bqkv.begin() + (size_t)i * D);
+        ++i;
+      }
+      put_bf(Wqkv.data(), Wqkv.size(), &L.Wqkv);
+      put_f(bqkv, &L.bqkv);
+      L.Wq = nullptr;
+      L.bq = nullptr;
+    }
+    put_bf(bf(p + ".o.w"), (size_t)D * D, &L.Wo);
+    put_f(tof(p + ".o.b"), &L.bo);
+    put_bf(bf(p + ".ffn1.w"), (size_t)F * D, &L.W1);
+    put_f(tof(p + ".ffn1.b"), &L.b1);
+    put_bf(bf(p + ".ffn2.w"), (size_t)D * F, &L.W2);
+    put_f(tof(p + ".ffn2.b"), &L.b2);
+  }
+  put_bf(bf("score.w1"), (size_t)D * 4 * D, &W.Ws1);
+  put_f(tof("score.b1"), &W.bs1);
+  put_f(tof("score.w2"), &W.ws2);
+  W.bs2 = bf16_to_f(bf("score.b2")[0]);
+  W.gate_logit = scalar("gate_logit");
+  W.lam = scalar("joint_scale");
+  {
+    const double gl = W.gate_logit;
+    const double gs = gl < -745.0 ? 0.0 : 1.0 / (1.0 + std::exp(-gl));
+    W.gate = (float)gs;
+  }
+
+  void* d = nullptr;
+  if (hipMalloc(&d, blob.host.size()) != hipSuccess)
+    return fail(CLEF_E_NOMEM, "hipMalloc of %zu bytes of weights failed", blob.host.size());
+  if (hipMemcpy(d, blob.host.data(), blob.host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(d);
+    return fail(CLEF_E_HIP, "copying weights to the device failed");
+  }
+  h->dweights = d;
+  for (auto& f : fix) *f.second = static_cast<const uint8_t*>(d) + f.first;
+  return CLEF_OK;
+}
+
+// workspace layout for one plan
+struct WsLayout {
+  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, gp, f, fstats, qkv, fattn, hs, pm,
+      pl, po, part, counters, total;
+};
+
+WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
+  const size_t H = c.hidden_size, NQ = p.NQ, NO = p.NO, Tp = p.Tpad, NR = c.routing_layers;
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o = align256(o + bytes); return r; };
+  L.tab = take(p.tab.size() * 4);
+  L.stats = take(Tp * 8);
+  L.pooled = take((NQ + NO + p.nact) * H * 4);
+  L.ebar = take(NO * H * 4);
+  L.prior = take(NO * 4);
+  L.mem = take(Tp * D * 2);
+  L.kv = take(NR * 2 * NH * Tp * 64 * 2);
+  L.u = take(NO * D * 4);
+  L.ustats = take(NO * 8);
+  L.qbuf = take(NO * D * 4);
+  L.attn = take(NO * D * 4);
+  L.hbuf = take(std::max(NO, NQ) * F * 4);
+  L.qv = take(NQ * D * 4);
+  L.gp = take((size_t)p.nact * D * 4);
+  L.f = take(NQ * D * 4);
+  L.fstats = take(NQ * 8);
+  L.qkv = take(NQ * 3 * D * 4);
+  L.fattn = take(NQ * D * 4);
+  L.hs = take(NO * D * 4);
+  L.pm = take((size_t)NH * p.Ptot * 4);
+  L.pl = take((size_t)NH * p.Ptot * 4);
+  L.po = take((size_t)NH * p.Ptot * 64 * 4);
+  size_t part = 0;
+  int cnt = 0;
+  const int shapes[][3] = {{p.NO, D, 3 * (int)H}, {p.NQ, D, (int)H}, {p.nact, D, (int)H}, {p.NO, D, D},
+                           {p.NO, F, D},        {p.NO, D, F},        {p.NQ, 3 * D, D},     {p.NQ, D, D},
+                           {p.NQ, F, D},        {p.NQ, D, F},        {p.NO, D, 4 * D}};
+  for (auto& s : shapes) {
+    if (s[0] == 0) continue;
+    const SgemmShape g = sgemm_shape(s[0], s[1], s[2]);
+    part = std::max(part, g.part_floats);
+    cnt = std::max(cnt, g.counters);
+  }
+  L.part = take(part * 4);
+  L.counters = take((size_t)std::max(cnt, 1) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* clef_head_last_error(void) { return g_err.c_str(); }
+
+int32_t clef_head_weight_count(const clef_head_config* cfg) {
+  if (check_config(cfg) != CLEF_OK) return -1;
+  return (int32_t)weight_list(*cfg).size();
+}
+
+int clef_head_weight_info(const clef_head_config* cfg, int32_t i, char* name, int32_t name_cap, int64_t* numel,
+                          int32_t* dtype) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  const auto s = weight_list(*cfg);
+  if (i < 0 || i >= (int32_t)s.size()) return fail(CLEF_E_ARG, "weight index %d out of range", i);
+  if (name) {
+    if (name_cap < (int32_t)s[i].name.size() + 1) return fail(CLEF_E_ARG, "name buffer too small");
+    memcpy(name, s[i].name.c_str(), s[i].name.size() + 1);
+  }
+  if (numel) *numel = s[i].numel;
+  if (dtype) *dtype = s[i].dtype;
+  return CLEF_OK;
+}
+
+int clef_head_check_batch(const clef_head_config* cfg, const clef_head_batch* batch, int64_t* num_rows) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  Plan p;
+  rc = build_plan(*cfg, batch, p, false);
+  if (rc) return rc;
+  if (num_rows) *num_rows = p.T;
+  return CLEF_OK;
+}
+
+int clef_head_span_rows(const clef_head_config* cfg, const clef_head_batch* batch, int32_t* rows) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!rows) return fail(CLEF_E_ARG, "rows is NULL");
+  Plan p;
+  rc = build_plan(*cfg, batch, p, false);
+  if (rc) return rc;
+  memcpy(rows, p.span_rows.data(), p.span_rows.size() * 4);
+  return CLEF_OK;
+}
+
+int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weights, int32_t num_weights,
+                     const void* lexical_table, clef_head** out) {
+  if (!out) return fail(CLEF_E_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!lexical_table) return fail(CLEF_E_ARG, "lexical_table is NULL");
+  clef_head* h = new clef_head();
+  h->cfg = *cfg;
+  h->table = static_cast<const bf16_t*>(lexical_table);
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return fail(CLEF_E_HIP, "no HIP device");
+  }
+  rc = build_weights(h, weights, num_weights);
+  if (rc) {
+    delete h;
+    return rc;
+  }
+  if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess) {
+    clef_head_destroy(h);
+    return fail(CLEF_E_HIP, "hipEventCreate failed");
+  }
+  *out = h;
+  return CLEF_OK;
+}
+
+void clef_head_destroy(clef_head* h) {
+  if (!h) return;
+  if (h->staged) {
+    if (h->staged_pending) (void)hipEventSynchronize(h->staged);
+    (void)hipEventDestroy(h->staged);
+  }
+  if (h->ws) (void)hipFree(h->ws);
+  if (h->tr) (void)hipFree(h->tr);
+  if (h->pinned) (void)hipHostFree(h->pinned);
+  if (h->dweights) (void)hipFree(h->dweights);
+  delete h;
+}
+
+int clef_head_set_trace(clef_head* h, int32_t enable) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  h->trace = enable != 0;
+  return CLEF_OK;
+}
+
+int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) {
+  if (!h || !host_dst) return fail(CLEF_E_ARG, "NULL argument");
+  if (!h->trace || !h->pooled) return fail(CLEF_E_ARG, "tracing was not enabled for the last forward");
+  HIPCHK(hipStreamSynchronize(h->last_stream));
+  const size_t H = h->cfg.hidden_size, NQ = h->last_NQ, NO = h->last_NO, B = h->last_B;
+  const void* src = nullptr;
+  size_t n = 0;
+  const int NR = h->cfg.routing_layers;
+  if (which == CLEF_TRACE_POOLED) { src = h->pooled; n = (NQ + NO + B) * H * 4; }
+  else if (which == CLEF_TRACE_LEXICAL) { src = h->ebar; n = NO * H * 4; }
+  else if (which == CLEF_TRACE_PRIOR) { src = h->prior; n = NO * 4; }
+  else if (which == CLEF_TRACE_MEMORY) { src = h->mem; n = (size_t)h->last_Tpad * D * 2; }
+  else if (which == CLEF_TRACE_F0) { src = h->tr_f0; n = NQ * D * 4; }
+  else if (which == CLEF_TRACE_F) { src = h->tr_f; n = NQ * D * 4; }
+  else if (which == CLEF_TRACE_JCOS) { src = h->tr_jcos; n = NO * 4; }
+  else if (which == CLEF_TRACE_MLP) { src = h->tr_mlp; n = NO * 4; }
+  else if (which >= CLEF_TRACE_U && which <= CLEF_TRACE_U + NR) {
+    src = h->tr_u + (size_t)(which - CLEF_TRACE_U) * NO * D;
+    n = NO * D * 4;
+  } else
+    return fail(CLEF_E_ARG, "unknown trace id %d", which);
+  if ((size_t)bytes != n) return fail(CLEF_E_ARG, "trace %d holds %zu bytes, %lld requested", which, n, (long long)bytes);
+  if (!src) return fail(CLEF_E_ARG, "trace %d was not recorded (joint branch skipped?)", which);
+  HIPCHK(hipMemcpy(host_dst, src, n, hipMemcpyDeviceToHost));
+  return CLEF_OK;
+}
+
+int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
+                      void* hip_stream) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  const clef_head_config& c = h->cfg;
+  Plan p;
+  int rc = build_plan(c, batch, p, true);
+  if (rc) return rc;
+  if (p.NQ == 0) return CLEF_OK;
+  if (!logits || !probs || !argmax) return fail(CLEF_E_ARG, "output buffer is NULL");
+  int dev_prev = 0;
+  HIPCHK(hipGetDevice(&dev_prev));
+  if (dev_prev != h->device) HIPCHK(hipSetDevice(h->device));
+  struct Restore {
+    int d, p;
+    ~Restore() { if (d != p) (void)hipSetDevice(p); }
+  } restore{h->device, dev_prev};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  const WsLayout L = ws_layout(c, p);
+  if (L.total > h->ws_bytes) {
+    if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
+    HIPCHK(hipDeviceSynchronize());
+    if (h->ws) (void)hipFree(h->ws);
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+    const size_t want = L.total + L.total / 4;
+    if (hipMalloc(&h->ws, want) != hipSuccess) return fail(CLEF_E_NOMEM, "workspace hipMalloc of %zu bytes failed", want);
+    h->ws_bytes = want;
+    HIPCHK(hipMemset(h->ws, 0, want));   // split-K tile counters start at zero and are reset by their kernels
+  }
+  const size_t tab_bytes = p.tab.size() * 4;
+  if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
+  if (tab_bytes > h->pinned_bytes) {
+    if (h->pinned) (void)hipHostFree(h->pinned);
+    h->pinned = nullptr;
+    h->pinned_bytes = 0;
+    const size_t want = tab_bytes + tab_bytes / 2 + 4096;
+    if (hipHostMalloc(&h->pinned, want, hipHostMallocDefault) != hipSuccess)
+      return fail(CLEF_E_NOMEM, "pinned staging of %zu bytes failed", want);
+    h->pinned_bytes = want;
+  }
+  const int NR = c.routing_layers, NL = c.layers, NQ = p.NQ, NO = p.NO;
+  const size_t H = c.hidden_size;
+  if (h->trace) {
+    const size_t need = align256((size_t)(NR + 1) * NO * D * 4) + 2 * align256((size_t)NQ * D * 4) + 2 * align256((size_t)NO * 4);
+    if (need > h->tr_bytes) {
+      HIPCHK(hipDeviceSynchronize());
+      if (h->tr) (void)hipFree(h->tr);
+      h->tr = nullptr;
+      h->tr_bytes = 0;
+      if (hipMalloc(&h->tr, need) != hipSuccess) return fail(CLEF_E_NOMEM, "trace hipMalloc failed");
+      h->tr_bytes = need;
+    }
+    uint8_t* t = static_cast<uint8_t*>(h->tr);
+    h->tr_u = reinterpret_cast<float*>(t);
+    t += align256((size_t)(NR + 1) * NO * D * 4);
+    h->tr_f0 = reinterpret_cast<float*>(t);
+    t += align256((size_t)NQ * D * 4);
+    h->tr_f = reinterpret_cast<float*>(t);
+    t += align256((size_t)NQ * D * 4);
+    h->tr_jcos = reinterpret_cast<float*>(t);
+    t += align256((size_t)NO * 4);
+    h->tr_mlp = reinterpret_cast<float*>(t);
+  }
+
+  memcpy(h->pinned, p.tab.data(), tab_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(h->ws);
+  int32_t* dtab = reinterpret_cast<int32_t*>(ws + L.tab);
+  HIPCHK(hipMemcpyAsync(dtab, h->pinned, tab_bytes, hipMemcpyHostToDevice, st));
+  HIPCHK(hipEventRecord(h->staged, st));
+  h->staged_pending = true;
+
+  const int* rec = dtab + p.off_rec;
+  const int4* tiles = reinterpret_cast<const int4*>(dtab + p.off_tiles);
+  const int4* kvtiles = reinterpret_cast<const int4*>(dtab + p.off_kvtiles);
+  const int4* pool = reinterpret_cast<const int4*>(dtab + p.off_pool);
+  const int4* lex = reinterpret_cast<const int4*>(dtab + p.off_lex);
+  const int* ids = dtab + p.off_ids;
+  const int* optq = dtab + p.off_optq;
+  const int* optrec = dtab + p.off_optrec;
+  const int* qrec = dtab + p.off_qrec;
+  const int* qtype = dtab + p.off_qtype;
+  const int* ooff = dtab + p.off_ooff;
+  const int2* items = reinterpret_cast<const int2*>(dtab + p.off_items);
+
+  float2* stats = reinterpret_cast<float2*>(ws + L.stats);
+  float* pooled = reinterpret_cast<float*>(ws + L.pooled);
+  float* ebar = reinterpret_cast<float*>(ws + L.ebar);
+  float* prior = reinterpret_cast<float*>(ws + L.prior);
+  bf16_t* mem = reinterpret_cast<bf16_t*>(ws + L.mem);
+  bf16_t* kv = reinterpret_cast<bf16_t*>(ws + L.kv);
+  float* u = reinterpret_cast<float*>(ws + L.u);
+  float2* ustats = reinterpret_cast<float2*>(ws + L.ustats);
+  float* qbuf = reinterpret_cast<float*>(ws + L.qbuf);
+  float* attn = reinterpret_cast<float*>(ws + L.attn);
+  float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
+  float* qv = reinterpret_cast<float*>(ws + L.qv);
+  float* gp = reinterpret_cast<float*>(ws + L.gp);
+  float* f = reinterpret_cast<float*>(ws + L.f);
+  float2* fstats = reinterpret_cast<float2*>(ws + L.fstats);
+  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  float* fattn = reinterpret_cast<float*>(ws + L.fattn);
+  float* hs = reinterpret_cast<float*>(ws + L.hs);
+  float* pm = reinterpret_cast<float*>(ws + L.pm);
+  float* pl = reinterpret_cast<float*>(ws + L.pl);
+  float* po = reinterpret_cast<float*>(ws + L.po);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  int* counters = reinterpret_cast<int*>(ws + L.counters);
+  const bf16_t* X = static_cast<const bf16_t*>(batch->hidden);
+  const Weights& W = h->w;
+  const float eps = c.ln_eps;
+  const bool joint = W.gate != 0.0f;
+
+  // step 1: row statistics, pooled vectors, lexical vectors and prior
+  launch_rowstats_bf16(st, X, (int)H, tiles, p.ntiles, stats, eps);
+  launch_pool(st, X, (int)H, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
+  launch_lex_prior(st, h->table, (int)H, lex, NO, ids, pooled, ebar, prior);
+
+  if (joint) {
+    // step 2: memory and K/V of every routing layer
+    if (NR > 0) {
+      launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
+      launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
+    }
+    // step 3: option queries, question base and global projections
+    launch_sgemm(st, LdSeg3{pooled + (size_t)NQ * H, ebar, pooled, optq, (int)H}, EpStore{u, D, W.ba7}, W.Wa7, NO, D,
+                 3 * (int)H, part, counters);
+    launch_sgemm(st, LdRows{pooled, (int)H, nullptr}, EpStore{qv, D, W.bqb}, W.Wqb, NQ, D, (int)H, part, counters);
+    launch_sgemm(st, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
+                 (int)H, part, counters);
+    if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_u, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
+    for (int r = 0; r < NR; ++r) {
+      const Layer& Ly = W.route[r];
+      const bf16_t* Kl = kv + (size_t)(2 * r) * NH * p.Tpad * 64;
+      const bf16_t* Vl = kv + (size_t)(2 * r + 1) * NH * p.Tpad * 64;
+      launch_rowstats_f32(st, u, NO, ustats, eps);
+      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part, counters);
+      launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot);
+      launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
+      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, counters);
+      launch_rowstats_f32(st, u, NO, ustats, eps);
+      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part, counters);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part, counters);
+      if (h->trace)
+        HIPCHK(hipMemcpyAsync(h->tr_u + (size_t)(r + 1) * NO * D, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
+    }
+    // step 4: field vectors and the field transformer
+    launch_field_agg(st, u, ooff, W.sw, W.sb, qv, gp, qrec, qtype, W.temb, NQ, f);
+    if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f0, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
+    for (int l = 0; l < NL; ++l) {
+      const Layer& Ly = W.field[l];
+      launch_rowstats_f32(st, f, NQ, fstats, eps);
+      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, EpStore{qkv, 3 * D, Ly.bqkv}, Ly.Wqkv, NQ, 3 * D, D, part,
+                   counters);
+      launch_field_attn(st, qkv, rec, p.nact, fattn);
+      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, counters);
+      launch_rowstats_f32(st, f, NQ, fstats, eps);
+      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part, counters);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part, counters);
+    }
+    if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
+    // step 5: residual-MLP hidden layer over [f, u, f*u, |f-u|]
+    launch_sgemm(st, LdZ{f, u, optq}, EpGelu{hs, D, W.bs1}, W.Ws1, NO, D, 4 * D, part, counters);
+  }
+  launch_score(st, u, f, hs, W.ws2, W.bs2, prior, W.gate, W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
+               h->trace && joint ? h->tr_jcos : nullptr, h->trace && joint ? h->tr_mlp : nullptr);
+  HIPCHK(hipGetLastError());
+
+  h->last_stream = st;
+  h->last_NQ = NQ;
+  h->last_NO = NO;
+  h->last_B = p.nact;
+  h->last_Tpad = p.Tpad;
+  h->pooled = pooled;
+  h->ebar = ebar;
+  h->prior = prior;
+  h->mem = (joint && NR > 0) ? mem : nullptr;
+  if (!h->trace || !joint) {
+    h->tr_u = h->tr_f0 = h->tr_f = h->tr_jcos = h->tr_mlp = nullptr;
+  }
+  return CLEF_OK;
+}
+
+}  // extern "C"

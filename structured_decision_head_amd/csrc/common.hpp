@@ -1,0 +1,98 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, wave64
+// reductions, MFMA operand vector types and the XCD-aware block remap.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;                                                  // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));                // MFMA operand
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));           // 16-byte register vector
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define DEV __device__ __forceinline__
+
+DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+DEV uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Unpack 8 bf16 held in a uint4 into floats.
+DEV void unpack8(const uint4 v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+DEV uint4 pack8(const float* f) {
+  uint4 v;
+  v.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
+  v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
+  v.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
+  v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+  return v;
+}
+
+// Split 8 floats into hi = bf16(x) and lo = bf16(x - hi); hi + lo carries
+// about 16 significant bits of x.
+DEV void split8(const float* f, uint4& hi, uint4& lo) {
+  float r[8];
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(f[i]);
+    r[i] = f[i] - bf2f(h[i]);
+  }
+  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16);
+  hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
+  lo = pack8(r);
+}
+
+DEV bf16x8 as_bf16x8(const uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+DEV bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a whole block of NW waves; every thread gets the result.  `sm`
+// needs NW floats; the call ends with a barrier so `sm` can be reused.
+template <int NW>
+DEV float block_sum(float v, float* sm) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += sm[i];
+  __syncthreads();
+  return t;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on
+// XCD b % 8).  Return a logical tile index such that consecutive logical
+// tiles land on the same XCD, so tiles that share operand rows share that
+// XCD's L2.  Bijective for any grid size.
+DEV int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int xcd = bid & 7, slot = bid >> 3;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }

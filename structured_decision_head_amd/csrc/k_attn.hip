@@ -1,0 +1,234 @@
+// Attention kernels of the head.
+//
+// Evidence routing (clef-4bit page §三 step 2; Clef-Flash overview §三): all
+// option queries of a record attend, per head, over every valid memory row of
+// that record.  The keys are split into 256-row chunks; one wave owns
+// (record, head, chunk), loops over its record's queries 32 at a time and
+// writes flash-decode partials (running max, running sum, unnormalised
+// output) that k_route_combine merges.  Scores and the value mix use
+// v_mfma_f32_32x32x16_bf16 in a transposed form (S^T = K Q^T, O^T = V^T P^T) so
+// that each lane owns one query: the softmax statistics stay lane-local and the
+// probabilities are already in the B-operand layout of the second product.
+//
+// Field self-attention (clef-4bit page §三 step 3): every field of a record
+// attends to every field of the same record; tiny (<= a few dozen fields), so
+// plain fp32 with an online softmax, one lane per query.
+#include "kernels.hpp"
+
+namespace clef {
+
+namespace {
+constexpr int CH = 256;   // keys per chunk (one wave)
+}
+
+// rec: per record 8 ints: kv0 (first row in the packed padded row space),
+// n (valid rows), o0 (first option), no (options), pbase, nc (chunks), q0, nq.
+__global__ __launch_bounds__(256) void k_route_attn(const float* __restrict__ Q, const bf16_t* __restrict__ Kl,
+                                                    const bf16_t* __restrict__ Vl, long long Tpad,
+                                                    const int2* __restrict__ items, int nitems,
+                                                    const int* __restrict__ rec, float* __restrict__ pm,
+                                                    float* __restrict__ pl, float* __restrict__ po, long long Ptot,
+                                                    float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int it = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (it >= nitems) return;
+  const int j = blockIdx.y;
+  const int2 bc = items[it];
+  const int* R = rec + 8 * bc.x;
+  const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
+  const int c = bc.y;
+  const int k_lo = c * CH, k_hi = min(n, k_lo + CH);
+  const bf16_t* Kj = Kl + (size_t)j * Tpad * 64;
+  const bf16_t* Vj = Vl + (size_t)j * Tpad * 64;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  for (int qb = 0; qb < no; qb += 32) {
+    const int qi = qb + l32;
+    const bool qvalid = qi < no;
+    bf16x8 qf[4];
+    {
+      const float* qp = Q + (size_t)(o0 + (qvalid ? qi : 0)) * 1024 + j * 64 + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float x[8];
+        const float4 a = *reinterpret_cast<const float4*>(qp + kk * 16);
+        const float4 b = *reinterpret_cast<const float4*>(qp + kk * 16 + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        if (!qvalid)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        qf[kk] = as_bf16x8(pack8(x));
+      }
+    }
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+
+    for (int kb = k_lo; kb < k_hi; kb += 32) {
+      // S^T (32 keys x 32 queries): A = K rows, B = Q^T.
+      f32x16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      const bf16_t* kp = Kj + (size_t)(kv0 + kb + l32) * 64 + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kp + kk * 16);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[kk], s, 0, 0, 0);
+      }
+      // lane owns query l32 and keys kb + 8 (e / 4) + 4 g + (e % 4)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
+        s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
+      const float alpha = exp2f(m - mn);      // m = -inf gives 0
+      float ls = 0.f;
+      float p[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = exp2f(s[e] - mn);
+        ls += p[e];
+      }
+      ls += __shfl_xor(ls, 32, 64);
+      l = l * alpha + ls;
+      m = mn;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        o[0][e] *= alpha;
+        o[1][e] *= alpha;
+      }
+      // O^T (64 d x 32 queries) += V^T (d x keys) P^T (keys x queries); the
+      // k-slot (g, e) of step t is key kb + 16 t + 8 (e / 4) + 4 g + (e % 4).
+      const bf16_t* vp = Vj + ((size_t)((kv0 + kb) >> 5) * 64) * 32;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pf = as_bf16x8(pack8(p + 8 * t));
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16_t* rowp = vp + (size_t)(dt * 32 + l32) * 32 + 16 * t + 4 * g;
+          const uint2 lo = *reinterpret_cast<const uint2*>(rowp);
+          const uint2 hi = *reinterpret_cast<const uint2*>(rowp + 8);
+          const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pf, o[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (qvalid) {
+      const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
+      if (g == 0) {
+        pm[slot] = m;
+        pl[slot] = l;
+      }
+      float* op = po + slot * 64;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(op + dt * 32 + 8 * i + 4 * g) =
+              make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
+    }
+  }
+}
+
+void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
+                       const int2* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                       long long Ptot) {
+  if (nitems == 0) return;
+  const float scale_log2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+  hipLaunchKernelGGL(k_route_attn, dim3((nitems + 3) / 4, 16), dim3(256), 0, st, Q, Kl, Vl, Tpad, items, nitems,
+                     rec, pm, pl, po, Ptot, scale_log2);
+}
+
+// Merge the chunk partials of (option, head): one wave, lane = output dim.
+__global__ __launch_bounds__(256) void k_route_combine(const float* __restrict__ pm, const float* __restrict__ pl,
+                                                       const float* __restrict__ po, long long Ptot,
+                                                       const int* __restrict__ opt_rec, const int* __restrict__ rec,
+                                                       int NO, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= NO) return;
+  const int j = blockIdx.y;
+  const int* R = rec + 8 * opt_rec[k];
+  const int o0 = R[2], pbase = R[4], nc = R[5];
+  const size_t s0 = (size_t)j * Ptot + pbase + (size_t)(k - o0) * nc;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, pm[s0 + c]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float a = exp2f(pm[s0 + c] - M);
+    L += a * pl[s0 + c];
+    O += a * po[(s0 + c) * 64 + lane];
+  }
+  out[(size_t)k * 1024 + j * 64 + lane] = O / L;
+}
+
+void launch_route_combine(hipStream_t st, const float* pm, const float* pl, const float* po, long long Ptot,
+                          const int* opt_rec, const int* rec, int NO, float* out) {
+  if (NO == 0) return;
+  hipLaunchKernelGGL(k_route_combine, dim3((NO + 3) / 4, 16), dim3(256), 0, st, pm, pl, po, Ptot, opt_rec, rec, NO,
+                     out);
+}
+
+// Field self-attention: one 64-lane block per (record, head); QKV rows are
+// [q | k | v] of width 3 x 1024.
+__global__ __launch_bounds__(64) void k_field_attn(const float* __restrict__ QKV, const int* __restrict__ rec,
+                                                   float* __restrict__ out) {
+  __shared__ float sK[64][65], sV[64][65];
+  const int lane = threadIdx.x;
+  const int* R = rec + 8 * blockIdx.x;
+  const int q0 = R[6], nq = R[7];
+  const int j = blockIdx.y;
+  const float scale = 0.125f;
+  for (int qb = 0; qb < nq; qb += 64) {
+    const int qi = qb + lane;
+    const bool valid = qi < nq;
+    float q[64], o[64];
+    const float* qp = QKV + (size_t)(q0 + (valid ? qi : 0)) * 3072 + j * 64;
+#pragma unroll
+    for (int d = 0; d < 64; ++d) {
+      q[d] = qp[d] * scale;
+      o[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    for (int kb = 0; kb < nq; kb += 64) {
+      const int nk = min(64, nq - kb);
+      __syncthreads();
+      for (int t = 0; t < nk; ++t) {
+        const float* rp = QKV + (size_t)(q0 + kb + t) * 3072 + j * 64;
+        sK[t][lane] = rp[1024 + lane];
+        sV[t][lane] = rp[2048 + lane];
+      }
+      __syncthreads();
+      for (int t = 0; t < nk; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < 64; ++d) s += q[d] * sK[t][d];
+        const float mn = fmaxf(m, s);
+        const float a = expf(m - mn);
+        const float p = expf(s - mn);
+        l = l * a + p;
+#pragma unroll
+        for (int d = 0; d < 64; ++d) o[d] = o[d] * a + p * sV[t][d];
+        m = mn;
+      }
+    }
+    if (valid) {
+      float* op = out + (size_t)(q0 + qi) * 1024 + j * 64;
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) op[d] = o[d] * inv;
+    }
+  }
+}
+
+void launch_field_attn(hipStream_t st, const float* QKV, const int* rec, int nrec, float* out) {
+  if (nrec == 0) return;
+  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(64), 0, st, QKV, rec, out);
+}
+
+}  // namespace clef

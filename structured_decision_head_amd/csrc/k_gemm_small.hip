@@ -1,0 +1,178 @@
+// Small-M GEMMs of the head: option-query projections, the routing layers'
+// Q / O / FFN maps, the field layers' QKV / O / FFN maps and the residual-MLP
+// first layer.  M is the number of options or questions (5 to ~1100), N and K
+// are 1024..15360; these are weight streams, so the work is split along K
+// until the grid fills the chip and the partial sums are reduced by the last
+// workgroup of each tile, in a fixed order (deterministic).
+//
+// Precision: activations are fp32; each 8-element group is split into
+// hi = bf16(x) and lo = bf16(x - hi) and both are multiplied against the exact
+// bf16 weights with v_mfma_f32_16x16x32_bf16, so the product carries about 16
+// significant bits of the activation and fp32 accumulation.
+//
+// Prologues (how A rows are formed) and epilogues (what is done with each
+// output) are small functors; see kernels.hpp.
+#include "kernels.hpp"
+
+namespace clef {
+
+namespace {
+
+constexpr int SBM = 64, SBN = 128, SKC = 128;
+
+template <class Ld, class Epi>
+__global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __restrict__ W, int M, int N,
+                                               int K, int kchunk, int mtiles, int ntiles, int nsplit,
+                                               float* __restrict__ part, int* __restrict__ counters) {
+  __shared__ uint4 sAh[SBM * 16], sAl[SBM * 16];   // [row * 16 + swizzled chunk], KC = 128 bf16 per row
+  __shared__ int s_last;
+
+  const int lt = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = lt % mtiles;
+  const int tn = (lt / mtiles) % ntiles;
+  const int ks = lt / (mtiles * ntiles);
+  const int m0 = tm * SBM, n0 = tn * SBN;
+  const int kb = ks * kchunk, ke = min(K, kb + kchunk);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16_t* wp[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)(n0 + w * 32 + cb * 16 + (lane & 15)) * K + (lane >> 4) * 8;
+
+  for (int k0 = kb; k0 < ke; k0 += SKC) {
+    uint4 bq[2][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + k0 + kk * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + 256 * i;
+      const int r = v >> 4, c = v & 15;
+      float x[8];
+      if (m0 + r < M) {
+        ld.load8(m0 + r, k0 + c * 8, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      uint4 hi, lo;
+      split8(x, hi, lo);
+      const int idx = r * 16 + (c ^ (r & 15));
+      sAh[idx] = hi;
+      sAl[idx] = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        const bf16x8 ah = as_bf16x8(sAh[r * 16 + (c ^ (r & 15))]);
+        const bf16x8 al = as_bf16x8(sAl[r * 16 + (c ^ (r & 15))]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const bf16x8 b = as_bf16x8(bq[cb][kk]);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 16x16 accumulator layout: lane holds column (lane & 15), rows 4 * (lane / 16) + e.
+  if (nsplit == 1) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
+          const int n = n0 + w * 32 + cb * 16 + (lane & 15);
+          if (m < M) epi(m, n, acc[rb][cb][e]);
+        }
+    return;
+  }
+
+  const size_t Mp = (size_t)mtiles * SBM;
+  float* P = part + (size_t)ks * Mp * N;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
+        const int n = n0 + w * 32 + cb * 16 + (lane & 15);
+        P[(size_t)m * N + n] = acc[rb][cb][e];
+      }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&counters[tm * ntiles + tn], 1) == nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
+        const int n = n0 + w * 32 + cb * 16 + (lane & 15);
+        float s = 0.f;
+        for (int q = 0; q < nsplit; ++q) s += __builtin_nontemporal_load(part + ((size_t)q * Mp + m) * N + n);
+        if (m < M) epi(m, n, s);
+      }
+  if (tid == 0) counters[tm * ntiles + tn] = 0;
+}
+
+}  // namespace
+
+SgemmShape sgemm_shape(int M, int N, int K) {
+  SgemmShape s;
+  s.mtiles = (M + SBM - 1) / SBM;
+  s.ntiles = N / SBN;
+  const int tiles = s.mtiles * s.ntiles;
+  const int kblocks = K / SKC;
+  int split = (512 + tiles - 1) / tiles;
+  if (split > kblocks) split = kblocks;
+  if (split < 1) split = 1;
+  const int per = (kblocks + split - 1) / split;
+  s.kchunk = per * SKC;
+  s.nsplit = (kblocks + per - 1) / per;
+  s.part_floats = s.nsplit > 1 ? (size_t)s.nsplit * s.mtiles * SBM * N : 0;
+  s.counters = s.mtiles * s.ntiles;
+  return s;
+}
+
+template <class Ld, class Epi>
+void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M, int N, int K,
+                  float* part, int* counters) {
+  if (M == 0) return;
+  const SgemmShape s = sgemm_shape(M, N, K);
+  hipLaunchKernelGGL((k_sgemm<Ld, Epi>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld, epi, W, M, N,
+                     K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part, counters);
+}
+
+#define INST(LD, EP)                                                                                   \
+  template void launch_sgemm<LD, EP>(hipStream_t, const LD&, const EP&, const bf16_t*, int, int, int, \
+                                     float*, int*);
+INST(LdRows, EpStore)
+INST(LdRows, EpResid)
+INST(LdLN, EpStore)
+INST(LdLN, EpGelu)
+INST(LdSeg3, EpStore)
+INST(LdZ, EpGelu)
+#undef INST
+
+}  // namespace clef

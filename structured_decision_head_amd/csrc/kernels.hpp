@@ -1,0 +1,144 @@
+// Internal launch interface between the host library and the gfx950 kernels.
+#pragma once
+#include "common.hpp"
+
+namespace clef {
+
+constexpr int kMaxOptions = 1024;   // options of one question (LDS arrays in the per-question kernels)
+
+// ---------------------------------------------------------------------------
+// row kernels
+// ---------------------------------------------------------------------------
+// tiles: int4 (first hidden row, first packed row, valid rows <= 256, record)
+void launch_rowstats_bf16(hipStream_t, const bf16_t* X, int H, const int4* tiles, int ntiles, float2* stats,
+                          float eps);
+// entries: int4 (first hidden row, length, first stats row, output slot)
+void launch_pool(hipStream_t, const bf16_t* X, int H, const int4* ent, int nent, const float2* stats,
+                 const float* gamma, const float* beta, float* out);
+// entries: int4 (first id, count, question slot, global slot)
+void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int nent, const int* ids,
+                      const float* pooled, float* ebar, float* prior);
+void launch_rowstats_f32(hipStream_t, const float* X, int M, float2* stats, float eps);
+
+// ---------------------------------------------------------------------------
+// big GEMMs (rows of the packed row space)
+// ---------------------------------------------------------------------------
+void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, const int4* tiles, int ntiles, const bf16_t* Wm,
+                     const float2* stats, const float* c, const float* d, bf16_t* mem);
+void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
+                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad);
+
+// ---------------------------------------------------------------------------
+// small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue
+// ---------------------------------------------------------------------------
+struct LdRows {          // A[m] = src[rows ? rows[m] : m]
+  const float* src;
+  int ld;
+  const int* rows;
+  DEV void load8(int m, int k, float* x) const {
+    const float* p = src + (size_t)(rows ? rows[m] : m) * ld + k;
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
+  const float* src;
+  int ld;
+  const float2* stats;
+  const float* g;
+  const float* b;
+  DEV void load8(int m, int k, float* x) const {
+    const float* p = src + (size_t)m * ld + k;
+    const float2 s = stats[m];
+    const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (v[i] - s.x) * s.y * g[k + i] + b[k + i];
+  }
+};
+
+struct LdSeg3 {          // A[m] = [p0[m] | p1[m] | p2[idx[m]]], each H wide
+  const float* p0;
+  const float* p1;
+  const float* p2;
+  const int* idx;
+  int H;
+  DEV void load8(int m, int k, float* x) const {
+    const int seg = k / H, c = k - seg * H;
+    const float* p = seg == 0 ? p0 + (size_t)m * H : seg == 1 ? p1 + (size_t)m * H : p2 + (size_t)idx[m] * H;
+    const float4 a = *reinterpret_cast<const float4*>(p + c), b = *reinterpret_cast<const float4*>(p + c + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m], each 1024 wide
+  const float* F;
+  const float* U;
+  const int* fq;
+  DEV void load8(int m, int k, float* x) const {
+    const int seg = k >> 10, c = k & 1023;
+    const float* fp = F + (size_t)fq[m] * 1024 + c;
+    const float* up = U + (size_t)m * 1024 + c;
+    const float4 f0 = *reinterpret_cast<const float4*>(fp), f1 = *reinterpret_cast<const float4*>(fp + 4);
+    const float4 u0 = *reinterpret_cast<const float4*>(up), u1 = *reinterpret_cast<const float4*>(up + 4);
+    const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x[i] = seg == 0 ? f[i] : seg == 1 ? u[i] : seg == 2 ? f[i] * u[i] : fabsf(f[i] - u[i]);
+  }
+};
+
+struct EpStore {         // C = acc + bias
+  float* C;
+  int ldc;
+  const float* bias;
+  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] = v + bias[n]; }
+};
+
+struct EpGelu {          // C = GELU(acc + bias)
+  float* C;
+  int ldc;
+  const float* bias;
+  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] = gelu_erf(v + bias[n]); }
+};
+
+struct EpResid {         // C += acc + bias (residual stream)
+  float* C;
+  int ldc;
+  const float* bias;
+  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] += v + bias[n]; }
+};
+
+struct SgemmShape {
+  int mtiles, ntiles, kchunk, nsplit, counters;
+  size_t part_floats;
+};
+SgemmShape sgemm_shape(int M, int N, int K);
+
+template <class Ld, class Epi>
+void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part,
+                  int* counters);
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+// rec: 8 ints per active record: kv0, n, o0, no, pbase, nc, q0, nq
+void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
+                       const int2* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                       long long Ptot);
+void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
+                          const int* opt_rec, const int* rec, int NO, float* out);
+void launch_field_attn(hipStream_t, const float* QKV, const int* rec, int nrec, float* out);
+
+// ---------------------------------------------------------------------------
+// aggregation and scoring
+// ---------------------------------------------------------------------------
+void launch_field_agg(hipStream_t, const float* U, const int* o_off, const float* sw, float sb, const float* qv,
+                      const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F);
+void launch_score(hipStream_t, const float* U, const float* F, const float* Hs, const float* w2, float b2,
+                  const float* prior, float gate, float lam, int joint, const int* o_off, int NQ, float* logits,
+                  float* probs, int* amax, float* jcos, float* mlp);
+
+}  // namespace clef
