@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the JointSchemaHead forward pass on one MI355X.
+
+One step = one clef_head_forward over one batch of the online-serving
+workload (B=8 records padded to L=4096, valid lengths U{2048..4096}, H=4096,
+8 fields per record, full 248320-row lexical table), with hidden states and
+the table already resident in HBM.  Prints one JSON line:
+records/s for the whole batch, per-stage GPU times from HIP events recorded on
+the forward's stream, the roofline of the dominant kernel, and the fp64 oracle
+timed on the host cores over a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+WORKLOADS = {
+    0: "single record: B=1, L=160, H=4096, 1 noul + 1 choice field, V=8192",
+    1: "online-serving batch: B=8, L=4096 padded, valid U{2048..4096}, H=4096, 8 fields/record "
+       "(3 noul, 3 choice of 2-6, 2 score of 5), V=248320",
+    2: "long state: B=1, L=16384, H=4096, 4 fields (15 options), V=248320",
+    3: "wide schema: B=4, L=8192, H=4096, 32 fields/record (8 noul, 16 choice of 4-16, 8 score), V=248320",
+    4: "heterogeneous large backbone: B=32, H=5120, valid log-uniform [512, 16384], 1-16 fields, V=248320",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "structured_decision_head_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(stage, cfg_index):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+    scaled by the copy-kernel calibration; None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_cfg{cfg_index}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != kernel_sources_sha(t.get("sources", [])):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the head shards by record with no exchange, and this build "
+              "runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd import synth
+    from structured_decision_head_amd.runner import HeadRunner
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    t = time.time()
+    case = synth.config_case(args.config)
+    b = case.batch
+    H, D = case.head.hidden_size, case.head.width
+    T = int(b.lengths.sum())
+    log(f"generated workload {args.config} in {time.time() - t:.1f}s: B={b.B} L={b.L} T={T} NQ={b.NQ} NO={b.NO}")
+
+    runner = HeadRunner(case)
+    runner.set_batch()
+    h = runner.handle
+    for _ in range(args.warmup):
+        runner.forward()
+    torch.cuda.synchronize()
+
+    # timed region: K forwards, host validation and table upload included
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner.forward()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"{ms_per_step * 1e3:.1f} us per forward")
+
+    # per-stage GPU time over the same number of forwards (events on the forward's stream)
+    C.clef_head_set_profiling(h, True)
+    for _ in range(args.steps):
+        runner.forward()
+    stage_ms, nfw = C.clef_head_stage_times(h)
+    C.clef_head_set_profiling(h, False)
+    stage_us = {k: v * 1e3 / nfw for k, v in stage_ms.items()}
+    log("stage us: " + ", ".join(f"{k}={v:.1f}" for k, v in stage_us.items()))
+    lg, pr, am = runner.outputs()
+
+    NR = case.head.routing_layers
+    gemm_flops = {"memory_gemm": 2.0 * T * H * D, "kv_gemm": 2.0 * T * D * (2 * D * NR)}
+    dominant = max(gemm_flops, key=lambda k: stage_us[k])
+    achieved = gemm_flops[dominant] / (stage_us[dominant] * 1e-6) / 1e12
+    traffic = load_traffic(dominant, args.config)
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    stages = {k: {"us": round(v, 2)} for k, v in stage_us.items()}
+    for k, fl in gemm_flops.items():
+        stages[k]["tflops"] = round(fl / (stage_us[k] * 1e-6) / 1e12, 1)
+    hid_bytes = 2.0 * T * H
+    stages["rowstats"]["gbs"] = round(hid_bytes / (stage_us["rowstats"] * 1e-6) / 1e9, 1)
+    kv_bytes = 2.0 * 2 * T * D * NR
+    stages["route_attn"]["gbs"] = round(kv_bytes / (stage_us["route_attn"] * 1e-6) / 1e9, 1)
+    lex_bytes = 2.0 * H * len(b.o_ids)
+    stages["lexical"]["gbs"] = round(lex_bytes / (stage_us["lexical"] * 1e-6) / 1e9, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import head as O
+        from threadpoolctl import threadpool_info
+        params = O.load_params(case.weights)
+        order = list(range(b.B))
+        done, t0 = [], time.perf_counter()
+        outs = []
+        for r in order:
+            outs.append(O.forward(case.weights, case.head, b, lambda ids: case.table[np.asarray(ids, np.int64)],
+                                  records=[r], params=params))
+            done.append(r)
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        # the sampled records also check the GPU outputs
+        o0 = [int(b.o_offsets[b.q_offsets[r]]) for r in done]
+        o1 = [int(b.o_offsets[b.q_offsets[r + 1]]) for r in done]
+        gl = np.concatenate([lg[a:c] for a, c in zip(o0, o1)])
+        gp = np.concatenate([pr[a:c] for a, c in zip(o0, o1)])
+        ol = np.concatenate([o[0] for o in outs])
+        op = np.concatenate([o[1] for o in outs])
+        cpu = {"value": round(len(done) / el, 3), "unit": "records/s", "cores": threads, "kind": "oracle",
+               "sample": f"records {done} of the same batch ({len(done)} of {b.B}), fp64 NumPy, {el:.1f}s",
+               "max_abs_dlogit_vs_gpu": float(np.abs(gl - ol).max()),
+               "max_abs_dprob_vs_gpu": float(np.abs(gp - op).max())}
+        log(f"oracle: {cpu}")
+
+    runner.close()
+    value = b.B / (ms_per_step * 1e-3)
+    line = {
+        "metric": "records/s (JointSchemaHead forward; also us/record)",
+        "value": round(value, 1),
+        "unit": "records/s",
+        "us_per_record": round(ms_per_step * 1e3 / b.B, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init head weights, N(0,1) hidden states, N(0,0.02) lexical table)",
+        "config": {"workload": f"cfg{args.config} " + WORKLOADS[args.config], "global_batch": int(b.B),
+                   "seq_len": int(b.L), "valid_rows": T, "questions": int(b.NQ), "options": int(b.NO)},
+        "roofline": roofline,
+        "stages": stages,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -181,6 +181,25 @@ CLEF_API int clef_head_weight_info(const clef_head_config *cfg, int32_t i, char 
 CLEF_API int clef_head_set_trace(clef_head *h, int32_t enable);
 CLEF_API int clef_head_trace(clef_head *h, int32_t which, void *host_dst, int64_t bytes);
 
+/* Per-stage GPU time of the following forwards, from HIP events recorded on
+ * the forward's stream between stages.  enable != 0 turns it on and clears
+ * the sums; while on, each forward waits for its own last event before
+ * returning.  clef_head_stage_times() writes the summed milliseconds of every
+ * stage (ms[CLEF_NUM_STAGES]) and the number of forwards summed. */
+#define CLEF_STAGE_ROWSTATS    0   /* LayerNorm statistics of the hidden rows */
+#define CLEF_STAGE_POOL        1   /* span means and global rows */
+#define CLEF_STAGE_LEXICAL     2   /* lexical gather-mean and prior */
+#define CLEF_STAGE_MEMORY_GEMM 3   /* memory projection (hidden width -> 1024) */
+#define CLEF_STAGE_KV_GEMM     4   /* K/V projections of every routing layer */
+#define CLEF_STAGE_QUERY_PROJ  5   /* option queries, question base, global projections */
+#define CLEF_STAGE_ROUTE_DENSE 6   /* routing layers: norms, Q / O / FFN maps */
+#define CLEF_STAGE_ROUTE_ATTN  7   /* routing cross-attention and its combine */
+#define CLEF_STAGE_FIELD       8   /* field aggregation and field transformer */
+#define CLEF_STAGE_SCORE       9   /* residual-MLP hidden layer, scoring, softmax, argmax */
+#define CLEF_NUM_STAGES       10
+CLEF_API int clef_head_set_profiling(clef_head *h, int32_t enable);
+CLEF_API int clef_head_stage_times(clef_head *h, double *ms, int64_t *forwards);
+
 #ifdef __cplusplus
 }
 #endif

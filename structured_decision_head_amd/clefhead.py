@@ -25,7 +25,9 @@ CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 
 
 EXPORTS = ("clef_head_create", "clef_head_forward", "clef_head_destroy", "clef_head_last_error",
            "clef_head_check_batch", "clef_head_span_rows", "clef_head_weight_count", "clef_head_weight_info",
-           "clef_head_set_trace", "clef_head_trace")
+           "clef_head_set_trace", "clef_head_trace", "clef_head_set_profiling", "clef_head_stage_times")
+STAGES = ("rowstats", "pool", "lexical", "memory_gemm", "kv_gemm", "query_proj", "route_dense", "route_attn",
+          "field", "score")
 
 
 class ClefError(RuntimeError):
@@ -81,6 +83,8 @@ def load() -> ctypes.CDLL:
                                         ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]
     L.clef_head_set_trace.argtypes = [_P, ctypes.c_int32]
     L.clef_head_trace.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_int64]
+    L.clef_head_set_profiling.argtypes = [_P, ctypes.c_int32]
+    L.clef_head_stage_times.argtypes = [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     _lib = L
     return L
 
@@ -197,3 +201,15 @@ def clef_head_set_trace(handle: int, enable: bool):
 def clef_head_trace(handle: int, which: int, out: np.ndarray) -> np.ndarray:
     _check(load().clef_head_trace(handle, which, out.ctypes.data, out.nbytes))
     return out
+
+
+def clef_head_set_profiling(handle: int, enable: bool):
+    _check(load().clef_head_set_profiling(handle, 1 if enable else 0))
+
+
+def clef_head_stage_times(handle: int):
+    """(dict stage -> summed ms, number of forwards)."""
+    ms = (ctypes.c_double * len(STAGES))()
+    n = ctypes.c_int64()
+    _check(load().clef_head_stage_times(handle, ms, ctypes.byref(n)))
+    return {k: ms[i] for i, k in enumerate(STAGES)}, n.value

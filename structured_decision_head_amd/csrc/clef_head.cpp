@@ -374,6 +374,11 @@ struct clef_head {
   float *pooled = nullptr, *ebar = nullptr, *prior = nullptr;
   bf16_t* mem = nullptr;
   float *tr_u = nullptr, *tr_f0 = nullptr, *tr_f = nullptr, *tr_jcos = nullptr, *tr_mlp = nullptr;
+  // stage timing
+  bool prof = false;
+  std::vector<hipEvent_t> ev;
+  double stage_ms[CLEF_NUM_STAGES] = {};
+  int64_t prof_calls = 0;
 };
 
 namespace {
@@ -567,7 +572,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 // workspace layout for one plan
 struct WsLayout {
   size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, gp, f, fstats, qkv, fattn, hs, pm,
-      pl, po, part, counters, total;
+      pl, po, part, total;
 };
 
 WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
@@ -598,7 +603,6 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.pl = take((size_t)NH * p.Ptot * 4);
   L.po = take((size_t)NH * p.Ptot * 64 * 4);
   size_t part = 0;
-  int cnt = 0;
   const int shapes[][3] = {{p.NO, D, 3 * (int)H}, {p.NQ, D, (int)H}, {p.nact, D, (int)H}, {p.NO, D, D},
                            {p.NO, F, D},        {p.NO, D, F},        {p.NQ, 3 * D, D},     {p.NQ, D, D},
                            {p.NQ, F, D},        {p.NQ, D, F},        {p.NO, D, 4 * D}};
@@ -606,10 +610,8 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
     if (s[0] == 0) continue;
     const SgemmShape g = sgemm_shape(s[0], s[1], s[2]);
     part = std::max(part, g.part_floats);
-    cnt = std::max(cnt, g.counters);
   }
   L.part = take(part * 4);
-  L.counters = take((size_t)std::max(cnt, 1) * 4);
   L.total = o;
   return L;
 }
@@ -693,6 +695,7 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
 
 void clef_head_destroy(clef_head* h) {
   if (!h) return;
+  for (auto e : h->ev) (void)hipEventDestroy(e);
   if (h->staged) {
     if (h->staged_pending) (void)hipEventSynchronize(h->staged);
     (void)hipEventDestroy(h->staged);
@@ -702,6 +705,21 @@ void clef_head_destroy(clef_head* h) {
   if (h->pinned) (void)hipHostFree(h->pinned);
   if (h->dweights) (void)hipFree(h->dweights);
   delete h;
+}
+
+int clef_head_set_profiling(clef_head* h, int32_t enable) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  h->prof = enable != 0;
+  for (double& x : h->stage_ms) x = 0.0;
+  h->prof_calls = 0;
+  return CLEF_OK;
+}
+
+int clef_head_stage_times(clef_head* h, double* ms, int64_t* forwards) {
+  if (!h || !ms) return fail(CLEF_E_ARG, "NULL argument");
+  for (int i = 0; i < CLEF_NUM_STAGES; ++i) ms[i] = h->stage_ms[i];
+  if (forwards) *forwards = h->prof_calls;
+  return CLEF_OK;
 }
 
 int clef_head_set_trace(clef_head* h, int32_t enable) {
@@ -765,7 +783,6 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     const size_t want = L.total + L.total / 4;
     if (hipMalloc(&h->ws, want) != hipSuccess) return fail(CLEF_E_NOMEM, "workspace hipMalloc of %zu bytes failed", want);
     h->ws_bytes = want;
-    HIPCHK(hipMemset(h->ws, 0, want));   // split-K tile counters start at zero and are reset by their kernels
   }
   const size_t tab_bytes = p.tab.size() * 4;
   if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
@@ -844,42 +861,66 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   float* pl = reinterpret_cast<float*>(ws + L.pl);
   float* po = reinterpret_cast<float*>(ws + L.po);
   float* part = reinterpret_cast<float*>(ws + L.part);
-  int* counters = reinterpret_cast<int*>(ws + L.counters);
   const bf16_t* X = static_cast<const bf16_t*>(batch->hidden);
   const Weights& W = h->w;
   const float eps = c.ln_eps;
   const bool joint = W.gate != 0.0f;
 
+  // stage timing: an event at every stage boundary, on the forward's stream
+  std::vector<int> marks;
+  auto mark = [&](int stage) -> int {
+    if (!h->prof) return CLEF_OK;
+    if (h->ev.size() <= marks.size()) {
+      hipEvent_t e;
+      HIPCHK(hipEventCreate(&e));
+      h->ev.push_back(e);
+    }
+    HIPCHK(hipEventRecord(h->ev[marks.size()], st));
+    marks.push_back(stage);
+    return CLEF_OK;
+  };
+#define MARK(s) do { int rc_ = mark(s); if (rc_) return rc_; } while (0)
+  MARK(-1);
+
   // step 1: row statistics, pooled vectors, lexical vectors and prior
   launch_rowstats_bf16(st, X, (int)H, tiles, p.ntiles, stats, eps);
+  MARK(CLEF_STAGE_ROWSTATS);
   launch_pool(st, X, (int)H, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
+  MARK(CLEF_STAGE_POOL);
   launch_lex_prior(st, h->table, (int)H, lex, NO, ids, pooled, ebar, prior);
+  MARK(CLEF_STAGE_LEXICAL);
 
   if (joint) {
     // step 2: memory and K/V of every routing layer
     if (NR > 0) {
       launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
+      MARK(CLEF_STAGE_MEMORY_GEMM);
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
+      MARK(CLEF_STAGE_KV_GEMM);
     }
     // step 3: option queries, question base and global projections
     launch_sgemm(st, LdSeg3{pooled + (size_t)NQ * H, ebar, pooled, optq, (int)H}, EpStore{u, D, W.ba7}, W.Wa7, NO, D,
-                 3 * (int)H, part, counters);
-    launch_sgemm(st, LdRows{pooled, (int)H, nullptr}, EpStore{qv, D, W.bqb}, W.Wqb, NQ, D, (int)H, part, counters);
+                 3 * (int)H, part);
+    launch_sgemm(st, LdRows{pooled, (int)H, nullptr}, EpStore{qv, D, W.bqb}, W.Wqb, NQ, D, (int)H, part);
     launch_sgemm(st, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
-                 (int)H, part, counters);
+                 (int)H, part);
+    MARK(CLEF_STAGE_QUERY_PROJ);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_u, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
     for (int r = 0; r < NR; ++r) {
       const Layer& Ly = W.route[r];
       const bf16_t* Kl = kv + (size_t)(2 * r) * NH * p.Tpad * 64;
       const bf16_t* Vl = kv + (size_t)(2 * r + 1) * NH * p.Tpad * 64;
       launch_rowstats_f32(st, u, NO, ustats, eps);
-      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part, counters);
+      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
+      MARK(CLEF_STAGE_ROUTE_DENSE);
       launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot);
       launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
-      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, counters);
+      MARK(CLEF_STAGE_ROUTE_ATTN);
+      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part);
       launch_rowstats_f32(st, u, NO, ustats, eps);
-      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part, counters);
-      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part, counters);
+      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part);
+      MARK(CLEF_STAGE_ROUTE_DENSE);
       if (h->trace)
         HIPCHK(hipMemcpyAsync(h->tr_u + (size_t)(r + 1) * NO * D, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
     }
@@ -889,21 +930,32 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     for (int l = 0; l < NL; ++l) {
       const Layer& Ly = W.field[l];
       launch_rowstats_f32(st, f, NQ, fstats, eps);
-      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, EpStore{qkv, 3 * D, Ly.bqkv}, Ly.Wqkv, NQ, 3 * D, D, part,
-                   counters);
+      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, EpStore{qkv, 3 * D, Ly.bqkv}, Ly.Wqkv, NQ, 3 * D, D, part);
       launch_field_attn(st, qkv, rec, p.nact, fattn);
-      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, counters);
+      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part);
       launch_rowstats_f32(st, f, NQ, fstats, eps);
-      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part, counters);
-      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part, counters);
+      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part);
     }
+    MARK(CLEF_STAGE_FIELD);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     // step 5: residual-MLP hidden layer over [f, u, f*u, |f-u|]
-    launch_sgemm(st, LdZ{f, u, optq}, EpGelu{hs, D, W.bs1}, W.Ws1, NO, D, 4 * D, part, counters);
+    launch_sgemm(st, LdZ{f, u, optq}, EpGelu{hs, D, W.bs1}, W.Ws1, NO, D, 4 * D, part);
   }
   launch_score(st, u, f, hs, W.ws2, W.bs2, prior, W.gate, W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
                h->trace && joint ? h->tr_jcos : nullptr, h->trace && joint ? h->tr_mlp : nullptr);
+  MARK(CLEF_STAGE_SCORE);
+#undef MARK
   HIPCHK(hipGetLastError());
+  if (h->prof) {
+    HIPCHK(hipEventSynchronize(h->ev[marks.size() - 1]));
+    for (size_t i = 1; i < marks.size(); ++i) {
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, h->ev[i - 1], h->ev[i]));
+      h->stage_ms[marks[i]] += ms;
+    }
+    ++h->prof_calls;
+  }
 
   h->last_stream = st;
   h->last_NQ = NQ;

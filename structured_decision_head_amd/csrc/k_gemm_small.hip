@@ -3,7 +3,7 @@
 // first layer.  M is the number of options or questions (5 to ~1100), N and K
 // are 1024..15360; these are weight streams, so the work is split along K
 // until the grid fills the chip and the partial sums are reduced by the last
-// workgroup of each tile, in a fixed order (deterministic).
+// second kernel that adds the slices in a fixed order (deterministic).
 //
 // Precision: activations are fp32; each 8-element group is split into
 // hi = bf16(x) and lo = bf16(x - hi) and both are multiplied against the exact
@@ -23,9 +23,8 @@ constexpr int SBM = 64, SBN = 128, SKC = 128;
 template <class Ld, class Epi>
 __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __restrict__ W, int M, int N,
                                                int K, int kchunk, int mtiles, int ntiles, int nsplit,
-                                               float* __restrict__ part, int* __restrict__ counters) {
+                                               float* __restrict__ part) {
   __shared__ uint4 sAh[SBM * 16], sAl[SBM * 16];   // [row * 16 + swizzled chunk], KC = 128 bf16 per row
-  __shared__ int s_last;
 
   const int lt = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = lt % mtiles;
@@ -103,6 +102,8 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
     return;
   }
 
+  // split-K: every workgroup writes its partial tile; k_splitk_reduce sums the
+  // slices in order in a second launch (the kernel boundary orders the writes)
   const size_t Mp = (size_t)mtiles * SBM;
   float* P = part + (size_t)ks * Mp * N;
 #pragma unroll
@@ -115,25 +116,25 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
         const int n = n0 + w * 32 + cb * 16 + (lane & 15);
         P[(size_t)m * N + n] = acc[rb][cb][e];
       }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counters[tm * ntiles + tn], 1) == nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
-        const int n = n0 + w * 32 + cb * 16 + (lane & 15);
-        float s = 0.f;
-        for (int q = 0; q < nsplit; ++q) s += __builtin_nontemporal_load(part + ((size_t)q * Mp + m) * N + n);
-        if (m < M) epi(m, n, s);
-      }
-  if (tid == 0) counters[tm * ntiles + tn] = 0;
+}
+
+// Sum the split-K slices in a fixed order and apply the epilogue; one thread
+// per 4 consecutive outputs.
+template <class Epi>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int nsplit, size_t Mp, int M,
+                                                       int N, Epi epi) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (size_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+  float4 s = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
+  for (int q = 1; q < nsplit; ++q) {
+    const float4 t = *reinterpret_cast<const float4*>(part + ((size_t)q * Mp + m) * N + n);
+    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+  }
+  epi(m, n, s.x);
+  epi(m, n + 1, s.y);
+  epi(m, n + 2, s.z);
+  epi(m, n + 3, s.w);
 }
 
 }  // namespace
@@ -145,28 +146,33 @@ SgemmShape sgemm_shape(int M, int N, int K) {
   const int tiles = s.mtiles * s.ntiles;
   const int kblocks = K / SKC;
   int split = (512 + tiles - 1) / tiles;
+  if (split > 16) split = 16;
   if (split > kblocks) split = kblocks;
   if (split < 1) split = 1;
   const int per = (kblocks + split - 1) / split;
   s.kchunk = per * SKC;
   s.nsplit = (kblocks + per - 1) / per;
   s.part_floats = s.nsplit > 1 ? (size_t)s.nsplit * s.mtiles * SBM * N : 0;
-  s.counters = s.mtiles * s.ntiles;
   return s;
 }
 
 template <class Ld, class Epi>
 void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M, int N, int K,
-                  float* part, int* counters) {
+                  float* part) {
   if (M == 0) return;
   const SgemmShape s = sgemm_shape(M, N, K);
   hipLaunchKernelGGL((k_sgemm<Ld, Epi>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld, epi, W, M, N,
-                     K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part, counters);
+                     K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part);
+  if (s.nsplit > 1) {
+    const size_t n4 = (size_t)M * N / 4;
+    hipLaunchKernelGGL((k_splitk_reduce<Epi>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, s.nsplit,
+                       (size_t)s.mtiles * SBM, M, N, epi);
+  }
 }
 
 #define INST(LD, EP)                                                                                   \
   template void launch_sgemm<LD, EP>(hipStream_t, const LD&, const EP&, const bf16_t*, int, int, int, \
-                                     float*, int*);
+                                     float*);
 INST(LdRows, EpStore)
 INST(LdRows, EpResid)
 INST(LdLN, EpStore)

@@ -112,14 +112,13 @@ struct EpResid {         // C += acc + bias (residual stream)
 };
 
 struct SgemmShape {
-  int mtiles, ntiles, kchunk, nsplit, counters;
+  int mtiles, ntiles, kchunk, nsplit;
   size_t part_floats;
 };
 SgemmShape sgemm_shape(int M, int N, int K);
 
 template <class Ld, class Epi>
-void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part,
-                  int* counters);
+void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part);
 
 // ---------------------------------------------------------------------------
 // attention

@@ -137,11 +137,16 @@ def test_determinism_and_batch_composition(torch_gpu):
     b = r.outputs()
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+    # a record alone: the split-K partition of the small GEMMs depends on the
+    # batch's row count, so only fp32 summation order may differ
+    ref = oracle_outputs(case)
     for rec in range(case.batch.B):
         sub = case.batch.record(rec)
         r.set_batch(sub)
         r.forward()
-        lg, pr, am = r.outputs()
+        alone = r.outputs()
         l2, p2, a2 = select(case.batch, [rec], *a)
-        assert np.abs(lg - l2).max() < 1e-4 and np.abs(pr - p2).max() < 1e-5
+        say(f"  record {rec}: alone vs in batch max|dlogit|={np.abs(alone[0] - l2).max():.2e}")
+        assert np.abs(alone[0] - l2).max() < 1e-3 and np.abs(alone[1] - p2).max() < 2e-4
+        compare(f"record {rec} alone", alone, select(case.batch, [rec], *ref), sub.o_offsets)
     r.close()
