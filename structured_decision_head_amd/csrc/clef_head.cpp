@@ -608,7 +608,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
                            {p.NQ, F, D},        {p.NQ, D, F},        {p.NO, D, 4 * D}};
   for (auto& s : shapes) {
     if (s[0] == 0) continue;
-    const SgemmShape g = sgemm_shape(s[0], s[1], s[2]);
+    const SgemmShape g = sgemm_shape(s[0], s[1], s[2], s[1] == D);
     part = std::max(part, g.part_floats);
   }
   L.part = take(part * 4);
@@ -898,9 +898,9 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
       MARK(CLEF_STAGE_KV_GEMM);
     }
-    // step 3: option queries, question base and global projections
+    // step 3: option queries (with the first routing LayerNorm statistics), question base and global projections
     launch_sgemm(st, LdSeg3{pooled + (size_t)NQ * H, ebar, pooled, optq, (int)H}, EpStore{u, D, W.ba7}, W.Wa7, NO, D,
-                 3 * (int)H, part);
+                 3 * (int)H, part, ustats, eps);
     launch_sgemm(st, LdRows{pooled, (int)H, nullptr}, EpStore{qv, D, W.bqb}, W.Wqb, NQ, D, (int)H, part);
     launch_sgemm(st, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
                  (int)H, part);
@@ -910,32 +910,30 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
       const Layer& Ly = W.route[r];
       const bf16_t* Kl = kv + (size_t)(2 * r) * NH * p.Tpad * 64;
       const bf16_t* Vl = kv + (size_t)(2 * r + 1) * NH * p.Tpad * 64;
-      launch_rowstats_f32(st, u, NO, ustats, eps);
       launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
       MARK(CLEF_STAGE_ROUTE_DENSE);
       launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot);
       launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
       MARK(CLEF_STAGE_ROUTE_ATTN);
-      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part);
-      launch_rowstats_f32(st, u, NO, ustats, eps);
+      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, ustats, eps);
       launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part);
-      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part,
+                   r + 1 < NR ? ustats : nullptr, eps);
       MARK(CLEF_STAGE_ROUTE_DENSE);
       if (h->trace)
         HIPCHK(hipMemcpyAsync(h->tr_u + (size_t)(r + 1) * NO * D, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
     }
-    // step 4: field vectors and the field transformer
-    launch_field_agg(st, u, ooff, W.sw, W.sb, qv, gp, qrec, qtype, W.temb, NQ, f);
+    // step 4: field vectors (with the first field LayerNorm statistics) and the field transformer
+    launch_field_agg(st, u, ooff, W.sw, W.sb, qv, gp, qrec, qtype, W.temb, NQ, f, fstats, eps);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f0, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     for (int l = 0; l < NL; ++l) {
       const Layer& Ly = W.field[l];
-      launch_rowstats_f32(st, f, NQ, fstats, eps);
       launch_sgemm(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, EpStore{qkv, 3 * D, Ly.bqkv}, Ly.Wqkv, NQ, 3 * D, D, part);
       launch_field_attn(st, qkv, rec, p.nact, fattn);
-      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part);
-      launch_rowstats_f32(st, f, NQ, fstats, eps);
+      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps);
       launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part);
-      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part);
+      launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part,
+                   l + 1 < NL ? fstats : nullptr, eps);
     }
     MARK(CLEF_STAGE_FIELD);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));

@@ -11,8 +11,8 @@
 // probabilities are already in the B-operand layout of the second product.
 //
 // Field self-attention (clef-4bit page §三 step 3): every field of a record
-// attends to every field of the same record; tiny (<= a few dozen fields), so
-// plain fp32 with an online softmax, one lane per query.
+// attends to every field of the same record; tiny (a few dozen fields), so
+// plain fp32 with an online softmax.
 #include "kernels.hpp"
 
 namespace clef {
@@ -174,61 +174,80 @@ void launch_route_combine(hipStream_t st, const float* pm, const float* pl, cons
                      out);
 }
 
-// Field self-attention: one 64-lane block per (record, head); QKV rows are
-// [q | k | v] of width 3 x 1024.
-__global__ __launch_bounds__(64) void k_field_attn(const float* __restrict__ QKV, const int* __restrict__ rec,
-                                                   float* __restrict__ out) {
-  __shared__ float sK[64][65], sV[64][65];
-  const int lane = threadIdx.x;
+// Field self-attention: one 256-thread block per (record, head).  Thread t
+// owns query row t / 4 of a 64-row block and 16 of its 64 dims (t % 4); a score
+// is the sum of the four partial dot products (two lane exchanges).  Keys and
+// values are staged in LDS 64 rows at a time with an online softmax, so any
+// number of fields works.  QKV rows are [q | k | v] of width 3 x 1024.
+__global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QKV, const int* __restrict__ rec,
+                                                    float* __restrict__ out) {
+  __shared__ float4 sK[64][16], sV[64][16];
   const int* R = rec + 8 * blockIdx.x;
   const int q0 = R[6], nq = R[7];
   const int j = blockIdx.y;
-  const float scale = 0.125f;
+  const int t = threadIdx.x, qi_l = t >> 2, part = t & 3;
   for (int qb = 0; qb < nq; qb += 64) {
-    const int qi = qb + lane;
+    const int qi = qb + qi_l;
     const bool valid = qi < nq;
-    float q[64], o[64];
-    const float* qp = QKV + (size_t)(q0 + (valid ? qi : 0)) * 3072 + j * 64;
+    float4 q[4], o[4];
+    const float* qp = QKV + (size_t)(q0 + (valid ? qi : 0)) * 3072 + j * 64 + part * 16;
 #pragma unroll
-    for (int d = 0; d < 64; ++d) {
-      q[d] = qp[d] * scale;
-      o[d] = 0.f;
+    for (int c = 0; c < 4; ++c) {
+      q[c] = *reinterpret_cast<const float4*>(qp + 4 * c);
+      q[c].x *= 0.125f; q[c].y *= 0.125f; q[c].z *= 0.125f; q[c].w *= 0.125f;
+      o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float m = -INFINITY, l = 0.f;
     for (int kb = 0; kb < nq; kb += 64) {
       const int nk = min(64, nq - kb);
       __syncthreads();
-      for (int t = 0; t < nk; ++t) {
-        const float* rp = QKV + (size_t)(q0 + kb + t) * 3072 + j * 64;
-        sK[t][lane] = rp[1024 + lane];
-        sV[t][lane] = rp[2048 + lane];
+      // 64 rows x 16 float4 each for K and V: 4 float4 per thread
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int idx = t + 256 * r, row = idx >> 4, c4 = idx & 15;
+        if (row < nk) {
+          const float* rp = QKV + (size_t)(q0 + kb + row) * 3072 + j * 64 + 4 * c4;
+          sK[row][c4] = *reinterpret_cast<const float4*>(rp + 1024);
+          sV[row][c4] = *reinterpret_cast<const float4*>(rp + 2048);
+        }
       }
       __syncthreads();
-      for (int t = 0; t < nk; ++t) {
+      for (int tk = 0; tk < nk; ++tk) {
         float s = 0.f;
 #pragma unroll
-        for (int d = 0; d < 64; ++d) s += q[d] * sK[t][d];
+        for (int c = 0; c < 4; ++c) {
+          const float4 k = sK[tk][part * 4 + c];
+          s += q[c].x * k.x + q[c].y * k.y + q[c].z * k.z + q[c].w * k.w;
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
         const float mn = fmaxf(m, s);
-        const float a = expf(m - mn);
-        const float p = expf(s - mn);
+        const float a = expf(m - mn), p = expf(s - mn);
         l = l * a + p;
-#pragma unroll
-        for (int d = 0; d < 64; ++d) o[d] = o[d] * a + p * sV[t][d];
         m = mn;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 v = sV[tk][part * 4 + c];
+          o[c].x = o[c].x * a + p * v.x;
+          o[c].y = o[c].y * a + p * v.y;
+          o[c].z = o[c].z * a + p * v.z;
+          o[c].w = o[c].w * a + p * v.w;
+        }
       }
     }
     if (valid) {
-      float* op = out + (size_t)(q0 + qi) * 1024 + j * 64;
       const float inv = 1.0f / l;
+      float* op = out + (size_t)(q0 + qi) * 1024 + j * 64 + part * 16;
 #pragma unroll
-      for (int d = 0; d < 64; ++d) op[d] = o[d] * inv;
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(op + 4 * c) = make_float4(o[c].x * inv, o[c].y * inv, o[c].z * inv, o[c].w * inv);
     }
   }
 }
 
 void launch_field_attn(hipStream_t st, const float* QKV, const int* rec, int nrec, float* out) {
   if (nrec == 0) return;
-  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(64), 0, st, QKV, rec, out);
+  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(256), 0, st, QKV, rec, out);
 }
 
 }  // namespace clef

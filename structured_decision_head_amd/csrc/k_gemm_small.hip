@@ -119,27 +119,32 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
 }
 
 // Sum the split-K slices in a fixed order and apply the epilogue; one thread
-// per 4 consecutive outputs.
+// per 4 consecutive outputs.  With stats (N = 1024, one block per row) the
+// block also computes the two-pass LayerNorm statistics of the row it wrote.
 template <class Epi>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int nsplit, size_t Mp, int M,
-                                                       int N, Epi epi) {
+                                                       int N, Epi epi, float2* __restrict__ stats, float eps) {
+  __shared__ float sm[4];
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= (size_t)M * N) return;
+  if (stats == nullptr && i >= (size_t)M * N) return;
   const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
   float4 s = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
   for (int q = 1; q < nsplit; ++q) {
     const float4 t = *reinterpret_cast<const float4*>(part + ((size_t)q * Mp + m) * N + n);
     s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
   }
-  epi(m, n, s.x);
-  epi(m, n + 1, s.y);
-  epi(m, n + 2, s.z);
-  epi(m, n + 3, s.w);
+  const float a = epi(m, n, s.x), b = epi(m, n + 1, s.y), c = epi(m, n + 2, s.z), d = epi(m, n + 3, s.w);
+  if (stats != nullptr) {
+    const float mu = block_sum<4>((a + b) + (c + d), sm) * (1.0f / 1024);
+    const float va = block_sum<4>((a - mu) * (a - mu) + (b - mu) * (b - mu) + (c - mu) * (c - mu) + (d - mu) * (d - mu),
+                                  sm) * (1.0f / 1024);
+    if (threadIdx.x == 0) stats[m] = make_float2(mu, 1.0f / sqrtf(va + eps));
+  }
 }
 
 }  // namespace
 
-SgemmShape sgemm_shape(int M, int N, int K) {
+SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
   SgemmShape s;
   s.mtiles = (M + SBM - 1) / SBM;
   s.ntiles = N / SBN;
@@ -149,6 +154,7 @@ SgemmShape sgemm_shape(int M, int N, int K) {
   if (split > 16) split = 16;
   if (split > kblocks) split = kblocks;
   if (split < 1) split = 1;
+  if (need_reduce && split < 2) split = 2;
   const int per = (kblocks + split - 1) / split;
   s.kchunk = per * SKC;
   s.nsplit = (kblocks + per - 1) / per;
@@ -158,21 +164,21 @@ SgemmShape sgemm_shape(int M, int N, int K) {
 
 template <class Ld, class Epi>
 void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M, int N, int K,
-                  float* part) {
+                  float* part, float2* stats, float eps) {
   if (M == 0) return;
-  const SgemmShape s = sgemm_shape(M, N, K);
+  const SgemmShape s = sgemm_shape(M, N, K, stats != nullptr);
   hipLaunchKernelGGL((k_sgemm<Ld, Epi>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld, epi, W, M, N,
                      K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part);
   if (s.nsplit > 1) {
     const size_t n4 = (size_t)M * N / 4;
     hipLaunchKernelGGL((k_splitk_reduce<Epi>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, s.nsplit,
-                       (size_t)s.mtiles * SBM, M, N, epi);
+                       (size_t)s.mtiles * SBM, M, N, epi, stats, eps);
   }
 }
 
 #define INST(LD, EP)                                                                                   \
   template void launch_sgemm<LD, EP>(hipStream_t, const LD&, const EP&, const bf16_t*, int, int, int, \
-                                     float*);
+                                     float*, float2*, float);
 INST(LdRows, EpStore)
 INST(LdRows, EpResid)
 INST(LdLN, EpStore)

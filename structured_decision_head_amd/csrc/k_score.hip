@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void k_field_agg(const float* __restrict__ U, 
                                                    const float* __restrict__ sw, float sb,
                                                    const float* __restrict__ qv, const float* __restrict__ gp,
                                                    const int* __restrict__ q_rec, const int* __restrict__ q_type,
-                                                   const float* __restrict__ temb, float* __restrict__ F) {
+                                                   const float* __restrict__ temb, float* __restrict__ F,
+                                                   float2* __restrict__ fstats, float eps) {
   __shared__ float sm[4];
   __shared__ float sc[kMaxOptions];
   const int q = blockIdx.x;
@@ -54,12 +55,19 @@ __global__ __launch_bounds__(256) void k_field_agg(const float* __restrict__ U, 
   r.z = a.z + acc.z + g.z + t.z;
   r.w = a.w + acc.w + g.w + t.w;
   *reinterpret_cast<float4*>(F + (size_t)q * 1024 + e) = r;
+  // LayerNorm statistics of the new field row (input of the first field layer)
+  const float mu = block_sum<4>((r.x + r.y) + (r.z + r.w), sm) * (1.0f / 1024);
+  const float va = block_sum<4>((r.x - mu) * (r.x - mu) + (r.y - mu) * (r.y - mu) + (r.z - mu) * (r.z - mu) +
+                                    (r.w - mu) * (r.w - mu), sm) * (1.0f / 1024);
+  if (threadIdx.x == 0) fstats[q] = make_float2(mu, 1.0f / sqrtf(va + eps));
 }
 
 void launch_field_agg(hipStream_t st, const float* U, const int* o_off, const float* sw, float sb, const float* qv,
-                      const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F) {
+                      const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F,
+                      float2* fstats, float eps) {
   if (NQ == 0) return;
-  hipLaunchKernelGGL(k_field_agg, dim3(NQ), dim3(256), 0, st, U, o_off, sw, sb, qv, gp, q_rec, q_type, temb, F);
+  hipLaunchKernelGGL(k_field_agg, dim3(NQ), dim3(256), 0, st, U, o_off, sw, sb, qv, gp, q_rec, q_type, temb, F,
+                     fstats, eps);
 }
 
 // One block per question.  Hs = GELU(W1 z + b1) rows [NO][1024] (unused when

@@ -90,35 +90,53 @@ struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m]
   }
 };
 
+// Epilogues store one output and return the stored value.
 struct EpStore {         // C = acc + bias
   float* C;
   int ldc;
   const float* bias;
-  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] = v + bias[n]; }
+  DEV float operator()(int m, int n, float v) const {
+    const float r = v + bias[n];
+    C[(size_t)m * ldc + n] = r;
+    return r;
+  }
 };
 
 struct EpGelu {          // C = GELU(acc + bias)
   float* C;
   int ldc;
   const float* bias;
-  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] = gelu_erf(v + bias[n]); }
+  DEV float operator()(int m, int n, float v) const {
+    const float r = gelu_erf(v + bias[n]);
+    C[(size_t)m * ldc + n] = r;
+    return r;
+  }
 };
 
 struct EpResid {         // C += acc + bias (residual stream)
   float* C;
   int ldc;
   const float* bias;
-  DEV void operator()(int m, int n, float v) const { C[(size_t)m * ldc + n] += v + bias[n]; }
+  DEV float operator()(int m, int n, float v) const {
+    float* p = C + (size_t)m * ldc + n;
+    const float r = *p + (v + bias[n]);
+    *p = r;
+    return r;
+  }
 };
 
 struct SgemmShape {
   int mtiles, ntiles, kchunk, nsplit;
   size_t part_floats;
 };
-SgemmShape sgemm_shape(int M, int N, int K);
+// need_reduce: always split K (>= 2 slices) so that a reduction pass runs
+SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce = false);
 
+// stats != nullptr (N must be 1024): the reduction pass also writes the
+// LayerNorm statistics (mean, 1/sqrt(var + eps)) of every finished output row.
 template <class Ld, class Epi>
-void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part);
+void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part,
+                  float2* stats = nullptr, float eps = 0.f);
 
 // ---------------------------------------------------------------------------
 // attention
@@ -135,7 +153,8 @@ void launch_field_attn(hipStream_t, const float* QKV, const int* rec, int nrec, 
 // aggregation and scoring
 // ---------------------------------------------------------------------------
 void launch_field_agg(hipStream_t, const float* U, const int* o_off, const float* sw, float sb, const float* qv,
-                      const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F);
+                      const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F,
+                      float2* fstats, float eps);
 void launch_score(hipStream_t, const float* U, const float* F, const float* Hs, const float* w2, float b2,
                   const float* prior, float gate, float lam, int joint, const int* o_off, int NQ, float* logits,
                   float* probs, int* amax, float* jcos, float* mlp);
