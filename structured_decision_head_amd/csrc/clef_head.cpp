@@ -342,8 +342,8 @@ struct Layer {
 };
 
 struct Weights {
-  const float *lnin_g, *lnin_b, *cmem, *dmem, *ba7, *bqb, *bg, *temb, *sw, *bkv, *bs1, *ws2;
-  const bf16_t *Wmem, *Wa7, *Wqb, *Wg, *Wkv, *Ws1;
+  const float *lnin_g, *lnin_b, *cmem, *dmem, *ba7, *bqq, *bg, *temb, *sw, *bkv, *bs1, *ws2;
+  const bf16_t *Wmem, *Wa7, *Wqq, *Wg, *Wkv, *Ws1;
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -362,6 +362,8 @@ struct clef_head {
   void* pinned = nullptr;
   size_t pinned_bytes = 0;
   hipEvent_t staged = nullptr;
+  hipStream_t side = nullptr;            // second stream for the work independent of the big GEMMs
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool staged_pending = false;
   // trace
   bool trace = false;
@@ -462,25 +464,31 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     put_f(cm, &W.cmem);
     put_f(dm, &W.dmem);
   }
-  // option-query projection: [W_c | W_l | W_qo] along K, biases summed
+  // option-query projection: [W_c | W_l] along K with the three biases summed; the
+  // question term W_qo q depends only on the question, so it is computed once per
+  // question, stacked under the field base projection: [W_q ; W_qo] (bias [b_q ; 0])
   {
-    std::vector<uint16_t> Wa((size_t)D * 3 * H);
+    std::vector<uint16_t> Wa((size_t)D * 2 * H);
     const uint16_t* a = bf("opt_ctx.w");
     const uint16_t* l = bf("opt_lex.w");
-    const uint16_t* q = bf("q_opt.w");
     for (int j = 0; j < D; ++j) {
-      memcpy(&Wa[(size_t)j * 3 * H], a + (size_t)j * H, H * 2);
-      memcpy(&Wa[(size_t)j * 3 * H + H], l + (size_t)j * H, H * 2);
-      memcpy(&Wa[(size_t)j * 3 * H + 2 * H], q + (size_t)j * H, H * 2);
+      memcpy(&Wa[(size_t)j * 2 * H], a + (size_t)j * H, H * 2);
+      memcpy(&Wa[(size_t)j * 2 * H + H], l + (size_t)j * H, H * 2);
     }
     put_bf(Wa.data(), Wa.size(), &W.Wa7);
     const auto b1 = tof("opt_ctx.b"), b2 = tof("opt_lex.b"), b3 = tof("q_opt.b");
     std::vector<float> bs(D);
     for (int j = 0; j < D; ++j) bs[j] = (float)((double)b1[j] + b2[j] + b3[j]);
     put_f(bs, &W.ba7);
+    std::vector<uint16_t> Wq((size_t)2 * D * H);
+    memcpy(Wq.data(), bf("q_base.w"), (size_t)D * H * 2);
+    memcpy(Wq.data() + (size_t)D * H, bf("q_opt.w"), (size_t)D * H * 2);
+    put_bf(Wq.data(), Wq.size(), &W.Wqq);
+    std::vector<float> bq(2 * D, 0.f);
+    const auto bb = tof("q_base.b");
+    std::copy(bb.begin(), bb.end(), bq.begin());
+    put_f(bq, &W.bqq);
   }
-  put_bf(bf("q_base.w"), (size_t)D * H, &W.Wqb);
-  put_f(tof("q_base.b"), &W.bqb);
   put_bf(bf("glob.w"), (size_t)D * H, &W.Wg);
   put_f(tof("glob.b"), &W.bg);
   put_f(tof("type_emb"), &W.temb);
@@ -571,7 +579,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 
 // workspace layout for one plan
 struct WsLayout {
-  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, gp, f, fstats, qkv, fattn, hs, pm,
+  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats, qkv, fattn, hs, pm,
       pl, po, part, total;
 };
 
@@ -593,6 +601,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.attn = take(NO * D * 4);
   L.hbuf = take(std::max(NO, NQ) * F * 4);
   L.qv = take(NQ * D * 4);
+  L.qo = take(NQ * D * 4);
   L.gp = take((size_t)p.nact * D * 4);
   L.f = take(NQ * D * 4);
   L.fstats = take(NQ * 8);
@@ -603,7 +612,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.pl = take((size_t)NH * p.Ptot * 4);
   L.po = take((size_t)NH * p.Ptot * 64 * 4);
   size_t part = 0;
-  const int shapes[][3] = {{p.NO, D, 3 * (int)H}, {p.NQ, D, (int)H}, {p.nact, D, (int)H}, {p.NO, D, D},
+  const int shapes[][3] = {{p.NO, D, 2 * (int)H}, {p.NQ, 2 * D, (int)H}, {p.nact, D, (int)H}, {p.NO, D, D},
                            {p.NO, F, D},        {p.NO, D, F},        {p.NQ, 3 * D, D},     {p.NQ, D, D},
                            {p.NQ, F, D},        {p.NQ, D, F},        {p.NO, D, 4 * D}};
   for (auto& s : shapes) {
@@ -685,9 +694,12 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
     delete h;
     return rc;
   }
-  if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess) {
+  if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
     clef_head_destroy(h);
-    return fail(CLEF_E_HIP, "hipEventCreate failed");
+    return fail(CLEF_E_HIP, "creating events / the side stream failed");
   }
   *out = h;
   return CLEF_OK;
@@ -696,6 +708,12 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
 void clef_head_destroy(clef_head* h) {
   if (!h) return;
   for (auto e : h->ev) (void)hipEventDestroy(e);
+  if (h->side) {
+    (void)hipStreamSynchronize(h->side);
+    (void)hipStreamDestroy(h->side);
+  }
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->staged) {
     if (h->staged_pending) (void)hipEventSynchronize(h->staged);
     (void)hipEventDestroy(h->staged);
@@ -851,6 +869,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   float* attn = reinterpret_cast<float*>(ws + L.attn);
   float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
   float* qv = reinterpret_cast<float*>(ws + L.qv);
+  float* qo = reinterpret_cast<float*>(ws + L.qo);
   float* gp = reinterpret_cast<float*>(ws + L.gp);
   float* f = reinterpret_cast<float*>(ws + L.f);
   float2* fstats = reinterpret_cast<float2*>(ws + L.fstats);
@@ -882,16 +901,28 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
 #define MARK(s) do { int rc_ = mark(s); if (rc_) return rc_; } while (0)
   MARK(-1);
 
+  // The option-query chain (pooling, lexical prior, query / question / global
+  // projections, the first routing layer's query projection) does not depend on
+  // the memory and K/V GEMMs: it runs on a second stream, forked after the row
+  // statistics and joined before the first routing attention, so its small
+  // kernels fill the CUs the big GEMMs leave idle.  Stage timing runs serially.
+  const bool fork = !h->prof;
+  hipStream_t s2 = fork ? h->side : st;
+
   // step 1: row statistics, pooled vectors, lexical vectors and prior
   launch_rowstats_bf16(st, X, (int)H, tiles, p.ntiles, stats, eps);
   MARK(CLEF_STAGE_ROWSTATS);
-  launch_pool(st, X, (int)H, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
+  if (fork) {
+    HIPCHK(hipEventRecord(h->ev_fork, st));
+    HIPCHK(hipStreamWaitEvent(s2, h->ev_fork, 0));
+  }
+  launch_pool(s2, X, (int)H, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
   MARK(CLEF_STAGE_POOL);
-  launch_lex_prior(st, h->table, (int)H, lex, NO, ids, pooled, ebar, prior);
+  launch_lex_prior(s2, h->table, (int)H, lex, NO, ids, pooled, ebar, prior);
   MARK(CLEF_STAGE_LEXICAL);
 
   if (joint) {
-    // step 2: memory and K/V of every routing layer
+    // step 2: memory and K/V of every routing layer (main stream)
     if (NR > 0) {
       launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
       MARK(CLEF_STAGE_MEMORY_GEMM);
@@ -899,19 +930,33 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
       MARK(CLEF_STAGE_KV_GEMM);
     }
     // step 3: option queries (with the first routing LayerNorm statistics), question base and global projections
-    launch_sgemm(st, LdSeg3{pooled + (size_t)NQ * H, ebar, pooled, optq, (int)H}, EpStore{u, D, W.ba7}, W.Wa7, NO, D,
-                 3 * (int)H, part, ustats, eps);
-    launch_sgemm(st, LdRows{pooled, (int)H, nullptr}, EpStore{qv, D, W.bqb}, W.Wqb, NQ, D, (int)H, part);
-    launch_sgemm(st, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
+    launch_sgemm(s2, LdRows{pooled, (int)H, nullptr}, EpSplit2{qv, qo, W.bqq}, W.Wqq, NQ, 2 * D, (int)H, part);
+    launch_sgemm(s2, LdSeg2{pooled + (size_t)NQ * H, ebar, (int)H}, EpAddRow{u, W.ba7, qo, optq}, W.Wa7, NO, D,
+                 2 * (int)H, part, ustats, eps);
+    launch_sgemm(s2, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
                  (int)H, part);
     MARK(CLEF_STAGE_QUERY_PROJ);
-    if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_u, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
+    if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_u, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, s2));
+    if (NR > 0) {
+      const Layer& Ly = W.route[0];
+      launch_sgemm(s2, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
+      MARK(CLEF_STAGE_ROUTE_DENSE);
+    }
+  }
+  if (fork) {
+    HIPCHK(hipEventRecord(h->ev_join, s2));
+    HIPCHK(hipStreamWaitEvent(st, h->ev_join, 0));
+  }
+
+  if (joint) {
     for (int r = 0; r < NR; ++r) {
       const Layer& Ly = W.route[r];
       const bf16_t* Kl = kv + (size_t)(2 * r) * NH * p.Tpad * 64;
       const bf16_t* Vl = kv + (size_t)(2 * r + 1) * NH * p.Tpad * 64;
-      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
-      MARK(CLEF_STAGE_ROUTE_DENSE);
+      if (r > 0) {
+        launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
+        MARK(CLEF_STAGE_ROUTE_DENSE);
+      }
       launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot);
       launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
       MARK(CLEF_STAGE_ROUTE_ATTN);

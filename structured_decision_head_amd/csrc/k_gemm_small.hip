@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
       const int r = v >> 4, c = v & 15;
       float x[8];
       if (m0 + r < M) {
-        ld.load8(m0 + r, k0 + c * 8, x);
+        ld.finish(ld.fetch(m0 + r, k0 + c * 8), m0 + r, k0 + c * 8, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -183,7 +183,8 @@ INST(LdRows, EpStore)
 INST(LdRows, EpResid)
 INST(LdLN, EpStore)
 INST(LdLN, EpGelu)
-INST(LdSeg3, EpStore)
+INST(LdSeg2, EpAddRow)
+INST(LdRows, EpSplit2)
 INST(LdZ, EpGelu)
 #undef INST
 

@@ -31,15 +31,24 @@ void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntile
 // ---------------------------------------------------------------------------
 // small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue
 // ---------------------------------------------------------------------------
+// A loaders: fetch() issues the global loads of 8 consecutive A elements
+// (row m, columns k..k+7) into a Raw value; finish() turns them into floats.
+// Splitting the two lets the GEMM keep the next chunk's loads in flight while
+// it multiplies the current one.
+DEV void f4x2(float4 a, float4 b, float* x) {
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 struct LdRows {          // A[m] = src[rows ? rows[m] : m]
   const float* src;
   int ld;
   const int* rows;
-  DEV void load8(int m, int k, float* x) const {
+  struct Raw { float4 a, b; };
+  DEV Raw fetch(int m, int k) const {
     const float* p = src + (size_t)(rows ? rows[m] : m) * ld + k;
-    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
+  DEV void finish(const Raw& r, int, int, float* x) const { f4x2(r.a, r.b, x); }
 };
 
 struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
@@ -48,42 +57,48 @@ struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
   const float2* stats;
   const float* g;
   const float* b;
-  DEV void load8(int m, int k, float* x) const {
+  struct Raw { float4 a, c; float2 s; };
+  DEV Raw fetch(int m, int k) const {
     const float* p = src + (size_t)m * ld + k;
-    const float2 s = stats[m];
-    const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4), stats[m]};
+  }
+  DEV void finish(const Raw& r, int, int k, float* x) const {
+    float v[8];
+    f4x2(r.a, r.c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (v[i] - s.x) * s.y * g[k + i] + b[k + i];
+    for (int i = 0; i < 8; ++i) x[i] = (v[i] - r.s.x) * r.s.y * g[k + i] + b[k + i];
   }
 };
 
-struct LdSeg3 {          // A[m] = [p0[m] | p1[m] | p2[idx[m]]], each H wide
+struct LdSeg2 {          // A[m] = [p0[m] | p1[m]], each H wide
   const float* p0;
   const float* p1;
-  const float* p2;
-  const int* idx;
   int H;
-  DEV void load8(int m, int k, float* x) const {
-    const int seg = k / H, c = k - seg * H;
-    const float* p = seg == 0 ? p0 + (size_t)m * H : seg == 1 ? p1 + (size_t)m * H : p2 + (size_t)idx[m] * H;
-    const float4 a = *reinterpret_cast<const float4*>(p + c), b = *reinterpret_cast<const float4*>(p + c + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  struct Raw { float4 a, b; };
+  DEV Raw fetch(int m, int k) const {
+    const float* p = k < H ? p0 + (size_t)m * H + k : p1 + (size_t)m * H + (k - H);
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
+  DEV void finish(const Raw& r, int, int, float* x) const { f4x2(r.a, r.b, x); }
 };
 
 struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m], each 1024 wide
   const float* F;
   const float* U;
   const int* fq;
-  DEV void load8(int m, int k, float* x) const {
-    const int seg = k >> 10, c = k & 1023;
+  struct Raw { float4 f0, f1, u0, u1; };
+  DEV Raw fetch(int m, int k) const {
+    const int c = k & 1023;
     const float* fp = F + (size_t)fq[m] * 1024 + c;
     const float* up = U + (size_t)m * 1024 + c;
-    const float4 f0 = *reinterpret_cast<const float4*>(fp), f1 = *reinterpret_cast<const float4*>(fp + 4);
-    const float4 u0 = *reinterpret_cast<const float4*>(up), u1 = *reinterpret_cast<const float4*>(up + 4);
-    const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    return Raw{*reinterpret_cast<const float4*>(fp), *reinterpret_cast<const float4*>(fp + 4),
+               *reinterpret_cast<const float4*>(up), *reinterpret_cast<const float4*>(up + 4)};
+  }
+  DEV void finish(const Raw& r, int, int k, float* x) const {
+    const int seg = k >> 10;
+    float f[8], u[8];
+    f4x2(r.f0, r.f1, f);
+    f4x2(r.u0, r.u1, u);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       x[i] = seg == 0 ? f[i] : seg == 1 ? u[i] : seg == 2 ? f[i] * u[i] : fabsf(f[i] - u[i]);
@@ -109,6 +124,29 @@ struct EpGelu {          // C = GELU(acc + bias)
   DEV float operator()(int m, int n, float v) const {
     const float r = gelu_erf(v + bias[n]);
     C[(size_t)m * ldc + n] = r;
+    return r;
+  }
+};
+
+struct EpAddRow {        // C = acc + bias + add[idx[m]] (a per-row gathered term), width 1024
+  float* C;
+  const float* bias;
+  const float* add;
+  const int* idx;
+  DEV float operator()(int m, int n, float v) const {
+    const float r = v + bias[n] + add[(size_t)idx[m] * 1024 + n];
+    C[(size_t)m * 1024 + n] = r;
+    return r;
+  }
+};
+
+struct EpSplit2 {        // columns [0, 1024) -> C0, [1024, 2048) -> C1, plus bias
+  float* C0;
+  float* C1;
+  const float* bias;
+  DEV float operator()(int m, int n, float v) const {
+    const float r = v + bias[n];
+    if (n < 1024) C0[(size_t)m * 1024 + n] = r; else C1[(size_t)m * 1024 + (n - 1024)] = r;
     return r;
   }
 };
