@@ -50,7 +50,7 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int D = 1024, F = 4096, NH = 16;
 constexpr int TILE = 256;     // row tile of the packed row space
-constexpr int KCH = 256;      // keys per routing-attention chunk
+constexpr int KCH = kAttnChunk;   // keys per routing-attention chunk
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -263,7 +263,8 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
       tiles.insert(tiles.end(), {int32_t(src0[r] + t0), int32_t(kv0 + t0), int32_t(std::min<int64_t>(TILE, len[r] - t0)), nact});
       kvtiles.insert(kvtiles.end(), {int32_t(kv0 + t0), int32_t(kv0 + t0), TILE, nact});
     }
-    for (int ch = 0; ch < nc; ++ch) items.insert(items.end(), {nact, ch});
+    for (int ch = 0; ch < nc; ++ch)
+      for (int qb = 0; qb < no; qb += 32) items.insert(items.end(), {nact, ch, qb, 0});
     kv0 += ceil_div(len[r], TILE) * TILE;
     pbase += (int64_t)no * nc;
     ++nact;
@@ -274,7 +275,7 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
   p.Tpad = kv0;
   p.Ptot = pbase;
   p.ntiles = (int)tiles.size() / 4;
-  p.nitems = (int)items.size() / 2;
+  p.nitems = (int)items.size() / 4;
 
   // pooling entries: questions, then options, then global rows; lexical entries per option
   std::vector<int32_t> opool;
@@ -855,7 +856,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   const int* qrec = dtab + p.off_qrec;
   const int* qtype = dtab + p.off_qtype;
   const int* ooff = dtab + p.off_ooff;
-  const int2* items = reinterpret_cast<const int2*>(dtab + p.off_items);
+  const int4* items = reinterpret_cast<const int4*>(dtab + p.off_items);
 
   float2* stats = reinterpret_cast<float2*>(ws + L.stats);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);

@@ -2,7 +2,7 @@
 //
 // Evidence routing (clef-4bit page §三 step 2; Clef-Flash overview §三): all
 // option queries of a record attend, per head, over every valid memory row of
-// that record.  The keys are split into 256-row chunks; one wave owns
+// that record.  The keys are split into 128-row chunks; one wave owns
 // (record, head, chunk), loops over its record's queries 32 at a time and
 // writes flash-decode partials (running max, running sum, unnormalised
 // output) that k_route_combine merges.  Scores and the value mix use
@@ -18,14 +18,78 @@
 namespace clef {
 
 namespace {
-constexpr int CH = 256;   // keys per chunk (one wave)
+
+// K rows of one 32-key step (A operand of S^T = K Q^T) and the V^T fragments
+// (A operand of O^T = V^T P^T) for both 16-key halves and both 32-dim halves.
+struct KV32 {
+  u32x4 k[4];
+  u32x4 v[2][2];
+};
+
+DEV void kv_load(KV32& r, const bf16_t* Kj, const bf16_t* Vj, int row0, int l32, int g) {
+  const bf16_t* kp = Kj + (size_t)(row0 + l32) * 64 + 8 * g;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) r.k[kk] = *reinterpret_cast<const u32x4*>(kp + kk * 16);
+  const bf16_t* vp = Vj + (size_t)(row0 >> 5) * 2048 + (size_t)l32 * 32 + 8 * g;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) r.v[t][dt] = *reinterpret_cast<const u32x4*>(vp + dt * 1024 + 16 * t);
 }
+
+// One 32-key step of the online softmax for the wave's 32 queries.
+DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, float scale_log2, float& m, float& l,
+                 f32x16 (&o)[2]) {
+  f32x16 s;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(r.k[kk]), qf[kk], s, 0, 0, 0);
+  // lane owns query (lane & 31) and keys kb + 8 (e / 4) + 4 g + (e % 4)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
+    s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, s[e]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
+  const float alpha = exp2f(m - mn);      // m = -inf gives 0
+  float ls = 0.f, p[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    p[e] = exp2f(s[e] - mn);
+    ls += p[e];
+  }
+  ls += __shfl_xor(ls, 32, 64);
+  l = l * alpha + ls;
+  m = mn;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    o[0][e] *= alpha;
+    o[1][e] *= alpha;
+  }
+  // the k-slot (g, e) of half t is key kb + 16 t + 8 (e / 4) + 4 g + (e % 4)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bf16x8 pf = as_bf16x8(pack8(p + 8 * t));
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(r.v[t][dt]), pf, o[dt], 0, 0, 0);
+  }
+}
+
+}  // namespace
 
 // rec: per record 8 ints: kv0 (first row in the packed padded row space),
 // n (valid rows), o0 (first option), no (options), pbase, nc (chunks), q0, nq.
-__global__ __launch_bounds__(256) void k_route_attn(const float* __restrict__ Q, const bf16_t* __restrict__ Kl,
+// One wave per (record, head, chunk of kAttnChunk keys, block of 32 queries);
+// the next 32-key step's K and V are in flight while the current one is
+// multiplied.  Query blocks of one chunk re-read the same K/V rows from cache.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_route_attn(const float* __restrict__ Q, const bf16_t* __restrict__ Kl,
                                                     const bf16_t* __restrict__ Vl, long long Tpad,
-                                                    const int2* __restrict__ items, int nitems,
+                                                    const int4* __restrict__ items, int nitems,
                                                     const int* __restrict__ rec, float* __restrict__ pm,
                                                     float* __restrict__ pl, float* __restrict__ po, long long Ptot,
                                                     float scale_log2) {
@@ -33,17 +97,17 @@ __global__ __launch_bounds__(256) void k_route_attn(const float* __restrict__ Q,
   const int it = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (it >= nitems) return;
   const int j = blockIdx.y;
-  const int2 bc = items[it];
+  const int4 bc = items[it];             // (record, chunk, first query of the block, -)
   const int* R = rec + 8 * bc.x;
   const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
   const int c = bc.y;
-  const int k_lo = c * CH, k_hi = min(n, k_lo + CH);
+  const int k_lo = c * kAttnChunk, k_hi = min(n, k_lo + kAttnChunk);
   const bf16_t* Kj = Kl + (size_t)j * Tpad * 64;
   const bf16_t* Vj = Vl + (size_t)j * Tpad * 64;
   const int g = lane >> 5, l32 = lane & 31;
 
-  for (int qb = 0; qb < no; qb += 32) {
-    const int qi = qb + l32;
+  {
+    const int qi = bc.z + l32;
     const bool qvalid = qi < no;
     bf16x8 qf[4];
     {
@@ -65,58 +129,16 @@ __global__ __launch_bounds__(256) void k_route_attn(const float* __restrict__ Q,
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
 
-    for (int kb = k_lo; kb < k_hi; kb += 32) {
-      // S^T (32 keys x 32 queries): A = K rows, B = Q^T.
-      f32x16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      const bf16_t* kp = Kj + (size_t)(kv0 + kb + l32) * 64 + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kp + kk * 16);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[kk], s, 0, 0, 0);
-      }
-      // lane owns query l32 and keys kb + 8 (e / 4) + 4 g + (e % 4)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
-        s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
-      const float alpha = exp2f(m - mn);      // m = -inf gives 0
-      float ls = 0.f;
-      float p[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = exp2f(s[e] - mn);
-        ls += p[e];
-      }
-      ls += __shfl_xor(ls, 32, 64);
-      l = l * alpha + ls;
-      m = mn;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        o[0][e] *= alpha;
-        o[1][e] *= alpha;
-      }
-      // O^T (64 d x 32 queries) += V^T (d x keys) P^T (keys x queries); the
-      // k-slot (g, e) of step t is key kb + 16 t + 8 (e / 4) + 4 g + (e % 4).
-      const bf16_t* vp = Vj + ((size_t)((kv0 + kb) >> 5) * 64) * 32;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pf = as_bf16x8(pack8(p + 8 * t));
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const bf16_t* rowp = vp + (size_t)(dt * 32 + l32) * 32 + 16 * t + 4 * g;
-          const uint2 lo = *reinterpret_cast<const uint2*>(rowp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(rowp + 8);
-          const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pf, o[dt], 0, 0, 0);
-        }
-      }
+    // two steps per iteration so that the double buffer has static registers
+    KV32 a, b;
+    kv_load(a, Kj, Vj, kv0 + k_lo, l32, g);
+    for (int kb = k_lo; kb < k_hi; kb += 64) {
+      const bool more = kb + 32 < k_hi;
+      if (more) kv_load(b, Kj, Vj, kv0 + kb + 32, l32, g);
+      kv_step(a, qf, kb, n, g, scale_log2, m, l, o);
+      if (!more) break;
+      if (kb + 64 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 64, l32, g);
+      kv_step(b, qf, kb + 32, n, g, scale_log2, m, l, o);
     }
     if (qvalid) {
       const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
@@ -136,7 +158,7 @@ __global__ __launch_bounds__(256) void k_route_attn(const float* __restrict__ Q,
 }
 
 void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
-                       const int2* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                       const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
                        long long Ptot) {
   if (nitems == 0) return;
   const float scale_log2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
@@ -144,7 +166,10 @@ void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const b
                      rec, pm, pl, po, Ptot, scale_log2);
 }
 
-// Merge the chunk partials of (option, head): one wave, lane = output dim.
+// Merge the chunk partials of (option, head): one wave.  Lanes split the
+// chunks to find the global max and the softmax denominator; then lane d sums
+// the rescaled unnormalised outputs of every chunk for output dim d, with the
+// chunk weights broadcast from the lane that computed them.
 __global__ __launch_bounds__(256) void k_route_combine(const float* __restrict__ pm, const float* __restrict__ pl,
                                                        const float* __restrict__ po, long long Ptot,
                                                        const int* __restrict__ opt_rec, const int* __restrict__ rec,
@@ -157,14 +182,27 @@ __global__ __launch_bounds__(256) void k_route_combine(const float* __restrict__
   const int o0 = R[2], pbase = R[4], nc = R[5];
   const size_t s0 = (size_t)j * Ptot + pbase + (size_t)(k - o0) * nc;
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, pm[s0 + c]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float a = exp2f(pm[s0 + c] - M);
-    L += a * pl[s0 + c];
-    O += a * po[(s0 + c) * 64 + lane];
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, pm[s0 + c]);
+  M = wave_max(M);
+  float Lsum = 0.f;
+  for (int c = lane; c < nc; c += 64) Lsum += exp2f(pm[s0 + c] - M) * pl[s0 + c];
+  Lsum = wave_sum(Lsum);
+  float O = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const float a_mine = (c0 + lane < nc) ? exp2f(pm[s0 + c0 + lane] - M) : 0.f;
+    const int cn = min(64, nc - c0);
+    const float* pp = po + (s0 + c0) * 64 + lane;
+    int c = 0;
+    for (; c + 8 <= cn; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = pp[(size_t)(c + i) * 64];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O += __shfl(a_mine, c + i, 64) * v[i];
+    }
+    for (; c < cn; ++c) O += __shfl(a_mine, c, 64) * pp[(size_t)c * 64];
   }
-  out[(size_t)k * 1024 + j * 64 + lane] = O / L;
+  out[(size_t)k * 1024 + j * 64 + lane] = O / Lsum;
 }
 
 void launch_route_combine(hipStream_t st, const float* pm, const float* pl, const float* po, long long Ptot,

@@ -55,9 +55,10 @@ struct EpiMem {
 
 // Columns are [K_0 | V_0 | K_1 | V_1 | ...] (1024 each).  K is stored
 // head-major [layer][head][row][64]; V is stored per 32-row block transposed,
-// [layer][head][row / 32][64][32], the layout the attention kernel's MFMA
-// operand wants.  V tiles are accumulated transposed (acc rows are output
-// columns, acc columns are rows), so 32 lanes store 64 contiguous bytes.
+// [layer][head][row / 32][64][32] with the 32 keys of a block in
+// vblock_pos() order, the layout the attention kernel's MFMA operand wants.
+// V tiles are accumulated transposed (acc rows are output columns, acc
+// columns are rows), so 32 lanes store 64 contiguous bytes.
 struct EpiKV {
   const float* bias;
   bf16_t* kv;          // layer r: K at kv + (2r) * 16 * Tpad * 64, V at kv + (2r+1) * 16 * Tpad * 64
@@ -92,7 +93,7 @@ struct EpiKV {
       for (int e = 0; e < 16; ++e) {
         const int col = col0 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const float b = bias[col];
-        bf16_t* base = head_base(col) + (size_t)(col & 63) * 32 + (lane & 31);
+        bf16_t* base = head_base(col) + (size_t)(col & 63) * 32 + vblock_pos(lane & 31);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const int rb = (row0 + ni * 32) >> 5;   // 32-row block (row0 is a multiple of 32)

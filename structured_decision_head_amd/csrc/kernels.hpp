@@ -5,6 +5,11 @@
 namespace clef {
 
 constexpr int kMaxOptions = 1024;   // options of one question (LDS arrays in the per-question kernels)
+constexpr int kAttnChunk = 128;     // keys per routing-attention work item (one wave)
+
+// Position of key k (0..31) inside a 32-key V block: the eight keys one lane
+// feeds to a V^T P^T MFMA step sit in 16 contiguous bytes.
+DEV int vblock_pos(int k) { return (k & 16) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
 // ---------------------------------------------------------------------------
 // row kernels
@@ -180,8 +185,9 @@ void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, in
 // attention
 // ---------------------------------------------------------------------------
 // rec: 8 ints per active record: kv0, n, o0, no, pbase, nc, q0, nq
+// items: int4 (active record, key chunk, first query of a 32-query block, 0)
 void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
-                       const int2* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                       const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
                        long long Ptot);
 void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
                           const int* opt_rec, const int* rec, int NO, float* out);
