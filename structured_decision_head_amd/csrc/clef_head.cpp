@@ -580,7 +580,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 
 // workspace layout for one plan
 struct WsLayout {
-  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats, qkv, fattn, hs, pm,
+  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats, fattn, pm,
       pl, po, part, total;
 };
 
@@ -606,9 +606,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.gp = take((size_t)p.nact * D * 4);
   L.f = take(NQ * D * 4);
   L.fstats = take(NQ * 8);
-  L.qkv = take(NQ * 3 * D * 4);
   L.fattn = take(NQ * D * 4);
-  L.hs = take(NO * D * 4);
   L.pm = take((size_t)NH * p.Ptot * 4);
   L.pl = take((size_t)NH * p.Ptot * 4);
   L.po = take((size_t)NH * p.Ptot * 64 * 4);
@@ -620,6 +618,13 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
     if (s[0] == 0) continue;
     const SgemmShape g = sgemm_shape(s[0], s[1], s[2], s[1] == D);
     part = std::max(part, g.part_floats);
+  }
+  // products whose slices are summed by their consumer (field QKV, scoring hidden layer)
+  const int pshapes[][3] = {{p.NQ, 3 * D, D}, {p.NO, D, 4 * D}};
+  for (auto& s : pshapes) {
+    if (s[0] == 0) continue;
+    const SgemmShape g = sgemm_shape(s[0], s[1], s[2], false);
+    part = std::max(part, (size_t)g.nsplit * g.mtiles * kSgemmRows * s[1]);
   }
   L.part = take(part * 4);
   L.total = o;
@@ -874,9 +879,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   float* gp = reinterpret_cast<float*>(ws + L.gp);
   float* f = reinterpret_cast<float*>(ws + L.f);
   float2* fstats = reinterpret_cast<float2*>(ws + L.fstats);
-  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
   float* fattn = reinterpret_cast<float*>(ws + L.fattn);
-  float* hs = reinterpret_cast<float*>(ws + L.hs);
   float* pm = reinterpret_cast<float*>(ws + L.pm);
   float* pl = reinterpret_cast<float*>(ws + L.pl);
   float* po = reinterpret_cast<float*>(ws + L.po);
@@ -949,6 +952,8 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     HIPCHK(hipStreamWaitEvent(st, h->ev_join, 0));
   }
 
+  SgemmShape gs{};   // scoring hidden-layer slices (joint branch only)
+  gs.nsplit = 1;
   if (joint) {
     for (int r = 0; r < NR; ++r) {
       const Layer& Ly = W.route[r];
@@ -974,8 +979,8 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f0, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     for (int l = 0; l < NL; ++l) {
       const Layer& Ly = W.field[l];
-      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, EpStore{qkv, 3 * D, Ly.bqkv}, Ly.Wqkv, NQ, 3 * D, D, part);
-      launch_field_attn(st, qkv, rec, p.nact, fattn);
+      const SgemmShape gq = launch_sgemm_partial(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, Ly.Wqkv, NQ, 3 * D, D, part);
+      launch_field_attn(st, part, gq.nsplit, (size_t)gq.mtiles * kSgemmRows * 3 * D, Ly.bqkv, rec, p.nact, fattn);
       launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps);
       launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part);
       launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part,
@@ -984,9 +989,10 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     MARK(CLEF_STAGE_FIELD);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     // step 5: residual-MLP hidden layer over [f, u, f*u, |f-u|]
-    launch_sgemm(st, LdZ{f, u, optq}, EpGelu{hs, D, W.bs1}, W.Ws1, NO, D, 4 * D, part);
+    gs = launch_sgemm_partial(st, LdZ{f, u, optq}, W.Ws1, NO, D, 4 * D, part);
   }
-  launch_score(st, u, f, hs, W.ws2, W.bs2, prior, W.gate, W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
+  launch_score(st, u, f, part, gs.nsplit, (size_t)gs.mtiles * kSgemmRows * D, W.bs1, W.ws2, W.bs2, prior, W.gate,
+               W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
                h->trace && joint ? h->tr_jcos : nullptr, h->trace && joint ? h->tr_mlp : nullptr);
   MARK(CLEF_STAGE_SCORE);
 #undef MARK

@@ -23,6 +23,13 @@ DEV uint32_t f2bf(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats to two bf16 (round to nearest even, hardware conversion), a in the low half.
+DEV uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Unpack 8 bf16 held in a uint4 into floats.
 DEV void unpack8(const uint4 v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);

@@ -217,7 +217,8 @@ void launch_route_combine(hipStream_t st, const float* pm, const float* pl, cons
 // is the sum of the four partial dot products (two lane exchanges).  Keys and
 // values are staged in LDS 64 rows at a time with an online softmax, so any
 // number of fields works.  QKV rows are [q | k | v] of width 3 x 1024.
-__global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QKV, const int* __restrict__ rec,
+__global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QKV, int nsplit, size_t stride,
+                                                    const float* __restrict__ bqkv, const int* __restrict__ rec,
                                                     float* __restrict__ out) {
   __shared__ float4 sK[64][16], sV[64][16];
   const int* R = rec + 8 * blockIdx.x;
@@ -228,10 +229,10 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
     const int qi = qb + qi_l;
     const bool valid = qi < nq;
     float4 q[4], o[4];
-    const float* qp = QKV + (size_t)(q0 + (valid ? qi : 0)) * 3072 + j * 64 + part * 16;
+    const size_t qo = (size_t)(q0 + (valid ? qi : 0)) * 3072 + j * 64 + part * 16;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      q[c] = *reinterpret_cast<const float4*>(qp + 4 * c);
+      q[c] = sum_slices4(QKV + qo + 4 * c, nsplit, stride, bqkv + j * 64 + part * 16 + 4 * c);
       q[c].x *= 0.125f; q[c].y *= 0.125f; q[c].z *= 0.125f; q[c].w *= 0.125f;
       o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -244,9 +245,9 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
       for (int r = 0; r < 4; ++r) {
         const int idx = t + 256 * r, row = idx >> 4, c4 = idx & 15;
         if (row < nk) {
-          const float* rp = QKV + (size_t)(q0 + kb + row) * 3072 + j * 64 + 4 * c4;
-          sK[row][c4] = *reinterpret_cast<const float4*>(rp + 1024);
-          sV[row][c4] = *reinterpret_cast<const float4*>(rp + 2048);
+          const size_t ro = (size_t)(q0 + kb + row) * 3072 + j * 64 + 4 * c4;
+          sK[row][c4] = sum_slices4(QKV + ro + 1024, nsplit, stride, bqkv + 1024 + j * 64 + 4 * c4);
+          sV[row][c4] = sum_slices4(QKV + ro + 2048, nsplit, stride, bqkv + 2048 + j * 64 + 4 * c4);
         }
       }
       __syncthreads();
@@ -283,9 +284,10 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
   }
 }
 
-void launch_field_attn(hipStream_t st, const float* QKV, const int* rec, int nrec, float* out) {
+void launch_field_attn(hipStream_t st, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
+                       const int* rec, int nrec, float* out) {
   if (nrec == 0) return;
-  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(256), 0, st, QKV, rec, out);
+  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, out);
 }
 
 }  // namespace clef

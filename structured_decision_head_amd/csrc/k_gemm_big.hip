@@ -20,88 +20,182 @@ namespace {
 
 constexpr int BM = 256, BN = 256;
 
-// Epilogues consume a wave's whole 128 x 128 accumulator block.  Accumulator
-// (mi, ni, e) of lane l sits at block row 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4
-// and block column 32 ni + (l % 32).  row0 / col0 locate the block in the
-// packed row space and the output columns; per-row and per-column values are
-// hoisted out of the element loops.
-struct EpiMem {
-  const float2* stats;
+// Epilogues.  Each tile is multiplied in the orientation that gives a lane
+// runs of consecutive output elements: "transposed" tiles take the W rows as
+// the MFMA A operand, so accumulator rows are output columns and a lane owns
+// one output row with runs of 4 consecutive columns.  Accumulator (mi, ni, e)
+// of lane l sits at block row 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4 and block
+// column 32 ni + (l % 32).
+//
+// The finished tile is converted to bf16 and written with 8- or 16-byte LDS
+// stores into an image of its final memory layout (the operand ring is free
+// by then); all 256 threads then copy the image out with 16-byte global
+// stores, each wave instruction covering 1 KB of contiguous memory.  Per-tile
+// constants are loaded by thread tid when the kernel starts, so their latency
+// hides under the main loop, and parked in a small LDS area behind the ring.
+constexpr int kConstFloats = 1024;
+
+struct EpiMem {          // transposed tiles; rows of out are the packed row space
+  const float2* stats;   // LayerNorm (mean, rstd) per output row
   const float* c;
   const float* d;
-  bf16_t* out;   // [rows][1024]
-  static constexpr bool kHasTransposed = false;
-  DEV bool transposed(int) const { return false; }
-  DEV void tile(const f32x16 (&acc)[4][4], int row0, int col0, int lane) const {
-    float cc[4], dd[4];
+  bf16_t* out;           // [rows][1024]
+  static constexpr bool kHasPlain = false;
+  static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
+  static constexpr int kImageBytes = 256 * kLd * 2;
+  DEV bool transposed(int) const { return true; }
+  // constants: [0, 256) c and [256, 512) d of the tile's columns, then (mean, rstd) of its rows
+  DEV void load_consts(int orow0, int ocol0, int tid, float (&r)[4]) const {
+    const float2 st = stats[orow0 + tid];
+    r[0] = c[ocol0 + tid]; r[1] = d[ocol0 + tid]; r[2] = st.x; r[3] = st.y;
+  }
+  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const {
+    cst[tid] = r[0]; cst[256 + tid] = r[1]; cst[512 + 2 * tid] = r[2]; cst[513 + 2 * tid] = r[3];
+  }
+  // lr0 / lc0: tile-local first row / column of the wave's block
+  DEV void stage_t(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
+    const int h4 = 4 * (lane >> 5);
+    float2 st[4];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int col = col0 + ni * 32 + (lane & 31);
-      cc[ni] = c[col];
-      dd[ni] = d[col];
-    }
+    for (int ni = 0; ni < 4; ++ni) st[ni] = *reinterpret_cast<const float2*>(cst + 512 + 2 * (lr0 + ni * 32 + (lane & 31)));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row0 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const float2 st = stats[row];
-        bf16_t* o = out + (size_t)row * 1024 + col0 + (lane & 31);
+      for (int g = 0; g < 4; ++g) {
+        const int lc = lc0 + mi * 32 + 8 * g + h4;
+        const float4 cc = *reinterpret_cast<const float4*>(cst + lc);
+        const float4 dd = *reinterpret_cast<const float4*>(cst + 256 + lc);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) o[ni * 32] = (bf16_t)f2bf(st.y * (acc[mi][ni][e] - st.x * cc[ni]) + dd[ni]);
+        for (int ni = 0; ni < 4; ++ni) {
+          const float mu = st[ni].x, rs = st[ni].y;
+          const f32x16& a = acc[mi][ni];
+          uint2 v;
+          v.x = pack_bf16x2(rs * (a[4 * g] - mu * cc.x) + dd.x, rs * (a[4 * g + 1] - mu * cc.y) + dd.y);
+          v.y = pack_bf16x2(rs * (a[4 * g + 2] - mu * cc.z) + dd.z, rs * (a[4 * g + 3] - mu * cc.w) + dd.w);
+          *reinterpret_cast<uint2*>(img + (lr0 + ni * 32 + (lane & 31)) * kLd + lc) = v;
+        }
       }
+  }
+  DEV void stage(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
+  DEV void store(const bf16_t* img, int orow0, int ocol0, bool, int tid) const {
+#pragma unroll 8
+    for (int i = tid; i < 256 * 32; i += 256) {
+      const int r = i >> 5, ch = i & 31;
+      *reinterpret_cast<uint4*>(out + (size_t)(orow0 + r) * 1024 + ocol0 + ch * 8) =
+          *reinterpret_cast<const uint4*>(img + r * kLd + ch * 8);
+    }
   }
 };
 
-// Columns are [K_0 | V_0 | K_1 | V_1 | ...] (1024 each).  K is stored
-// head-major [layer][head][row][64]; V is stored per 32-row block transposed,
-// [layer][head][row / 32][64][32] with the 32 keys of a block in
-// vblock_pos() order, the layout the attention kernel's MFMA operand wants.
-// V tiles are accumulated transposed (acc rows are output columns, acc
-// columns are rows), so 32 lanes store 64 contiguous bytes.
+// Columns are [K_0 | V_0 | K_1 | V_1 | ...] (1024 each), so a 256-column tile
+// is four heads of one K or one V, and the tile's 256 rows of one head are a
+// contiguous 32 KB run in either layout.  K is stored head-major
+// [layer][head][row][64] (transposed tiles).  V is stored per 32-row block
+// transposed, [layer][head][row / 32][64][32] with the 32 keys of a block in
+// vblock_pos() order (plain tiles: a lane's accumulators e = 8 q .. 8 q + 7
+// land on 8 consecutive key positions, one 16-byte run).
 struct EpiKV {
   const float* bias;
   bf16_t* kv;          // layer r: K at kv + (2r) * 16 * Tpad * 64, V at kv + (2r+1) * 16 * Tpad * 64
   long long Tpad;
-  static constexpr bool kHasTransposed = true;
-  DEV bool transposed(int tn) const { return ((tn * BN) >> 10) & 1; }
+  static constexpr bool kHasPlain = true;
+  static constexpr int kLdK = 72;                      // K image row pitch (bf16): 128 B + 16 B
+  static constexpr int kImageBytes = 4 * 256 * kLdK * 2;
+  DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV bf16_t* head_base(int col) const {
     const int r = col >> 11, isv = (col >> 10) & 1, h = (col >> 6) & 15;
     return kv + ((size_t)(2 * r + isv) * 16 + h) * (size_t)Tpad * 64;
   }
-  // K: acc rows are rows, acc columns are output columns
-  DEV void tile(const f32x16 (&acc)[4][4], int row0, int col0, int lane) const {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int col = col0 + ni * 32 + (lane & 31);
-      const float b = bias[col];
-      bf16_t* base = head_base(col) + (col & 63);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row0 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          base[(size_t)row * 64] = (bf16_t)f2bf(acc[mi][ni][e] + b);
-        }
-    }
-  }
-  // V: acc rows are output columns (col0 + ...), acc columns are rows (row0 + ...)
-  DEV void tile_t(const f32x16 (&acc)[4][4], int row0, int col0, int lane) const {
+  DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
+  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
+  // K (transposed): image [head][row][kLdK]
+  DEV void stage_t(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
+    const int h4 = 4 * (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int col = col0 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const float b = bias[col];
-        bf16_t* base = head_base(col) + (size_t)(col & 63) * 32 + vblock_pos(lane & 31);
+      for (int g = 0; g < 4; ++g) {
+        const int lc = lc0 + mi * 32 + 8 * g + h4;
+        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
+        bf16_t* base = img + (lc >> 6) * (256 * kLdK) + (lc & 63);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const int rb = (row0 + ni * 32) >> 5;   // 32-row block (row0 is a multiple of 32)
-          base[(size_t)rb * 2048] = (bf16_t)f2bf(acc[mi][ni][e] + b);
+          const f32x16& a = acc[mi][ni];
+          uint2 v;
+          v.x = pack_bf16x2(a[4 * g] + b.x, a[4 * g + 1] + b.y);
+          v.y = pack_bf16x2(a[4 * g + 2] + b.z, a[4 * g + 3] + b.w);
+          *reinterpret_cast<uint2*>(base + (lr0 + ni * 32 + (lane & 31)) * kLdK) = v;
         }
       }
   }
+  // V (plain): image [head][row block][64][32] in memory order; 16-byte chunk c
+  // of a 64-byte feature row f sits at c ^ (f & 3) to spread LDS banks
+  DEV void stage(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int lc = lc0 + ni * 32 + (lane & 31);
+      const float b = cst[lc];
+      const int f = lc & 63;
+      bf16_t* base = img + (lc >> 6) * 16384 + f * 32;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        bf16_t* blk = base + ((lr0 >> 5) + mi) * 2048;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x16& a = acc[mi][ni];
+          const int e = 8 * q;
+          uint4 v;
+          v.x = pack_bf16x2(a[e] + b, a[e + 1] + b);
+          v.y = pack_bf16x2(a[e + 2] + b, a[e + 3] + b);
+          v.z = pack_bf16x2(a[e + 4] + b, a[e + 5] + b);
+          v.w = pack_bf16x2(a[e + 6] + b, a[e + 7] + b);
+          *reinterpret_cast<uint4*>(blk + 8 * ((2 * q + hh) ^ (f & 3))) = v;
+        }
+      }
+    }
+  }
+  DEV void store(const bf16_t* img, int orow0, int ocol0, bool tr, int tid) const {
+    if (tr) {
+#pragma unroll 8
+      for (int i = tid; i < 4 * 2048; i += 256) {          // 4 heads x 256 rows x 8 chunks of 16 B
+        const int hh = i >> 11, r = (i >> 3) & 255, ch = i & 7;
+        bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)orow0 * 64;
+        *reinterpret_cast<uint4*>(dst + r * 64 + ch * 8) =
+            *reinterpret_cast<const uint4*>(img + (hh * 256 + r) * kLdK + ch * 8);
+      }
+    } else {
+#pragma unroll 8
+      for (int i = tid; i < 4 * 2048; i += 256) {          // 4 heads x 32 KB in memory order
+        const int hh = i >> 11, j = i & 2047, f = (j >> 2) & 63, c = j & 3;
+        bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)(orow0 >> 5) * 2048;
+        *reinterpret_cast<uint4*>(dst + j * 8) =
+            *reinterpret_cast<const uint4*>(img + hh * 16384 + (j >> 2) * 32 + 8 * (c ^ (f & 3)));
+      }
+    }
+  }
 };
+
+// Output tile of workgroup b.  Workgroups are dealt to the 8 XCDs round-robin
+// (b % 8), each XCD with its own L2.  Column tiles are grouped in fours
+// (256 x 4 W rows: 2 MB at K = 1024, 8 MB at K = 4096); XCD x works on column
+// group x % G and on part x / G of the row tiles, taken in order, so the W
+// slice it multiplies stays in its L2 while the A rows stream past, and each
+// A row tile is fetched by G XCDs instead of once per column tile pass.
+DEV void tile_order(int b, int ntm, int ntn, int& tm, int& tn) {
+  const int G = ntn >> 2;
+  if ((ntn & 3) == 0 && G <= 8 && (8 % G) == 0 && ((ntm * ntn) & 7) == 0) {
+    const int x = b & 7, j = b >> 3, R = 8 / G;
+    const int cg = x % G, part = x / G;
+    const int u = part * (4 * ntm / R) + j;   // index in the group's row-major list of 4 ntm tiles
+    tm = u >> 2;
+    tn = 4 * cg + (u & 3);
+  } else {
+    const int lt = xcd_remap(b, ntm * ntn);
+    tm = lt / ntn;
+    tn = lt - tm * ntn;
+  }
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -124,10 +218,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
                const bf16_t* __restrict__ W, int K, Epi epi) {
   constexpr int KS = 32, NST = 4;
-  __shared__ u32x4 smem[NST][2][BM * 4];   // [stage][A|B][row * 4 + swizzled chunk]
+  constexpr int kRingBytes = NST * 2 * BM * 4 * 16;
+  constexpr int kSpan = Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
+  // operand ring [stage][A|B][row * 4 + swizzled chunk] (after the main loop the
+  // same bytes hold the output image), then the tile constants
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSpan + kConstFloats * 4];
+  u32x4 (*smem)[2][BM * 4] = reinterpret_cast<u32x4 (*)[2][BM * 4]>(lds);
+  float* cst = reinterpret_cast<float*>(lds + kSpan);
 
-  const int lt = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = lt / ntile_n, tn = lt - tm * ntile_n;
+  int tm, tn;
+  tile_order(blockIdx.x, gridDim.x / ntile_n, ntile_n, tm, tn);
   const int4 T = tiles[tm];              // (first A row, first output row, valid rows, record)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,6 +279,9 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                        \
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[mi], F##b[ni], acc[mi][ni], 0, 0, 0);
 
+  float kc[4];
+  epi.load_consts(T.y, tn * BN, tid, kc);   // consumed after the main loop
+
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -193,6 +296,7 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   for (int st = 0; st < NST - 1; ++st) { COPY_STAGE(st, st * KS) }
   WAIT_VM(8 * (NST - 2));
   __builtin_amdgcn_s_barrier();
+  epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
   COPY_STAGE(NST - 1, (NST - 1) * KS)
   LOAD_FRAGS(X, 0, 0)
   int kt = 0;
@@ -244,13 +348,16 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 
   // All 256 rows are stored: rows past the valid count come from clamped
   // (finite) inputs and keep the padded part of the row space finite.
-  if constexpr (Epi::kHasTransposed) {
-    if (tr) {
-      epi.tile_t(acc, T.y + wb * 128, tn * BN + wa * 128, lane);
-      return;
-    }
+  bf16_t* img = reinterpret_cast<bf16_t*>(lds);
+  __syncthreads();                       // every wave is done with the operand ring
+  if constexpr (Epi::kHasPlain) {
+    if (!tr) epi.stage(acc, cst, img, wa * 128, wb * 128, lane);
+    else epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
+  } else {
+    epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
   }
-  epi.tile(acc, T.y + wa * 128, tn * BN + wb * 128, lane);
+  __syncthreads();
+  epi.store(img, T.y, tn * BN, tr, tid);
 }
 
 }  // namespace

@@ -18,7 +18,7 @@ namespace clef {
 
 namespace {
 
-constexpr int SBM = 64, SBN = 128, SKC = 128;
+constexpr int SBM = kSgemmRows, SBN = 128, SKC = 128;
 
 template <class Ld, class Epi>
 __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __restrict__ W, int M, int N,
@@ -44,19 +44,30 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)(n0 + w * 32 + cb * 16 + (lane & 15)) * K + (lane >> 4) * 8;
 
+  // Register double buffer: the next chunk's A and B loads are issued before
+  // the current chunk's MFMAs, so each workgroup pays one memory round trip
+  // per launch instead of one per chunk.
+  typename Ld::Raw ra[4];
+  uint4 bq[2][4];
+#define SG_FETCH(K0)                                                                     \
+  {                                                                                      \
+    _Pragma("unroll") for (int cb = 0; cb < 2; ++cb)                                     \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                   \
+        bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (K0) + kk * 32);           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+      const int v = tid + 256 * i, r = v >> 4, c = v & 15;                               \
+      if (m0 + r < M) ra[i] = ld.fetch(m0 + r, (K0) + c * 8);                            \
+    }                                                                                    \
+  }
+  SG_FETCH(kb)
   for (int k0 = kb; k0 < ke; k0 += SKC) {
-    uint4 bq[2][4];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + k0 + kk * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = tid + 256 * i;
       const int r = v >> 4, c = v & 15;
       float x[8];
       if (m0 + r < M) {
-        ld.finish(ld.fetch(m0 + r, k0 + c * 8), m0 + r, k0 + c * 8, x);
+        ld.finish(ra[i], m0 + r, k0 + c * 8, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -67,7 +78,13 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
       sAh[idx] = hi;
       sAl[idx] = lo;
     }
+    uint4 bc[2][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bc[cb][kk] = bq[cb][kk];
     __syncthreads();
+    if (k0 + SKC < ke) SG_FETCH(k0 + SKC)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk * 4 + (lane >> 4);
@@ -78,7 +95,7 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
         const bf16x8 al = as_bf16x8(sAl[r * 16 + (c ^ (r & 15))]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          const bf16x8 b = as_bf16x8(bq[cb][kk]);
+          const bf16x8 b = as_bf16x8(bc[cb][kk]);
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[rb][cb], 0, 0, 0);
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[rb][cb], 0, 0, 0);
         }
@@ -86,6 +103,7 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
     }
     __syncthreads();
   }
+#undef SG_FETCH
 
   // 16x16 accumulator layout: lane holds column (lane & 15), rows 4 * (lane / 16) + e.
   if (nsplit == 1) {
@@ -128,11 +146,15 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (stats == nullptr && i >= (size_t)M * N) return;
   const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
-  float4 s = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
-  for (int q = 1; q < nsplit; ++q) {
-    const float4 t = *reinterpret_cast<const float4*>(part + ((size_t)q * Mp + m) * N + n);
-    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-  }
+  // all slices in flight at once, summed in slice order
+  float4 t[kMaxSplit];
+#pragma unroll
+  for (int q = 0; q < kMaxSplit; ++q)
+    if (q < nsplit) t[q] = *reinterpret_cast<const float4*>(part + ((size_t)q * Mp + m) * N + n);
+  float4 s = t[0];
+#pragma unroll
+  for (int q = 1; q < kMaxSplit; ++q)
+    if (q < nsplit) { s.x += t[q].x; s.y += t[q].y; s.z += t[q].z; s.w += t[q].w; }
   const float a = epi(m, n, s.x), b = epi(m, n + 1, s.y), c = epi(m, n + 2, s.z), d = epi(m, n + 3, s.w);
   if (stats != nullptr) {
     const float mu = block_sum<4>((a + b) + (c + d), sm) * (1.0f / 1024);
@@ -151,7 +173,7 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
   const int tiles = s.mtiles * s.ntiles;
   const int kblocks = K / SKC;
   int split = (512 + tiles - 1) / tiles;
-  if (split > 16) split = 16;
+  if (split > kMaxSplit) split = kMaxSplit;
   if (split > kblocks) split = kblocks;
   if (split < 1) split = 1;
   if (need_reduce && split < 2) split = 2;
@@ -176,6 +198,17 @@ void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W,
   }
 }
 
+template <class Ld>
+SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, int M, int N, int K, float* part) {
+  const SgemmShape s = sgemm_shape(M, N, K, false);
+  if (M == 0) return s;
+  hipLaunchKernelGGL((k_sgemm<Ld, EpPart>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld,
+                     EpPart{part, N}, W, M, N, K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part);
+  return s;
+}
+template SgemmShape launch_sgemm_partial<LdLN>(hipStream_t, const LdLN&, const bf16_t*, int, int, int, float*);
+template SgemmShape launch_sgemm_partial<LdZ>(hipStream_t, const LdZ&, const bf16_t*, int, int, int, float*);
+
 #define INST(LD, EP)                                                                                   \
   template void launch_sgemm<LD, EP>(hipStream_t, const LD&, const EP&, const bf16_t*, int, int, int, \
                                      float*, float2*, float);
@@ -185,7 +218,6 @@ INST(LdLN, EpStore)
 INST(LdLN, EpGelu)
 INST(LdSeg2, EpAddRow)
 INST(LdRows, EpSplit2)
-INST(LdZ, EpGelu)
 #undef INST
 
 }  // namespace clef

@@ -70,10 +70,13 @@ void launch_field_agg(hipStream_t st, const float* U, const int* o_off, const fl
                      fstats, eps);
 }
 
-// One block per question.  Hs = GELU(W1 z + b1) rows [NO][1024] (unused when
-// joint == 0).  jcos / mlp may be null.
+// One block per question.  The hidden layer GELU(W1 z + b1) of option k is
+// formed here from the split-K slices of W1 z (hpart, nsplit slices
+// hstride floats apart, rows of 1024; unused when joint == 0).  jcos / mlp may
+// be null.
 __global__ __launch_bounds__(256) void k_score(const float* __restrict__ U, const float* __restrict__ F,
-                                               const float* __restrict__ Hs, const float* __restrict__ w2, float b2,
+                                               const float* __restrict__ hpart, int nsplit, size_t hstride,
+                                               const float* __restrict__ b1, const float* __restrict__ w2, float b2,
                                                const float* __restrict__ prior, float gate, float lam, int joint,
                                                const int* __restrict__ o_off, float* __restrict__ logits,
                                                float* __restrict__ probs, int* __restrict__ amax,
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(256) void k_score(const float* __restrict__ U, cons
     const float ff = block_sum<4>(dot4(f, f), sm);
     for (int k = o0; k < o1; ++k) {
       const float4 u = ld4(U + (size_t)k * 1024 + e);
-      const float4 h = ld4(Hs + (size_t)k * 1024 + e);
+      float4 h = sum_slices4(hpart + (size_t)k * 1024 + e, nsplit, hstride, b1 + e);
+      h.x = gelu_erf(h.x); h.y = gelu_erf(h.y); h.z = gelu_erf(h.z); h.w = gelu_erf(h.w);
       const float uf = block_sum<4>(dot4(u, f), sm);
       const float uu = block_sum<4>(dot4(u, u), sm);
       const float r = block_sum<4>(dot4(w, h), sm) + b2;
@@ -119,12 +123,12 @@ __global__ __launch_bounds__(256) void k_score(const float* __restrict__ U, cons
   }
 }
 
-void launch_score(hipStream_t st, const float* U, const float* F, const float* Hs, const float* w2, float b2,
-                  const float* prior, float gate, float lam, int joint, const int* o_off, int NQ, float* logits,
-                  float* probs, int* amax, float* jcos, float* mlp) {
+void launch_score(hipStream_t st, const float* U, const float* F, const float* hpart, int nsplit, size_t hstride,
+                  const float* b1, const float* w2, float b2, const float* prior, float gate, float lam, int joint,
+                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp) {
   if (NQ == 0) return;
-  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(256), 0, st, U, F, Hs, w2, b2, prior, gate, lam, joint, o_off, logits,
-                     probs, amax, jcos, mlp);
+  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(256), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
+                     joint, o_off, logits, probs, amax, jcos, mlp);
 }
 
 }  // namespace clef

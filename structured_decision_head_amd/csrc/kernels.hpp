@@ -168,6 +168,33 @@ struct EpResid {         // C += acc + bias (residual stream)
   }
 };
 
+struct EpPart {          // C = acc (one raw split-K slice; the consumer adds the bias)
+  float* C;
+  int ldc;
+  DEV float operator()(int m, int n, float v) const {
+    C[(size_t)m * ldc + n] = v;
+    return v;
+  }
+};
+
+constexpr int kMaxSplit = 16;   // most K slices a small GEMM is split into
+constexpr int kSgemmRows = 64;  // rows per small-GEMM tile (slice row stride is a multiple)
+
+// Sum of the split-K slices of 4 consecutive outputs, in slice order, plus bias
+// (the same order the reduction kernel uses).
+DEV float4 sum_slices4(const float* p, int nsplit, size_t stride, const float* bias) {
+  float4 t[kMaxSplit];
+#pragma unroll
+  for (int q = 0; q < kMaxSplit; ++q)
+    if (q < nsplit) t[q] = *reinterpret_cast<const float4*>(p + (size_t)q * stride);
+  float4 s = t[0];
+#pragma unroll
+  for (int q = 1; q < kMaxSplit; ++q)
+    if (q < nsplit) { s.x += t[q].x; s.y += t[q].y; s.z += t[q].z; s.w += t[q].w; }
+  const float4 b = *reinterpret_cast<const float4*>(bias);
+  return make_float4(s.x + b.x, s.y + b.y, s.z + b.z, s.w + b.w);
+}
+
 struct SgemmShape {
   int mtiles, ntiles, kchunk, nsplit;
   size_t part_floats;
@@ -181,6 +208,11 @@ template <class Ld, class Epi>
 void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part,
                   float2* stats = nullptr, float eps = 0.f);
 
+// No reduction pass: slice q of A W^T (without bias) is left at
+// part + (q * mtiles * kSgemmRows + m) * N + n for the consumer to sum.
+template <class Ld>
+SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, int N, int K, float* part);
+
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
@@ -191,7 +223,9 @@ void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16
                        long long Ptot);
 void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
                           const int* opt_rec, const int* rec, int NO, float* out);
-void launch_field_attn(hipStream_t, const float* QKV, const int* rec, int nrec, float* out);
+// QKV: split-K slices (nsplit, slice stride in floats, row width 3072) + bias
+void launch_field_attn(hipStream_t, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
+                       const int* rec, int nrec, float* out);
 
 // ---------------------------------------------------------------------------
 // aggregation and scoring
@@ -199,8 +233,9 @@ void launch_field_attn(hipStream_t, const float* QKV, const int* rec, int nrec, 
 void launch_field_agg(hipStream_t, const float* U, const int* o_off, const float* sw, float sb, const float* qv,
                       const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F,
                       float2* fstats, float eps);
-void launch_score(hipStream_t, const float* U, const float* F, const float* Hs, const float* w2, float b2,
-                  const float* prior, float gate, float lam, int joint, const int* o_off, int NQ, float* logits,
-                  float* probs, int* amax, float* jcos, float* mlp);
+// hpart: split-K slices of W1 z (nsplit, slice stride in floats), b1 its bias
+void launch_score(hipStream_t, const float* U, const float* F, const float* hpart, int nsplit, size_t hstride,
+                  const float* b1, const float* w2, float b2, const float* prior, float gate, float lam, int joint,
+                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp);
 
 }  // namespace clef
