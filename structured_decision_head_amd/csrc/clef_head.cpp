@@ -354,6 +354,7 @@ struct Weights {
 struct clef_head {
   clef_head_config cfg;
   int device = 0;
+  int num_cu = 256;                      // compute units of the device (one big-GEMM tile each)
   const bf16_t* table = nullptr;
   void* dweights = nullptr;
   Weights w;
@@ -364,7 +365,8 @@ struct clef_head {
   size_t pinned_bytes = 0;
   hipEvent_t staged = nullptr;
   hipStream_t side = nullptr;            // second stream for the work independent of the big GEMMs
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t third = nullptr;           // K/V of the first row tiles, beside the memory GEMM's last round
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_mem0 = nullptr, ev_kv0 = nullptr;
   bool staged_pending = false;
   // trace
   bool trace = false;
@@ -691,7 +693,9 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
   clef_head* h = new clef_head();
   h->cfg = *cfg;
   h->table = static_cast<const bf16_t*>(lexical_table);
-  if (hipGetDevice(&h->device) != hipSuccess) {
+  if (hipGetDevice(&h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+      h->num_cu <= 0) {
     delete h;
     return fail(CLEF_E_HIP, "no HIP device");
   }
@@ -703,7 +707,10 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
   if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
-      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
+      hipEventCreateWithFlags(&h->ev_mem0, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_kv0, hipEventDisableTiming) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->third, hipStreamNonBlocking) != hipSuccess) {
     clef_head_destroy(h);
     return fail(CLEF_E_HIP, "creating events / the side stream failed");
   }
@@ -718,8 +725,14 @@ void clef_head_destroy(clef_head* h) {
     (void)hipStreamSynchronize(h->side);
     (void)hipStreamDestroy(h->side);
   }
+  if (h->third) {
+    (void)hipStreamSynchronize(h->third);
+    (void)hipStreamDestroy(h->third);
+  }
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_mem0) (void)hipEventDestroy(h->ev_mem0);
+  if (h->ev_kv0) (void)hipEventDestroy(h->ev_kv0);
   if (h->staged) {
     if (h->staged_pending) (void)hipEventSynchronize(h->staged);
     (void)hipEventDestroy(h->staged);
@@ -927,7 +940,22 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
 
   if (joint) {
     // step 2: memory and K/V of every routing layer (main stream)
-    if (NR > 0) {
+    // The memory GEMM runs 4 workgroups per row tile, one per CU.  When its
+    // last round is partial, it is launched in two parts: the K/V GEMM of the
+    // first part's rows starts on a third stream as soon as that part is done
+    // and fills the CUs the second part leaves idle.
+    const int full = (p.ntiles * 4 / h->num_cu) * h->num_cu / 4;   // row tiles filling whole rounds
+    const int first = (fork && full > 0 && full < p.ntiles) ? full : 0;
+    if (NR > 0 && first > 0) {
+      launch_gemm_mem(st, X, (int)H, tiles, first, W.Wmem, stats, W.cmem, W.dmem, mem);
+      HIPCHK(hipEventRecord(h->ev_mem0, st));
+      launch_gemm_mem(st, X, (int)H, tiles + first, p.ntiles - first, W.Wmem, stats, W.cmem, W.dmem, mem);
+      HIPCHK(hipStreamWaitEvent(h->third, h->ev_mem0, 0));
+      launch_gemm_kv(h->third, mem, kvtiles, first, W.Wkv, W.bkv, NR, kv, p.Tpad);
+      HIPCHK(hipEventRecord(h->ev_kv0, h->third));
+      launch_gemm_kv(st, mem, kvtiles + first, p.ntiles - first, W.Wkv, W.bkv, NR, kv, p.Tpad);
+      HIPCHK(hipStreamWaitEvent(st, h->ev_kv0, 0));
+    } else if (NR > 0) {
       launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
       MARK(CLEF_STAGE_MEMORY_GEMM);
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);

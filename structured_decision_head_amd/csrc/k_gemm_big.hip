@@ -316,15 +316,20 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
     WAIT_VM(8 * (NST - 2));              // the next stage has landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    COPY_STAGE(cur, (kt + NST) * KS)
     LOAD_FRAGS(X, (kt + 1) % NST, 0)
+    COPY_STAGE(cur, (kt + NST) * KS)
     MULTIPLY(Y)
+    // the next step's fragment reads go first so they land before it starts;
+    // the stage refill copies ride along the later MFMAs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // LDS read
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // global -> LDS copy
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -191,35 +191,4 @@ void launch_lex_prior(hipStream_t st, const bf16_t* E, int H, const int4* ent, i
   }
 }
 
-// ---------------------------------------------------------------------------
-// mu / rstd of fp32 rows of width 1024 (one wave per row).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rowstats_f32(const float* __restrict__ X, int M,
-                                                      float2* __restrict__ stats, float eps) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= M) return;
-  const float4* row = reinterpret_cast<const float4*>(X + (size_t)r * 1024);
-  float4 v[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) v[c] = row[c * 64 + lane];
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
-  const float mu = wave_sum(s) * (1.0f / 1024);
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float a = v[c].x - mu, b = v[c].y - mu, d = v[c].z - mu, e = v[c].w - mu;
-    ss += a * a + b * b + d * d + e * e;
-  }
-  const float var = wave_sum(ss) * (1.0f / 1024);
-  if (lane == 0) stats[r] = make_float2(mu, 1.0f / sqrtf(var + eps));
-}
-
-void launch_rowstats_f32(hipStream_t st, const float* X, int M, float2* stats, float eps) {
-  if (M == 0) return;
-  hipLaunchKernelGGL(k_rowstats_f32, dim3((M + 3) / 4), dim3(256), 0, st, X, M, stats, eps);
-}
-
 }  // namespace clef

@@ -23,7 +23,6 @@ void launch_pool(hipStream_t, const bf16_t* X, int H, const int4* ent, int nent,
 // entries: int4 (first id, count, question slot, global slot)
 void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int nent, const int* ids,
                       const float* pooled, float* ebar, float* prior);
-void launch_rowstats_f32(hipStream_t, const float* X, int M, float2* stats, float eps);
 
 // ---------------------------------------------------------------------------
 // big GEMMs (rows of the packed row space)
