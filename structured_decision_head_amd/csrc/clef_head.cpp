@@ -50,7 +50,12 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int D = 1024, F = 4096, NH = 16;
 constexpr int TILE = 256;     // row tile of the packed row space
-constexpr int KCH = kAttnChunk;   // keys per routing-attention chunk
+// Routing attention splits each record's keys into chunks, one wave per
+// (record, head, chunk, 32-query block).  The chunk is the largest power of
+// two from 128 to 4096 keys that still yields kAttnMinWaves waves: longer
+// chunks mean fewer flash-decode partials to write and merge, which matters
+// when a record has many query blocks.
+constexpr int kAttnMinWaves = 2048;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -138,7 +143,7 @@ int check_config(const clef_head_config* c) {
 struct Plan {
   int B = 0, NQ = 0, NO = 0, nact = 0;
   int64_t T = 0, Tpad = 0, Ptot = 0, nids = 0;
-  int ntiles = 0, npool = 0, nitems = 0;
+  int ntiles = 0, npool = 0, nitems = 0, kchunk = 128;
   std::vector<int32_t> tab;   // all int32 tables, back to back
   size_t off_rec = 0, off_tiles = 0, off_kvtiles = 0, off_pool = 0, off_lex = 0, off_ids = 0, off_optq = 0,
          off_optrec = 0, off_qrec = 0, off_qtype = 0, off_ooff = 0, off_items = 0;
@@ -252,6 +257,19 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
   std::vector<int> act_of(B, -1);
   int64_t kv0 = 0, pbase = 0;
   int nact = 0;
+  auto attn_waves = [&](int64_t ch) {
+    int64_t w = 0;
+    for (int r = 0; r < B; ++r) {
+      const int q0 = b->q_offsets[r], nq = b->q_offsets[r + 1] - q0;
+      if (nq == 0) continue;
+      const int no = b->o_offsets[q0 + nq] - b->o_offsets[q0];
+      w += ceil_div(len[r], ch) * ceil_div(no, 32);
+    }
+    return w * NH;
+  };
+  int KCH = 128;
+  while (KCH < 4096 && attn_waves(2 * KCH) >= kAttnMinWaves) KCH *= 2;
+  p.kchunk = KCH;
   for (int r = 0; r < B; ++r) {
     const int q0 = b->q_offsets[r], nq = b->q_offsets[r + 1] - q0;
     if (nq == 0) continue;
@@ -991,7 +1009,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
         launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
         MARK(CLEF_STAGE_ROUTE_DENSE);
       }
-      launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot);
+      launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot, p.kchunk);
       launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
       MARK(CLEF_STAGE_ROUTE_ATTN);
       launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, ustats, eps);

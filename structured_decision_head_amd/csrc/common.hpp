@@ -77,6 +77,20 @@ DEV float wave_max(float v) {
   return v;
 }
 
+// Maximum over a whole block of NW waves; every thread gets the result.
+template <int NW>
+DEV float block_max(float v, float* sm) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm[w] = v;
+  __syncthreads();
+  float t = sm[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) t = fmaxf(t, sm[i]);
+  __syncthreads();
+  return t;
+}
+
 // Sum over a whole block of NW waves; every thread gets the result.  `sm`
 // needs NW floats; the call ends with a barrier so `sm` can be reused.
 template <int NW>

@@ -2,7 +2,8 @@
 //
 // Evidence routing (clef-4bit page §三 step 2; Clef-Flash overview §三): all
 // option queries of a record attend, per head, over every valid memory row of
-// that record.  The keys are split into 128-row chunks; one wave owns
+// that record.  The keys are split into chunks (a multiple of 64 rows, chosen
+// per batch); one wave owns
 // (record, head, chunk), loops over its record's queries 32 at a time and
 // writes flash-decode partials (running max, running sum, unnormalised
 // output) that k_route_combine merges.  Scores and the value mix use
@@ -84,7 +85,7 @@ DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, flo
 
 // rec: per record 8 ints: kv0 (first row in the packed padded row space),
 // n (valid rows), o0 (first option), no (options), pbase, nc (chunks), q0, nq.
-// One wave per (record, head, chunk of kAttnChunk keys, block of 32 queries);
+// One wave per (record, head, chunk of `chunk` keys, block of 32 queries);
 // the next 32-key step's K and V are in flight while the current one is
 // multiplied.  Query blocks of one chunk re-read the same K/V rows from cache.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_route_attn(const float* __restrict__ Q, const bf16_t* __restrict__ Kl,
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                     const int4* __restrict__ items, int nitems,
                                                     const int* __restrict__ rec, float* __restrict__ pm,
                                                     float* __restrict__ pl, float* __restrict__ po, long long Ptot,
-                                                    float scale_log2) {
+                                                    int chunk, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int it = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (it >= nitems) return;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int* R = rec + 8 * bc.x;
   const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
   const int c = bc.y;
-  const int k_lo = c * kAttnChunk, k_hi = min(n, k_lo + kAttnChunk);
+  const int k_lo = c * chunk, k_hi = min(n, k_lo + chunk);
   const bf16_t* Kj = Kl + (size_t)j * Tpad * 64;
   const bf16_t* Vj = Vl + (size_t)j * Tpad * 64;
   const int g = lane >> 5, l32 = lane & 31;
@@ -159,11 +160,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
                        const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
-                       long long Ptot) {
+                       long long Ptot, int chunk) {
   if (nitems == 0) return;
   const float scale_log2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
   hipLaunchKernelGGL(k_route_attn, dim3((nitems + 3) / 4, 16), dim3(256), 0, st, Q, Kl, Vl, Tpad, items, nitems,
-                     rec, pm, pl, po, Ptot, scale_log2);
+                     rec, pm, pl, po, Ptot, chunk, scale_log2);
 }
 
 // Merge the chunk partials of (option, head): one wave.  Lanes split the
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
     float m = -INFINITY, l = 0.f;
     for (int kb = 0; kb < nq; kb += 64) {
       const int nk = min(64, nq - kb);
-      __syncthreads();
+      if (qb > 0 || kb > 0) __syncthreads();   // the previous block's keys are still being read
       // 64 rows x 16 float4 each for K and V: 4 float4 per thread
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

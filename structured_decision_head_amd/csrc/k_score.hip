@@ -18,47 +18,64 @@ DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 DEV float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 }  // namespace
 
-// One block (256 threads, 4 elements each) per question.
-__global__ __launch_bounds__(256) void k_field_agg(const float* __restrict__ U, const int* __restrict__ o_off,
+constexpr int kQW = 8;                 // waves per question block
+constexpr int kQT = kQW * 64;
+
+// Lane l of a wave owns elements 4 l + 256 c .. + 3 (c = 0..3) of a 1024-wide
+// row, so each float4 load of a wave reads 1 KB of contiguous memory.
+DEV int el(int lane, int c) { return lane * 4 + 256 * c; }
+
+// One block (8 waves) per question.  The option scores w_s . u_k + b_s are
+// computed one option per wave (wave-level sums, no block barrier between
+// options); the softmax-weighted option sum is formed with two elements per
+// thread; the new field row's LayerNorm statistics close the kernel.
+__global__ __launch_bounds__(kQT) void k_field_agg(const float* __restrict__ U, const int* __restrict__ o_off,
                                                    const float* __restrict__ sw, float sb,
                                                    const float* __restrict__ qv, const float* __restrict__ gp,
                                                    const int* __restrict__ q_rec, const int* __restrict__ q_type,
                                                    const float* __restrict__ temb, float* __restrict__ F,
                                                    float2* __restrict__ fstats, float eps) {
-  __shared__ float sm[4];
+  __shared__ float sm[kQW];
   __shared__ float sc[kMaxOptions];
   const int q = blockIdx.x;
-  const int o0 = o_off[q], o1 = o_off[q + 1];
-  const int e = threadIdx.x * 4;
-  const float4 w = ld4(sw + e);
-  for (int k = o0; k < o1; ++k) {
-    const float s = block_sum<4>(dot4(w, ld4(U + (size_t)k * 1024 + e)), sm);
-    if (threadIdx.x == 0) sc[k - o0] = s + sb;
+  const int o0 = o_off[q], no = o_off[q + 1] - o0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float4 wv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) wv[c] = ld4(sw + el(lane, c));
+  for (int k = w; k < no; k += kQW) {
+    const float* u = U + (size_t)(o0 + k) * 1024;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += dot4(wv[c], ld4(u + el(lane, c)));
+    s = wave_sum(s);
+    if (lane == 0) sc[k] = s + sb;
   }
   __syncthreads();
-  float mx = -INFINITY;
-  for (int k = 0; k < o1 - o0; ++k) mx = fmaxf(mx, sc[k]);
+  float m = -INFINITY;
+  for (int k = threadIdx.x; k < no; k += kQT) m = fmaxf(m, sc[k]);
+  m = block_max<kQW>(m, sm);
   float z = 0.f;
-  for (int k = 0; k < o1 - o0; ++k) z += expf(sc[k] - mx);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = o0; k < o1; ++k) {
-    const float b = expf(sc[k - o0] - mx) / z;
-    const float4 u = ld4(U + (size_t)k * 1024 + e);
-    acc.x += b * u.x; acc.y += b * u.y; acc.z += b * u.z; acc.w += b * u.w;
+  for (int k = threadIdx.x; k < no; k += kQT) z += expf(sc[k] - m);
+  z = block_sum<kQW>(z, sm);
+  const float iz = 1.0f / z;
+  // two consecutive elements per thread
+  const int e = threadIdx.x * 2;
+  float a0 = 0.f, a1 = 0.f;
+  for (int k = 0; k < no; ++k) {
+    const float b = expf(sc[k] - m) * iz;
+    const float2 u = *reinterpret_cast<const float2*>(U + (size_t)(o0 + k) * 1024 + e);
+    a0 += b * u.x;
+    a1 += b * u.y;
   }
-  const float4 a = ld4(qv + (size_t)q * 1024 + e);
-  const float4 g = ld4(gp + (size_t)q_rec[q] * 1024 + e);
-  const float4 t = ld4(temb + (size_t)q_type[q] * 1024 + e);
-  float4 r;
-  r.x = a.x + acc.x + g.x + t.x;
-  r.y = a.y + acc.y + g.y + t.y;
-  r.z = a.z + acc.z + g.z + t.z;
-  r.w = a.w + acc.w + g.w + t.w;
-  *reinterpret_cast<float4*>(F + (size_t)q * 1024 + e) = r;
+  const float2 a = *reinterpret_cast<const float2*>(qv + (size_t)q * 1024 + e);
+  const float2 g = *reinterpret_cast<const float2*>(gp + (size_t)q_rec[q] * 1024 + e);
+  const float2 t = *reinterpret_cast<const float2*>(temb + (size_t)q_type[q] * 1024 + e);
+  const float r0 = a.x + a0 + g.x + t.x, r1 = a.y + a1 + g.y + t.y;
+  *reinterpret_cast<float2*>(F + (size_t)q * 1024 + e) = make_float2(r0, r1);
   // LayerNorm statistics of the new field row (input of the first field layer)
-  const float mu = block_sum<4>((r.x + r.y) + (r.z + r.w), sm) * (1.0f / 1024);
-  const float va = block_sum<4>((r.x - mu) * (r.x - mu) + (r.y - mu) * (r.y - mu) + (r.z - mu) * (r.z - mu) +
-                                    (r.w - mu) * (r.w - mu), sm) * (1.0f / 1024);
+  const float mu = block_sum<kQW>(r0 + r1, sm) * (1.0f / 1024);
+  const float va = block_sum<kQW>((r0 - mu) * (r0 - mu) + (r1 - mu) * (r1 - mu), sm) * (1.0f / 1024);
   if (threadIdx.x == 0) fstats[q] = make_float2(mu, 1.0f / sqrtf(va + eps));
 }
 
@@ -66,68 +83,98 @@ void launch_field_agg(hipStream_t st, const float* U, const int* o_off, const fl
                       const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F,
                       float2* fstats, float eps) {
   if (NQ == 0) return;
-  hipLaunchKernelGGL(k_field_agg, dim3(NQ), dim3(256), 0, st, U, o_off, sw, sb, qv, gp, q_rec, q_type, temb, F,
+  hipLaunchKernelGGL(k_field_agg, dim3(NQ), dim3(kQT), 0, st, U, o_off, sw, sb, qv, gp, q_rec, q_type, temb, F,
                      fstats, eps);
 }
 
-// One block per question.  The hidden layer GELU(W1 z + b1) of option k is
-// formed here from the split-K slices of W1 z (hpart, nsplit slices
-// hstride floats apart, rows of 1024; unused when joint == 0).  jcos / mlp may
-// be null.
-__global__ __launch_bounds__(256) void k_score(const float* __restrict__ U, const float* __restrict__ F,
+// One block (8 waves) per question; one option per wave.  The hidden layer
+// GELU(W1 z + b1) of option k is formed here from the split-K slices of W1 z
+// (hpart, nsplit slices hstride floats apart, rows of 1024; unused when
+// joint == 0).  Softmax and first-index argmax run over the whole block.
+// jcos / mlp may be null.
+__global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, const float* __restrict__ F,
                                                const float* __restrict__ hpart, int nsplit, size_t hstride,
                                                const float* __restrict__ b1, const float* __restrict__ w2, float b2,
                                                const float* __restrict__ prior, float gate, float lam, int joint,
                                                const int* __restrict__ o_off, float* __restrict__ logits,
                                                float* __restrict__ probs, int* __restrict__ amax,
                                                float* __restrict__ jcos, float* __restrict__ mlp) {
-  __shared__ float sm[4];
+  __shared__ float sm[kQW];
+  __shared__ int si[kQW];
   __shared__ float sl[kMaxOptions];
   const int q = blockIdx.x;
-  const int o0 = o_off[q], o1 = o_off[q + 1];
-  const int e = threadIdx.x * 4;
+  const int o0 = o_off[q], no = o_off[q + 1] - o0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (joint) {
-    const float4 f = ld4(F + (size_t)q * 1024 + e);
-    const float4 w = ld4(w2 + e);
-    const float ff = block_sum<4>(dot4(f, f), sm);
-    for (int k = o0; k < o1; ++k) {
-      const float4 u = ld4(U + (size_t)k * 1024 + e);
-      float4 h = sum_slices4(hpart + (size_t)k * 1024 + e, nsplit, hstride, b1 + e);
-      h.x = gelu_erf(h.x); h.y = gelu_erf(h.y); h.z = gelu_erf(h.z); h.w = gelu_erf(h.w);
-      const float uf = block_sum<4>(dot4(u, f), sm);
-      const float uu = block_sum<4>(dot4(u, u), sm);
-      const float r = block_sum<4>(dot4(w, h), sm) + b2;
-      if (threadIdx.x == 0) {
-        const float c = uf / (fmaxf(sqrtf(uu), 1e-8f) * fmaxf(sqrtf(ff), 1e-8f));
-        sl[k - o0] = prior[k] + gate * (lam * c + r);
-        if (jcos) jcos[k] = c;
-        if (mlp) mlp[k] = r;
+    float4 f[4], wv[4];
+    float ff = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f[c] = ld4(F + (size_t)q * 1024 + el(lane, c));
+      wv[c] = ld4(w2 + el(lane, c));
+      ff += dot4(f[c], f[c]);
+    }
+    ff = wave_sum(ff);
+    for (int k = w; k < no; k += kQW) {
+      const size_t row = (size_t)(o0 + k) * 1024;
+      float uf = 0.f, uu = 0.f, r = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 u = ld4(U + row + el(lane, c));
+        float4 h = sum_slices4(hpart + row + el(lane, c), nsplit, hstride, b1 + el(lane, c));
+        h.x = gelu_erf(h.x); h.y = gelu_erf(h.y); h.z = gelu_erf(h.z); h.w = gelu_erf(h.w);
+        uf += dot4(u, f[c]);
+        uu += dot4(u, u);
+        r += dot4(wv[c], h);
+      }
+      uf = wave_sum(uf);
+      uu = wave_sum(uu);
+      r = wave_sum(r) + b2;
+      if (lane == 0) {
+        const float cs = uf / (fmaxf(sqrtf(uu), 1e-8f) * fmaxf(sqrtf(ff), 1e-8f));
+        sl[k] = prior[o0 + k] + gate * (lam * cs + r);
+        if (jcos) jcos[o0 + k] = cs;
+        if (mlp) mlp[o0 + k] = r;
       }
     }
-  } else if (threadIdx.x == 0) {
-    for (int k = o0; k < o1; ++k) sl[k - o0] = prior[k];
+  } else {
+    for (int k = threadIdx.x; k < no; k += kQT) sl[k] = prior[o0 + k];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mx = sl[0];
-    int best = 0;
-    for (int k = 1; k < o1 - o0; ++k)
-      if (sl[k] > mx) { mx = sl[k]; best = k; }
-    float z = 0.f;
-    for (int k = 0; k < o1 - o0; ++k) z += expf(sl[k] - mx);
-    for (int k = 0; k < o1 - o0; ++k) {
-      logits[o0 + k] = sl[k];
-      probs[o0 + k] = expf(sl[k] - mx) / z;
-    }
-    amax[q] = best;
+  // first maximal index: larger value wins, ties go to the smaller index
+  float m = -INFINITY;
+  int best = 0x7fffffff;
+  for (int k = threadIdx.x; k < no; k += kQT)
+    if (sl[k] > m) { m = sl[k]; best = k; }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float mo = __shfl_xor(m, o, 64);
+    const int bo = __shfl_xor(best, o, 64);
+    if (mo > m || (mo == m && bo < best)) { m = mo; best = bo; }
   }
+  if (lane == 0) { sm[w] = m; si[w] = best; }
+  __syncthreads();
+  m = sm[0];
+  best = si[0];
+#pragma unroll
+  for (int i = 1; i < kQW; ++i)
+    if (sm[i] > m || (sm[i] == m && si[i] < best)) { m = sm[i]; best = si[i]; }
+  __syncthreads();
+  float z = 0.f;
+  for (int k = threadIdx.x; k < no; k += kQT) z += expf(sl[k] - m);
+  z = block_sum<kQW>(z, sm);
+  for (int k = threadIdx.x; k < no; k += kQT) {
+    logits[o0 + k] = sl[k];
+    probs[o0 + k] = expf(sl[k] - m) / z;
+  }
+  if (threadIdx.x == 0) amax[q] = best == 0x7fffffff ? 0 : best;   // no comparable value: index 0
 }
 
 void launch_score(hipStream_t st, const float* U, const float* F, const float* hpart, int nsplit, size_t hstride,
                   const float* b1, const float* w2, float b2, const float* prior, float gate, float lam, int joint,
                   const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp) {
   if (NQ == 0) return;
-  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(256), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
+  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(kQT), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
                      joint, o_off, logits, probs, amax, jcos, mlp);
 }
 

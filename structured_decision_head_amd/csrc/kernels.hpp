@@ -5,7 +5,6 @@
 namespace clef {
 
 constexpr int kMaxOptions = 1024;   // options of one question (LDS arrays in the per-question kernels)
-constexpr int kAttnChunk = 128;     // keys per routing-attention work item (one wave)
 
 // Position of key k (0..31) inside a 32-key V block: the eight keys one lane
 // feeds to a V^T P^T MFMA step sit in 16 contiguous bytes.
@@ -216,10 +215,11 @@ SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, 
 // attention
 // ---------------------------------------------------------------------------
 // rec: 8 ints per active record: kv0, n, o0, no, pbase, nc, q0, nq
-// items: int4 (active record, key chunk, first query of a 32-query block, 0)
+// items: int4 (active record, key chunk, first query of a 32-query block, 0);
+// chunk: keys per chunk, a multiple of 64
 void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
                        const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
-                       long long Ptot);
+                       long long Ptot, int chunk);
 void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
                           const int* opt_rec, const int* rec, int NO, float* out);
 // QKV: split-K slices (nsplit, slice stride in floats, row width 3072) + bias
