@@ -55,7 +55,7 @@ constexpr int TILE = 256;     // row tile of the packed row space
 // two from 128 to 4096 keys that still yields kAttnMinWaves waves: longer
 // chunks mean fewer flash-decode partials to write and merge, which matters
 // when a record has many query blocks.
-constexpr int kAttnMinWaves = 2048;
+constexpr int kAttnMinWaves = 1024;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

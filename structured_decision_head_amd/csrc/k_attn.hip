@@ -95,9 +95,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                     float* __restrict__ pl, float* __restrict__ po, long long Ptot,
                                                     int chunk, float scale_log2) {
   const int lane = threadIdx.x & 63;
-  const int it = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // consecutive item groups of one head (the query blocks of one key chunk)
+  // go to the same XCD, so they share the chunk through its L2
+  const int gx = gridDim.x;
+  const int rl = xcd_remap(blockIdx.x + blockIdx.y * gx, gx * gridDim.y);
+  const int it = (rl % gx) * 4 + (threadIdx.x >> 6);
   if (it >= nitems) return;
-  const int j = blockIdx.y;
+  const int j = rl / gx;
   const int4 bc = items[it];             // (record, chunk, first query of the block, -)
   const int* R = rec + 8 * bc.x;
   const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
