@@ -52,9 +52,10 @@ constexpr int D = 1024, F = 4096, NH = 16;
 constexpr int TILE = 256;     // row tile of the packed row space
 // Routing attention splits each record's keys into chunks, one wave per
 // (record, head, chunk, 32-query block).  The chunk is the largest power of
-// two from 128 to 4096 keys that still yields kAttnMinWaves waves: longer
+// two from 128 to 1024 keys that still yields kAttnMinWaves waves: longer
 // chunks mean fewer flash-decode partials to write and merge, which matters
-// when a record has many query blocks.
+// when a record has many query blocks; beyond 1024 keys the longest records'
+// waves form a tail.
 constexpr int kAttnMinWaves = 1024;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -268,7 +269,7 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
     return w * NH;
   };
   int KCH = 128;
-  while (KCH < 4096 && attn_waves(2 * KCH) >= kAttnMinWaves) KCH *= 2;
+  while (KCH < 1024 && attn_waves(2 * KCH) >= kAttnMinWaves) KCH *= 2;
   p.kchunk = KCH;
   for (int r = 0; r < B; ++r) {
     const int q0 = b->q_offsets[r], nq = b->q_offsets[r + 1] - q0;

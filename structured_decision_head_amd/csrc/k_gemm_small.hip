@@ -18,12 +18,17 @@ namespace clef {
 
 namespace {
 
-constexpr int SBM = kSgemmRows, SBN = 128, SKC = 128;
+constexpr int SBM = kSgemmRows, SKC = 128;
 
-template <class Ld, class Epi>
+// Tile: 64 rows x (32 * 4 / WR) columns.  The 4 waves form a WR x (4 / WR)
+// grid; each wave owns 64 / WR rows and 32 columns.  Narrow tiles (WR = 2, 4)
+// give more workgroups for narrow outputs, so that the whole chip streams
+// the weights.
+template <int WR, class Ld, class Epi>
 __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __restrict__ W, int M, int N,
                                                int K, int kchunk, int mtiles, int ntiles, int nsplit,
                                                float* __restrict__ part) {
+  constexpr int WC = 4 / WR, SBN = 32 * WC, RB = 4 / WR;
   __shared__ uint4 sAh[SBM * 16], sAl[SBM * 16];   // [row * 16 + swizzled chunk], KC = 128 bf16 per row
 
   const int lt = xcd_remap(blockIdx.x, gridDim.x);
@@ -33,16 +38,17 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
   const int m0 = tm * SBM, n0 = tn * SBN;
   const int kb = ks * kchunk, ke = min(K, kb + kchunk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr0 = (w / WC) * (SBM / WR), wc0 = (w % WC) * 32;   // the wave's first row / column in the tile
 
-  f32x4 acc[4][2];
+  f32x4 acc[RB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16_t* wp[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)(n0 + w * 32 + cb * 16 + (lane & 15)) * K + (lane >> 4) * 8;
+  for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)(n0 + wc0 + cb * 16 + (lane & 15)) * K + (lane >> 4) * 8;
 
   // Register double buffer: the next chunk's A and B loads are issued before
   // the current chunk's MFMAs, so each workgroup pays one memory round trip
@@ -89,8 +95,8 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk * 4 + (lane >> 4);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int r = rb * 16 + (lane & 15);
+      for (int rb = 0; rb < RB; ++rb) {
+        const int r = wr0 + rb * 16 + (lane & 15);
         const bf16x8 ah = as_bf16x8(sAh[r * 16 + (c ^ (r & 15))]);
         const bf16x8 al = as_bf16x8(sAl[r * 16 + (c ^ (r & 15))]);
 #pragma unroll
@@ -108,13 +114,13 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
   // 16x16 accumulator layout: lane holds column (lane & 15), rows 4 * (lane / 16) + e.
   if (nsplit == 1) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
-          const int n = n0 + w * 32 + cb * 16 + (lane & 15);
+          const int m = m0 + wr0 + rb * 16 + 4 * (lane >> 4) + e;
+          const int n = n0 + wc0 + cb * 16 + (lane & 15);
           if (m < M) epi(m, n, acc[rb][cb][e]);
         }
     return;
@@ -125,13 +131,13 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
   const size_t Mp = (size_t)mtiles * SBM;
   float* P = part + (size_t)ks * Mp * N;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + rb * 16 + 4 * (lane >> 4) + e;
-        const int n = n0 + w * 32 + cb * 16 + (lane & 15);
+        const int m = m0 + wr0 + rb * 16 + 4 * (lane >> 4) + e;
+        const int n = n0 + wc0 + cb * 16 + (lane & 15);
         P[(size_t)m * N + n] = acc[rb][cb][e];
       }
 }
@@ -166,22 +172,45 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 }  // namespace
 
+// The widest tile (128, 64 or 32 columns) whose grid, split along K towards
+// 512 workgroups (at most kMaxSplit slices of 128-deep chunks), still has at
+// least 256 workgroups.
 SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
-  SgemmShape s;
+  SgemmShape s{};
   s.mtiles = (M + SBM - 1) / SBM;
-  s.ntiles = N / SBN;
-  const int tiles = s.mtiles * s.ntiles;
   const int kblocks = K / SKC;
-  int split = (512 + tiles - 1) / tiles;
-  if (split > kMaxSplit) split = kMaxSplit;
-  if (split > kblocks) split = kblocks;
-  if (split < 1) split = 1;
-  if (need_reduce && split < 2) split = 2;
-  const int per = (kblocks + split - 1) / split;
-  s.kchunk = per * SKC;
-  s.nsplit = (kblocks + per - 1) / per;
+  for (int wr = 1; wr <= 4; wr *= 2) {
+    const int sbn = 128 / wr;
+    s.wr = wr;
+    s.ntiles = N / sbn;
+    const int tiles = s.mtiles * s.ntiles;
+    int split = (512 + tiles - 1) / tiles;
+    if (split > kMaxSplit) split = kMaxSplit;
+    if (split > kblocks) split = kblocks;
+    if (split < 1) split = 1;
+    if (need_reduce && split < 2) split = 2;
+    const int per = (kblocks + split - 1) / split;
+    s.kchunk = per * SKC;
+    s.nsplit = (kblocks + per - 1) / per;
+    if (tiles * s.nsplit >= 256 || wr == 4 || (N / (sbn / 2)) * (sbn / 2) != N) break;
+  }
   s.part_floats = s.nsplit > 1 ? (size_t)s.nsplit * s.mtiles * SBM * N : 0;
   return s;
+}
+
+template <class Ld, class Epi>
+static void launch_tile(const SgemmShape& s, hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M,
+                        int N, int K, float* part) {
+  const dim3 grid(s.mtiles * s.ntiles * s.nsplit);
+  if (s.wr == 1)
+    hipLaunchKernelGGL((k_sgemm<1, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, part);
+  else if (s.wr == 2)
+    hipLaunchKernelGGL((k_sgemm<2, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, part);
+  else
+    hipLaunchKernelGGL((k_sgemm<4, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, part);
 }
 
 template <class Ld, class Epi>
@@ -189,8 +218,7 @@ void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W,
                   float* part, float2* stats, float eps) {
   if (M == 0) return;
   const SgemmShape s = sgemm_shape(M, N, K, stats != nullptr);
-  hipLaunchKernelGGL((k_sgemm<Ld, Epi>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld, epi, W, M, N,
-                     K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part);
+  launch_tile(s, st, ld, epi, W, M, N, K, part);
   if (s.nsplit > 1) {
     const size_t n4 = (size_t)M * N / 4;
     hipLaunchKernelGGL((k_splitk_reduce<Epi>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, s.nsplit,
@@ -202,8 +230,7 @@ template <class Ld>
 SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, int M, int N, int K, float* part) {
   const SgemmShape s = sgemm_shape(M, N, K, false);
   if (M == 0) return s;
-  hipLaunchKernelGGL((k_sgemm<Ld, EpPart>), dim3(s.mtiles * s.ntiles * s.nsplit), dim3(256), 0, st, ld,
-                     EpPart{part, N}, W, M, N, K, s.kchunk, s.mtiles, s.ntiles, s.nsplit, part);
+  launch_tile(s, st, ld, EpPart{part, N}, W, M, N, K, part);
   return s;
 }
 template SgemmShape launch_sgemm_partial<LdLN>(hipStream_t, const LdLN&, const bf16_t*, int, int, int, float*);

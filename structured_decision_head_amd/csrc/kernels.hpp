@@ -195,6 +195,7 @@ DEV float4 sum_slices4(const float* p, int nsplit, size_t stride, const float* b
 
 struct SgemmShape {
   int mtiles, ntiles, kchunk, nsplit;
+  int wr;                 // waves along rows: tile width 128 / wr columns
   size_t part_floats;
 };
 // need_reduce: always split K (>= 2 slices) so that a reduction pass runs
