@@ -204,26 +204,29 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // s_waitcnt lgkmcnt(0) only
 #define WAIT_LDS() __builtin_amdgcn_s_waitcnt((7 << 4) | 15 | (3 << 14))
 
-// Operand tiles live in a 4-stage LDS ring of 32-wide K steps; rows are 64 B
-// (four 16-byte chunks) and chunk c of row r sits at position c ^ ((r >> 2) & 3),
-// which keeps the fragment reads free of bank conflicts.  Global -> LDS copies
-// use global_load_lds_dwordx4: lane l of a wave writes the l-th 16-byte slot of
-// a 1 KB block, so each lane fetches the chunk that belongs in its slot.
+// Operand tiles live in a 2-stage LDS ring of 64-deep K steps; rows are 128 B
+// (eight 16-byte chunks) and chunk c of row r sits at position c ^ ((r >> 1) & 7),
+// which keeps the fragment reads of 16 lanes on distinct banks.  Global -> LDS
+// copies use buffer_load_dwordx4 ... lds: lane l of a wave writes the l-th
+// 16-byte slot of a 1 KB block (8 rows), so each lane fetches the chunk that
+// belongs in its slot.  Whole 128-byte row segments per copy stream about twice as fast
+// into a CU as 64-byte ones.
 //
-// Per K step a wave runs two 16-deep halves of 16 MFMAs; the fragments of the
-// next half are read while the current half multiplies, and the stage consumed
-// in this step is refilled (K step + 4) right after the mid-step barrier.
+// Per stage a wave runs four 16-deep substeps of 16 MFMAs, reading the next
+// substep's fragments while the current one multiplies.  The next stage was
+// copied during the whole previous stage; one barrier per stage hands it over
+// and frees the slot just consumed, which is refilled two stages ahead.
 template <class Epi>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
                const bf16_t* __restrict__ W, int K, Epi epi) {
-  constexpr int KS = 32, NST = 4;
-  constexpr int kRingBytes = NST * 2 * BM * 4 * 16;
+  constexpr int KS = 64, NST = 2;
+  constexpr int kRingBytes = NST * 2 * BM * 8 * 16;
   constexpr int kSpan = Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
-  // operand ring [stage][A|B][row * 4 + swizzled chunk] (after the main loop the
+  // operand ring [stage][A|B][row * 8 + swizzled chunk] (after the main loop the
   // same bytes hold the output image), then the tile constants
   __shared__ __attribute__((aligned(16))) unsigned char lds[kSpan + kConstFloats * 4];
-  u32x4 (*smem)[2][BM * 4] = reinterpret_cast<u32x4 (*)[2][BM * 4]>(lds);
+  u32x4 (*smem)[2][BM * 8] = reinterpret_cast<u32x4 (*)[2][BM * 8]>(lds);
   float* cst = reinterpret_cast<float*>(lds + kSpan);
 
   int tm, tn;
@@ -238,46 +241,54 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   const int ra_src = tr ? 1 : 0, rb_src = tr ? 0 : 1;
   const int wa = tr ? wn : wm, wb = tr ? wm : wn;
 
-  // copy sources: instruction i of wave w fills rows 16 (4 w + i) .. +16 of a stage;
-  // A rows past the tile's valid count are clamped to its last valid row
-  const bf16_t* ga[4];
-  const bf16_t* gb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (w * 4 + i) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
-    ga[i] = A + (size_t)(T.x + min(row, T.z - 1)) * lda + c * 8;
-    gb[i] = W + (size_t)(tn * BN + row) * K + c * 8;
-  }
-  // fragment positions: 32x32x16 operands, lane -> row (lane & 31), chunk 2 kk + (lane >> 5)
-  int offA[2][4], offB[2][4];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wa * 128 + i * 32 + (lane & 31);
-      const int rb = wb * 128 + i * 32 + (lane & 31);
-      offA[kk][i] = ra_src * (BM * 4) + ra * 4 + (ch ^ ((ra >> 2) & 3));
-      offB[kk][i] = rb_src * (BM * 4) + rb * 4 + (ch ^ ((rb >> 2) & 3));
-    }
-  }
-#define COPY_STAGE(stage, k0)                                                                                  \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                              \
-    __builtin_amdgcn_global_load_lds((const void*)(ga[i] + (k0)), (lds_ptr_t)&smem[stage][0][64 * (w * 4 + i)], \
-                                     16, 0, 0);                                                                \
-    __builtin_amdgcn_global_load_lds((const void*)(gb[i] + (k0)), (lds_ptr_t)&smem[stage][1][64 * (w * 4 + i)], \
-                                     16, 0, 0);                                                                \
-  }
-#define LOAD_FRAGS(F, stage, kk)                                  \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                 \
-    F##a[i] = as_bf16x8(smem[stage][0][offA[kk][i]]);             \
-    F##b[i] = as_bf16x8(smem[stage][0][offB[kk][i]]);             \
+  // copy sources: instruction i of wave w fills rows 8 (8 w + i) .. +8 of a stage.
+  // Buffer copies: a uniform resource per operand (its record count bounds every
+  // copy to the tile's valid rows), a 32-bit byte offset per lane, the K position
+  // as the scalar offset.
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + (size_t)T.x * lda), 0, T.z * lda * 2, 0x00020000);   // valid rows only
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)(tn * BN) * K), 0, BN * K * 2, 0x00020000);
+  // rows of copy i are 8 i after those of copy 0, so their swizzle term
+  // ((row >> 1) & 7) differs by 4 i mod 8: even and odd copies use two bases.
+  // Rows past the tile's valid count read zeros (outside the A resource).
+  const int crow = 64 * w + (lane >> 3);
+  const int cch = (lane & 7) ^ ((crow >> 1) & 7);
+  const uint32_t aoffE = (uint32_t)(crow * lda + cch * 8) * 2, aoffO = (uint32_t)(crow * lda + (cch ^ 4) * 8) * 2;
+  const uint32_t woffE = (uint32_t)(crow * K + cch * 8) * 2, woffO = (uint32_t)(crow * K + (cch ^ 4) * 8) * 2;
+  const uint32_t astep = (uint32_t)(8 * lda) * 2, wstep = (uint32_t)(8 * K) * 2;
+  // fragment positions: 32x32x16 operands, lane -> row (lane & 31), chunk 2 kk + (lane >> 5).
+  // Block bases are multiples of 32 rows, so the swizzle depends on the lane only
+  // and block i of a substep sits 256 chunks after block 0.
+  const int l31 = lane & 31, hl = lane >> 5, fsw = (l31 >> 1) & 7;
+  const int fa0 = ra_src * (BM * 8) + (wa * 128 + l31) * 8;
+  const int fb0 = rb_src * (BM * 8) + (wb * 128 + l31) * 8;
+#define COPY_A(stage, k0)                                                                                      \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + i)], 16,            \
+                                             ((i & 1) ? aoffO : aoffE) + i * astep, (k0) * 2, 0, 0);
+#define COPY_B(stage, k0)                                                                                      \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + i)], 16,            \
+                                             ((i & 1) ? woffO : woffE) + i * wstep, (k0) * 2, 0, 0);
+#define COPY_STAGE(stage, k0) COPY_A(stage, k0) COPY_B(stage, k0)
+#define LOAD_FRAGS(F, stage, kk)                                                 \
+  {                                                                              \
+    const int ph_ = (2 * (kk) + hl) ^ fsw, sb_ = (stage) * (2 * BM * 8) + ph_;   \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                              \
+      F##a[i] = as_bf16x8(smem[0][0][sb_ + fa0 + i * 256]);                      \
+      F##b[i] = as_bf16x8(smem[0][0][sb_ + fb0 + i * 256]);                      \
+    }                                                                            \
   }
 #define MULTIPLY(F)                                                                       \
   _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                        \
   _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                        \
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[mi], F##b[ni], acc[mi][ni], 0, 0, 0);
+#define INTERLEAVE_DS(id)                                                      \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                             \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, id);   /* 2 MFMA */        \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, id);   /* 1 LDS read */    \
+  }
 
   float kc[4];
   epi.load_consts(T.y, tn * BN, tid, kc);   // consumed after the main loop
@@ -291,65 +302,43 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   bf16x8 Xa[4], Xb[4], Ya[4], Yb[4];
 
-  const int nk = K / KS;                 // >= 4 (K >= 128)
-#pragma unroll
-  for (int st = 0; st < NST - 1; ++st) { COPY_STAGE(st, st * KS) }
-  WAIT_VM(8 * (NST - 2));
+  const int nk = K / KS;                 // >= 2 (K a multiple of 128)
+  COPY_STAGE(0, 0)
+  WAIT_VM(0);
   __builtin_amdgcn_s_barrier();
   epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
-  COPY_STAGE(NST - 1, (NST - 1) * KS)
   LOAD_FRAGS(X, 0, 0)
-  int kt = 0;
-  for (; kt < nk - NST; ++kt) {          // steady state: refill the consumed stage with K step kt + 4
-    const int cur = kt % NST;
+  // One iteration per 32-deep half h of stage kt (substeps 2 h, 2 h + 1).  The
+  // first half copies stage kt + 1 into the other slot (freed by the previous
+  // stage's barrier); the second half ends with the barrier that hands it over.
+  for (int j = 0; j < 2 * nk; ++j) {
+    const int kt = j >> 1, h = j & 1, cur = kt & 1;
+    const bool cp = h == 0 && kt + 1 < nk;
+    if (cp) COPY_A(cur ^ 1, (kt + 1) * KS)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    LOAD_FRAGS(Y, cur, 1)
+    LOAD_FRAGS(Y, cur, 2 * h + 1)
     MULTIPLY(X)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-    }
+    INTERLEAVE_DS(0)
     __builtin_amdgcn_sched_barrier(0);
-    WAIT_LDS();                          // this stage is in registers everywhere after the barrier
-    WAIT_VM(8 * (NST - 2));              // the next stage has landed
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    LOAD_FRAGS(X, (kt + 1) % NST, 0)
-    COPY_STAGE(cur, (kt + NST) * KS)
-    MULTIPLY(Y)
-    // the next step's fragment reads go first so they land before it starts;
-    // the stage refill copies ride along the later MFMAs
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // LDS read
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // global -> LDS copy
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (; kt < nk; ++kt) {                // drain the ring
-    const int cur = kt % NST;
-    WAIT_LDS();
-    LOAD_FRAGS(Y, cur, 1)
-    MULTIPLY(X)
-    if (kt + 1 < nk) {
-      const int ahead = (nk - 1) - (kt + 1);
-      WAIT_LDS();
-      if (ahead >= 2) WAIT_VM(16); else if (ahead == 1) WAIT_VM(8); else WAIT_VM(0);
+    WAIT_LDS();                          // at h = 1 this stage is in registers everywhere after the barrier
+    if (h == 1 && kt + 1 < nk) {
+      WAIT_VM(0);                        // the next stage has landed
       __builtin_amdgcn_s_barrier();
-      LOAD_FRAGS(X, (kt + 1) % NST, 0)
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (cp) COPY_B(cur ^ 1, (kt + 1) * KS)
+    LOAD_FRAGS(X, h ? (cur ^ 1) : cur, h ? 0 : 2)
     MULTIPLY(Y)
+    INTERLEAVE_DS(1)
+    __builtin_amdgcn_sched_barrier(0);
   }
 #undef COPY_STAGE
+#undef COPY_A
+#undef COPY_B
 #undef LOAD_FRAGS
 #undef MULTIPLY
+#undef INTERLEAVE_DS
 
   // All 256 rows are stored: rows past the valid count come from clamped
   // (finite) inputs and keep the padded part of the row space finite.
