@@ -86,7 +86,7 @@ DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, flo
 // rec: per record 8 ints: kv0 (first row in the packed padded row space),
 // n (valid rows), o0 (first option), no (options), pbase, nc (chunks), q0, nq.
 // One wave per (record, head, chunk of `chunk` keys, block of 32 queries);
-// the next 32-key step's K and V are in flight while the current one is
+// the next two 32-key steps' K and V are in flight while the current one is
 // multiplied.  Query blocks of one chunk re-read the same K/V rows from cache.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_route_attn(const float* __restrict__ Q, const bf16_t* __restrict__ Kl,
                                                     const bf16_t* __restrict__ Vl, long long Tpad,
@@ -134,16 +134,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
 
-    // two steps per iteration so that the double buffer has static registers
-    KV32 a, b;
+    // three 32-key steps per iteration so that the triple buffer has static
+    // registers: two steps' K and V are in flight while one is multiplied
+    KV32 a, b, c3;
     kv_load(a, Kj, Vj, kv0 + k_lo, l32, g);
-    for (int kb = k_lo; kb < k_hi; kb += 64) {
-      const bool more = kb + 32 < k_hi;
-      if (more) kv_load(b, Kj, Vj, kv0 + kb + 32, l32, g);
+    if (k_lo + 32 < k_hi) kv_load(b, Kj, Vj, kv0 + k_lo + 32, l32, g);
+    for (int kb = k_lo; kb < k_hi; kb += 96) {
+      if (kb + 64 < k_hi) kv_load(c3, Kj, Vj, kv0 + kb + 64, l32, g);
       kv_step(a, qf, kb, n, g, scale_log2, m, l, o);
-      if (!more) break;
-      if (kb + 64 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 64, l32, g);
+      if (kb + 32 >= k_hi) break;
+      if (kb + 96 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 96, l32, g);
       kv_step(b, qf, kb + 32, n, g, scale_log2, m, l, o);
+      if (kb + 64 >= k_hi) break;
+      if (kb + 128 < k_hi) kv_load(b, Kj, Vj, kv0 + kb + 128, l32, g);
+      kv_step(c3, qf, kb + 64, n, g, scale_log2, m, l, o);
     }
     if (qvalid) {
       const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
