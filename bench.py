@@ -34,6 +34,8 @@ WORKLOADS = {
     3: "wide schema: B=4, L=8192, H=4096, 32 fields/record (8 noul, 16 choice of 4-16, 8 score), V=248320",
     4: "heterogeneous large backbone: B=32, H=5120, valid log-uniform [512, 16384], 1-16 fields, V=248320",
 }
+WORKLOAD_SLUGS = {0: "single_record_l160", 1: "online_serving_b8_l4096", 2: "long_state_l16384",
+                  3: "wide_schema_b4_l8192", 4: "heterogeneous_b32_h5120"}
 
 
 def log(*a):
@@ -51,7 +53,7 @@ def kernel_sources_sha(names):
 def load_traffic(stage, cfg_index):
     """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
     scaled by the copy-kernel calibration; None if absent or stale."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_cfg{cfg_index}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{WORKLOAD_SLUGS[cfg_index]}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -191,7 +193,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init head weights, N(0,1) hidden states, N(0,0.02) lexical table)",
-        "config": {"workload": f"cfg{args.config} " + WORKLOADS[args.config], "global_batch": int(b.B),
+        "config": {"workload": WORKLOADS[args.config], "global_batch": int(b.B),
                    "seq_len": int(b.L), "valid_rows": T, "questions": int(b.NQ), "options": int(b.NO)},
         "roofline": roofline,
         "stages": stages,

@@ -227,7 +227,7 @@ class CaseSpec:
     B: int
     L: Optional[int]                     # padded length; None = longest record
     lengths: Tuple[str, float, float]    # ("fixed", n, n) | ("uniform", lo, hi) | ("loguniform", lo, hi)
-    fields: str                          # "cfg0" | "counts" | "ordered" | "random"
+    fields: str                          # "single" | "counts" | "ordered" | "random"
     counts: Tuple[int, int, int] = (0, 0, 0)      # noul, choice, score (fields == "counts")
     ordered: Tuple[Tuple[int, int], ...] = ()     # (type, options) in order (fields == "ordered")
     field_range: Tuple[int, int] = (1, 16)        # fields == "random"
@@ -307,7 +307,7 @@ def _schema_block(rng, fields, spec: CaseSpec):
     return pos, out
 
 
-def _cfg0_schema(rng):
+def _single_record_schema(rng):
     """The explicit single-record layout: prefix 0-35, state 36-95, schema 96-150,
     suffix 151-159; noul field (instruction [97,107), options [107,110) and
     [110,113)); choice field (instruction [114,124), three options of 4-8 tokens
@@ -347,8 +347,8 @@ def make_batch(spec: CaseSpec) -> Batch:
     q_off = [0]
     for b in range(spec.B):
         n = lengths[b]
-        if spec.fields == "cfg0":
-            fl = _cfg0_schema(rs)
+        if spec.fields == "single":
+            fl = _single_record_schema(rs)
         else:
             for _attempt in range(10000):
                 fields = _draw_fields(rs, spec)
@@ -419,15 +419,15 @@ def config_spec(i: int, **over) -> CaseSpec:
     4: H=5120, B=32, valid log-uniform [512, 16384], 1-16 random fields.
     """
     base = {
-        0: CaseSpec("cfg0", 1000, HeadConfig(vocab_size=8192), 1, 160, ("fixed", 160, 160), "cfg0",
+        0: CaseSpec("single-record", 1000, HeadConfig(vocab_size=8192), 1, 160, ("fixed", 160, 160), "single",
                     suffix=9),
-        1: CaseSpec("cfg1", 1001, HeadConfig(), 8, 4096, ("uniform", 2048, 4096), "counts",
+        1: CaseSpec("online-serving", 1001, HeadConfig(), 8, 4096, ("uniform", 2048, 4096), "counts",
                     counts=(3, 3, 2), choice_opts=(2, 6)),
-        2: CaseSpec("cfg2", 1002, HeadConfig(), 1, 16384, ("fixed", 16384, 16384), "ordered",
+        2: CaseSpec("long-state", 1002, HeadConfig(), 1, 16384, ("fixed", 16384, 16384), "ordered",
                     ordered=((NOUL, 2), (CHOICE, 4), (CHOICE, 4), (SCORE, 5))),
-        3: CaseSpec("cfg3", 1003, HeadConfig(), 4, 8192, ("fixed", 8192, 8192), "counts",
+        3: CaseSpec("wide-schema", 1003, HeadConfig(), 4, 8192, ("fixed", 8192, 8192), "counts",
                     counts=(8, 16, 8), choice_opts=(4, 16)),
-        4: CaseSpec("cfg4", 1004, HeadConfig(hidden_size=5120), 32, None, ("loguniform", 512, 16384),
+        4: CaseSpec("heterogeneous-h5120", 1004, HeadConfig(hidden_size=5120), 32, None, ("loguniform", 512, 16384),
                     "random", field_range=(1, 16), choice_opts=(2, 8), pad_fill="nan"),
     }[i]
     head_over = {k: over.pop(k) for k in list(over) if k in HeadConfig.__dataclass_fields__}

@@ -34,8 +34,8 @@ def _check(case, out, name):
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_full_size_parity(torch_gpu, cfg):
     from structured_decision_head_amd.runner import HeadRunner
-    say(f"case cfg{cfg} full size")
     case = synth.config_case(cfg)
+    say(f"case {case.spec.name} full size")
     b = case.batch
     say(f"  B={b.B} L={b.L} T={int(b.lengths.sum())} NQ={b.NQ} NO={b.NO}")
     r = HeadRunner(case)
@@ -43,13 +43,13 @@ def test_full_size_parity(torch_gpu, cfg):
     r.forward()
     out = r.outputs()
     r.close()
-    _check(case, out, f"cfg{cfg}")
+    _check(case, out, case.spec.name)
 
 
-def test_full_size_cfg4_padded_and_varlen(torch_gpu):
+def test_full_size_h5120_padded_and_varlen(torch_gpu):
     from structured_decision_head_amd import clefhead as C
     from structured_decision_head_amd.runner import HeadRunner
-    say("case cfg4 full size (H=5120, B=32, NaN padding), padded and varlen")
+    say("case heterogeneous H=5120 full size (B=32, NaN padding), padded and varlen")
     case = synth.config_case(4)
     b = case.batch
     say(f"  B={b.B} L={b.L} T={int(b.lengths.sum())} NQ={b.NQ} NO={b.NO}")
@@ -63,4 +63,4 @@ def test_full_size_cfg4_padded_and_varlen(torch_gpu):
     r.close()
     for a, c in zip(out_p, out_v):
         assert np.array_equal(a, c)
-    _check(case, out_p, "cfg4")
+    _check(case, out_p, case.spec.name)

@@ -38,8 +38,8 @@ def mini_spec(**over):
     return synth.config_spec(1, **kw)
 
 
-def test_cfg0_parity_and_stages(torch_gpu):
-    say("case cfg0 (B=1, L=160, H=4096)")
+def test_single_record_parity_and_stages(torch_gpu):
+    say("case single record (B=1, L=160, H=4096)")
     case = synth.config_case(0)
     r, out = _run(case, trace=True)
     b = case.batch
@@ -78,7 +78,7 @@ def test_cfg0_parity_and_stages(torch_gpu):
         assert stages[k] < 1e-4, (k, stages[k])
     assert stages["memory"] < 1e-2
     r.close()
-    compare("cfg0", out, ref, b.o_offsets)
+    compare(case.spec.name, out, ref, b.o_offsets)
 
 
 def test_mini_ragged_parity(torch_gpu):
