@@ -122,6 +122,22 @@ typedef struct {
 CLEF_API int clef_head_create(const clef_head_config *cfg, const clef_head_weight *weights, int32_t num_weights,
                      const void *lexical_table, clef_head **out);
 
+/* A second head over the same weights (the JointSchemaHead of "clef-4bit ...
+ * JointSchemaHead" §三, same operation as clef_head_forward): it reads src's
+ * device weight blob and lexical table and has its own workspace and events,
+ * so a serving loop can keep several batches in flight, one per head, each on
+ * its own stream.  The heads also share the one internal stream on which a
+ * forward runs its work that does not wait for the big GEMMs, so n heads in
+ * flight need n + 1 streams (HIP gives a process 4 hardware queues by
+ * default), and they take turns for the big GEMMs: a forward's memory GEMM
+ * starts after the K/V GEMM of the group's previously issued forward, so one
+ * batch's GEMMs run beside the other batches' small-GEMM chains.  Results do
+ * not depend on this order.  The weight blob and that stream are released with the last head
+ * that uses them; src may be destroyed first.  The new head lives on src's
+ * device (the current device is left as it was).  Errors: CLEF_E_ARG for NULL
+ * src / out, CLEF_E_HIP when events cannot be created (nothing is leaked). */
+CLEF_API int clef_head_create_sharing(const clef_head *src, clef_head **out);
+
 /* Forward pass on hip_stream (a hipStream_t, or NULL for the default stream).
  * Outputs (DEVICE, caller-owned): logits fp32 [NO], probs fp32 [NO] (softmax
  * over each question's options), argmax int32 [NQ] (index of the first

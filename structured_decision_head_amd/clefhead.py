@@ -23,7 +23,7 @@ CLEF_PADDED, CLEF_VARLEN = 0, 1
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
 
-EXPORTS = ("clef_head_create", "clef_head_forward", "clef_head_destroy", "clef_head_last_error",
+EXPORTS = ("clef_head_create", "clef_head_create_sharing", "clef_head_forward", "clef_head_destroy", "clef_head_last_error",
            "clef_head_check_batch", "clef_head_span_rows", "clef_head_weight_count", "clef_head_weight_info",
            "clef_head_set_trace", "clef_head_trace", "clef_head_set_profiling", "clef_head_stage_times")
 STAGES = ("rowstats", "pool", "lexical", "memory_gemm", "kv_gemm", "query_proj", "route_dense", "route_attn",
@@ -71,6 +71,7 @@ def load() -> ctypes.CDLL:
     L.clef_head_create.argtypes = [ctypes.POINTER(clef_head_config), ctypes.POINTER(clef_head_weight), ctypes.c_int32,
                                    _P, ctypes.POINTER(_P)]
     L.clef_head_forward.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P, _P]
+    L.clef_head_create_sharing.argtypes = [_P, ctypes.POINTER(_P)]
     L.clef_head_destroy.argtypes = [_P]
     L.clef_head_destroy.restype = None
     L.clef_head_last_error.restype = ctypes.c_char_p
@@ -177,6 +178,13 @@ def clef_head_create(head, weights: Dict[str, np.ndarray], table_ptr: int) -> in
         arr[i].dtype = CLEF_BF16 if v.dtype == np.uint16 else CLEF_F32 if v.dtype == np.float32 else 0
     h = _P()
     _check(load().clef_head_create(ctypes.byref(cfg), arr, len(items), table_ptr, ctypes.byref(h)))
+    return h.value
+
+
+def clef_head_create_sharing(src: int) -> int:
+    """A second handle over src's device weights (own workspace and streams)."""
+    h = _P()
+    _check(load().clef_head_create_sharing(src, ctypes.byref(h)))
     return h.value
 
 

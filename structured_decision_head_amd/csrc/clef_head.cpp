@@ -20,7 +20,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <string>
+#include <type_traits>
 #include <unordered_map>
 #include <vector>
 
@@ -370,12 +373,26 @@ struct Weights {
 
 }  // namespace
 
+// What the heads made from one clef_head_create share besides the weights: the
+// side stream and the order of their big-GEMM phases.  A head waits for the
+// previous head's K/V GEMM before its memory GEMM starts and marks its own K/V
+// GEMM done, so with several batches in flight the (MFMA-bound) big GEMMs of
+// one batch run beside the (latency-bound) small-GEMM chains of the others
+// instead of all batches doing their GEMMs at once.
+struct HeadGroup {
+  std::mutex mu;
+  hipEvent_t gemm_done = nullptr;
+  bool recorded = false;
+  ~HeadGroup() {
+    if (gemm_done) (void)hipEventDestroy(gemm_done);
+  }
+};
+
 struct clef_head {
   clef_head_config cfg;
   int device = 0;
-  int num_cu = 256;                      // compute units of the device (one big-GEMM tile each)
   const bf16_t* table = nullptr;
-  void* dweights = nullptr;
+  std::shared_ptr<void> dweights;        // the weight blob, shared by heads made with clef_head_create_sharing
   Weights w;
   // workspace
   void* ws = nullptr;
@@ -383,9 +400,12 @@ struct clef_head {
   void* pinned = nullptr;
   size_t pinned_bytes = 0;
   hipEvent_t staged = nullptr;
-  hipStream_t side = nullptr;            // second stream for the work independent of the big GEMMs
-  hipStream_t third = nullptr;           // K/V of the first row tiles, beside the memory GEMM's last round
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_mem0 = nullptr, ev_kv0 = nullptr;
+  // second stream for the work independent of the big GEMMs; heads made with
+  // clef_head_create_sharing use their source's, so that several heads in
+  // flight take one extra hardware queue between them, not one each
+  std::shared_ptr<std::remove_pointer_t<hipStream_t>> side;
+  std::shared_ptr<HeadGroup> group;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool staged_pending = false;
   // trace
   bool trace = false;
@@ -594,7 +614,14 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     (void)hipFree(d);
     return fail(CLEF_E_HIP, "copying weights to the device failed");
   }
-  h->dweights = d;
+  const int dev = h->device;
+  h->dweights = std::shared_ptr<void>(d, [dev](void* q) {
+    int cur = dev;
+    (void)hipGetDevice(&cur);
+    if (cur != dev) (void)hipSetDevice(dev);
+    (void)hipFree(q);
+    if (cur != dev) (void)hipSetDevice(cur);
+  });
   for (auto& f : fix) *f.second = static_cast<const uint8_t*>(d) + f.first;
   return CLEF_OK;
 }
@@ -702,6 +729,32 @@ int clef_head_span_rows(const clef_head_config* cfg, const clef_head_batch* batc
   return CLEF_OK;
 }
 
+namespace {
+
+// Events of a handle and, unless it already has them, its side stream and
+// group; created on the current device.
+bool create_streams(clef_head* h) {
+  if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
+    return false;
+  if (!h->group) {
+    auto g = std::make_shared<HeadGroup>();
+    if (hipEventCreateWithFlags(&g->gemm_done, hipEventDisableTiming) != hipSuccess) return false;
+    h->group = g;
+  }
+  if (h->side) return true;
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return false;
+  h->side.reset(s, [](hipStream_t q) {
+    (void)hipStreamSynchronize(q);
+    (void)hipStreamDestroy(q);
+  });
+  return true;
+}
+
+}  // namespace
+
 int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weights, int32_t num_weights,
                      const void* lexical_table, clef_head** out) {
   if (!out) return fail(CLEF_E_ARG, "out is NULL");
@@ -712,9 +765,10 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
   clef_head* h = new clef_head();
   h->cfg = *cfg;
   h->table = static_cast<const bf16_t*>(lexical_table);
+  int num_cu = 0;
   if (hipGetDevice(&h->device) != hipSuccess ||
-      hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
-      h->num_cu <= 0) {
+      hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+      num_cu <= 0) {
     delete h;
     return fail(CLEF_E_HIP, "no HIP device");
   }
@@ -723,13 +777,7 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
     delete h;
     return rc;
   }
-  if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_mem0, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_kv0, hipEventDisableTiming) != hipSuccess ||
-      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      hipStreamCreateWithFlags(&h->third, hipStreamNonBlocking) != hipSuccess) {
+  if (!create_streams(h)) {
     clef_head_destroy(h);
     return fail(CLEF_E_HIP, "creating events / the side stream failed");
   }
@@ -737,21 +785,37 @@ int clef_head_create(const clef_head_config* cfg, const clef_head_weight* weight
   return CLEF_OK;
 }
 
+int clef_head_create_sharing(const clef_head* src, clef_head** out) {
+  if (!out) return fail(CLEF_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!src || !src->dweights) return fail(CLEF_E_ARG, "source handle is NULL");
+  int dev_prev = src->device;
+  if (hipGetDevice(&dev_prev) != hipSuccess) return fail(CLEF_E_HIP, "no HIP device");
+  if (dev_prev != src->device && hipSetDevice(src->device) != hipSuccess)
+    return fail(CLEF_E_HIP, "cannot select the source handle's device");
+  clef_head* h = new clef_head();
+  h->cfg = src->cfg;
+  h->device = src->device;
+  h->table = src->table;
+  h->w = src->w;
+  h->dweights = src->dweights;
+  h->side = src->side;
+  h->group = src->group;
+  const bool ok = create_streams(h);
+  if (!ok) clef_head_destroy(h);
+  if (dev_prev != src->device) (void)hipSetDevice(dev_prev);
+  if (!ok) return fail(CLEF_E_HIP, "creating events / the side stream failed");
+  *out = h;
+  return CLEF_OK;
+}
+
 void clef_head_destroy(clef_head* h) {
   if (!h) return;
   for (auto e : h->ev) (void)hipEventDestroy(e);
-  if (h->side) {
-    (void)hipStreamSynchronize(h->side);
-    (void)hipStreamDestroy(h->side);
-  }
-  if (h->third) {
-    (void)hipStreamSynchronize(h->third);
-    (void)hipStreamDestroy(h->third);
-  }
+  if (h->side) (void)hipStreamSynchronize(h->side.get());   // this head's side work; the stream goes with its last user
+  h->side.reset();
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
-  if (h->ev_mem0) (void)hipEventDestroy(h->ev_mem0);
-  if (h->ev_kv0) (void)hipEventDestroy(h->ev_kv0);
   if (h->staged) {
     if (h->staged_pending) (void)hipEventSynchronize(h->staged);
     (void)hipEventDestroy(h->staged);
@@ -759,7 +823,7 @@ void clef_head_destroy(clef_head* h) {
   if (h->ws) (void)hipFree(h->ws);
   if (h->tr) (void)hipFree(h->tr);
   if (h->pinned) (void)hipHostFree(h->pinned);
-  if (h->dweights) (void)hipFree(h->dweights);
+  h->dweights.reset();
   delete h;
 }
 
@@ -943,7 +1007,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   // statistics and joined before the first routing attention, so its small
   // kernels fill the CUs the big GEMMs leave idle.  Stage timing runs serially.
   const bool fork = !h->prof;
-  hipStream_t s2 = fork ? h->side : st;
+  hipStream_t s2 = fork ? h->side.get() : st;
 
   // step 1: row statistics, pooled vectors, lexical vectors and prior
   launch_rowstats_bf16(st, X, (int)H, tiles, p.ntiles, stats, eps);
@@ -958,27 +1022,23 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   MARK(CLEF_STAGE_LEXICAL);
 
   if (joint) {
-    // step 2: memory and K/V of every routing layer (main stream)
-    // The memory GEMM runs 4 workgroups per row tile, one per CU.  When its
-    // last round is partial, it is launched in two parts: the K/V GEMM of the
-    // first part's rows starts on a third stream as soon as that part is done
-    // and fills the CUs the second part leaves idle.
-    const int full = (p.ntiles * 4 / h->num_cu) * h->num_cu / 4;   // row tiles filling whole rounds
-    const int first = (fork && full > 0 && full < p.ntiles) ? full : 0;
-    if (NR > 0 && first > 0) {
-      launch_gemm_mem(st, X, (int)H, tiles, first, W.Wmem, stats, W.cmem, W.dmem, mem);
-      HIPCHK(hipEventRecord(h->ev_mem0, st));
-      launch_gemm_mem(st, X, (int)H, tiles + first, p.ntiles - first, W.Wmem, stats, W.cmem, W.dmem, mem);
-      HIPCHK(hipStreamWaitEvent(h->third, h->ev_mem0, 0));
-      launch_gemm_kv(h->third, mem, kvtiles, first, W.Wkv, W.bkv, NR, kv, p.Tpad);
-      HIPCHK(hipEventRecord(h->ev_kv0, h->third));
-      launch_gemm_kv(st, mem, kvtiles + first, p.ntiles - first, W.Wkv, W.bkv, NR, kv, p.Tpad);
-      HIPCHK(hipStreamWaitEvent(st, h->ev_kv0, 0));
-    } else if (NR > 0) {
+    // step 2: memory and K/V of every routing layer (main stream), after the
+    // big GEMMs of the group's previous forward
+    if (NR > 0) {
+      HeadGroup& g = *h->group;
+      if (fork) {
+        std::lock_guard<std::mutex> lk(g.mu);
+        if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
+      }
       launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
       MARK(CLEF_STAGE_MEMORY_GEMM);
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
       MARK(CLEF_STAGE_KV_GEMM);
+      if (fork) {
+        std::lock_guard<std::mutex> lk(g.mu);
+        HIPCHK(hipEventRecord(g.gemm_done, st));
+        g.recorded = true;
+      }
     }
     // step 3: option queries (with the first routing LayerNorm statistics), question base and global projections
     launch_sgemm(s2, LdRows{pooled, (int)H, nullptr}, EpSplit2{qv, qo, W.bqq}, W.Wqq, NQ, 2 * D, (int)H, part);

@@ -19,14 +19,22 @@ def to_device_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 class HeadRunner:
-    def __init__(self, case, table: Optional[torch.Tensor] = None, device="cuda"):
+    """share: another HeadRunner whose device weights and lexical table this
+    one reuses (clef_head_create_sharing); it gets its own workspace."""
+
+    def __init__(self, case, table: Optional[torch.Tensor] = None, device="cuda",
+                 share: Optional["HeadRunner"] = None):
         if not torch.cuda.is_available():
             raise RuntimeError("HeadRunner needs a HIP device")
         C.load()
         self.case = case
         self.device = device
-        self.table = table if table is not None else to_device_bf16(case.table, device)
-        self.handle = C.clef_head_create(case.head, case.weights, self.table.data_ptr())
+        if share is not None:
+            self.table = share.table
+            self.handle = C.clef_head_create_sharing(share.handle)
+        else:
+            self.table = table if table is not None else to_device_bf16(case.table, device)
+            self.handle = C.clef_head_create(case.head, case.weights, self.table.data_ptr())
         self.hidden = None
         self.args = None
 

@@ -163,3 +163,9 @@ def test_create_without_gpu_or_with_bad_weights_fails_cleanly():
         C.clef_head_create(head, w, 0x1000)
     # missing weight (or no device here): either way an error code, never a crash
     assert e.value.code in (C.CLEF_E_ARG, C.CLEF_E_HIP)
+
+
+def test_create_sharing_rejects_null_source():
+    with pytest.raises(C.ClefError) as e:
+        C.clef_head_create_sharing(0)
+    assert e.value.code == C.CLEF_E_ARG
