@@ -173,8 +173,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }  // namespace
 
 // The widest tile (128, 64 or 32 columns) whose grid, split along K towards
-// 512 workgroups (at most kMaxSplit slices of 128-deep chunks), still has at
-// least 256 workgroups.
+// 256 workgroups (at most kMaxSplit slices of 128-deep chunks), still has at
+// least 128 workgroups.  Fewer, longer workgroups hold the CUs for less time
+// in total, which matters most when another batch's kernels share the chip.
 SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
   SgemmShape s{};
   s.mtiles = (M + SBM - 1) / SBM;
@@ -184,7 +185,7 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
     s.wr = wr;
     s.ntiles = N / sbn;
     const int tiles = s.mtiles * s.ntiles;
-    int split = (512 + tiles - 1) / tiles;
+    int split = (256 + tiles - 1) / tiles;
     if (split > kMaxSplit) split = kMaxSplit;
     if (split > kblocks) split = kblocks;
     if (split < 1) split = 1;
@@ -192,7 +193,7 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
     const int per = (kblocks + split - 1) / split;
     s.kchunk = per * SKC;
     s.nsplit = (kblocks + per - 1) / per;
-    if (tiles * s.nsplit >= 256 || wr == 4 || (N / (sbn / 2)) * (sbn / 2) != N) break;
+    if (tiles * s.nsplit >= 128 || wr == 4 || (N / (sbn / 2)) * (sbn / 2) != N) break;
   }
   s.part_floats = s.nsplit > 1 ? (size_t)s.nsplit * s.mtiles * SBM * N : 0;
   return s;
