@@ -671,7 +671,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   const int pshapes[][3] = {{p.NQ, 3 * D, D}, {p.NO, D, 4 * D}};
   for (auto& s : pshapes) {
     if (s[0] == 0) continue;
-    const SgemmShape g = sgemm_shape(s[0], s[1], s[2], false);
+    const SgemmShape g = sgemm_shape(s[0], s[1], s[2], false, true);
     part = std::max(part, (size_t)g.nsplit * g.mtiles * kSgemmRows * s[1]);
   }
   L.part = take(part * 4);

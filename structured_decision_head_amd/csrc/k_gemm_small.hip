@@ -176,7 +176,10 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // 256 workgroups (at most kMaxSplit slices of 128-deep chunks), still has at
 // least 128 workgroups.  Fewer, longer workgroups hold the CUs for less time
 // in total, which matters most when another batch's kernels share the chip.
-SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
+// When the consumer sums the slices itself (no reduction pass) the split goes
+// towards 512 workgroups with at least 256.
+SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce, bool consumer_sums) {
+  const int target = consumer_sums ? 512 : 256, least = consumer_sums ? 256 : 128;
   SgemmShape s{};
   s.mtiles = (M + SBM - 1) / SBM;
   const int kblocks = K / SKC;
@@ -185,7 +188,7 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
     s.wr = wr;
     s.ntiles = N / sbn;
     const int tiles = s.mtiles * s.ntiles;
-    int split = (256 + tiles - 1) / tiles;
+    int split = (target + tiles - 1) / tiles;
     if (split > kMaxSplit) split = kMaxSplit;
     if (split > kblocks) split = kblocks;
     if (split < 1) split = 1;
@@ -193,7 +196,7 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce) {
     const int per = (kblocks + split - 1) / split;
     s.kchunk = per * SKC;
     s.nsplit = (kblocks + per - 1) / per;
-    if (tiles * s.nsplit >= 128 || wr == 4 || (N / (sbn / 2)) * (sbn / 2) != N) break;
+    if (tiles * s.nsplit >= least || wr == 4 || (N / (sbn / 2)) * (sbn / 2) != N) break;
   }
   s.part_floats = s.nsplit > 1 ? (size_t)s.nsplit * s.mtiles * SBM * N : 0;
   return s;
@@ -229,7 +232,7 @@ void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W,
 
 template <class Ld>
 SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, int M, int N, int K, float* part) {
-  const SgemmShape s = sgemm_shape(M, N, K, false);
+  const SgemmShape s = sgemm_shape(M, N, K, false, true);
   if (M == 0) return s;
   launch_tile(s, st, ld, EpPart{part, N}, W, M, N, K, part);
   return s;

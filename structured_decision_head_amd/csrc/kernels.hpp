@@ -198,8 +198,9 @@ struct SgemmShape {
   int wr;                 // waves along rows: tile width 128 / wr columns
   size_t part_floats;
 };
-// need_reduce: always split K (>= 2 slices) so that a reduction pass runs
-SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce = false);
+// need_reduce: always split K (>= 2 slices) so that a reduction pass runs;
+// consumer_sums: the slices are summed by the consuming kernel (no reduction pass)
+SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce = false, bool consumer_sums = false);
 
 // stats != nullptr (N must be 1024): the reduction pass also writes the
 // LayerNorm statistics (mean, 1/sqrt(var + eps)) of every finished output row.
