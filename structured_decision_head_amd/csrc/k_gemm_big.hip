@@ -99,8 +99,7 @@ struct EpiKV {
   bf16_t* kv;          // layer r: K at kv + (2r) * 16 * Tpad * 64, V at kv + (2r+1) * 16 * Tpad * 64
   long long Tpad;
   static constexpr bool kHasPlain = true;
-  static constexpr int kLdK = 72;                      // K image row pitch (bf16): 128 B + 16 B
-  static constexpr int kImageBytes = 4 * 256 * kLdK * 2;
+  static constexpr int kImageBytes = 4 * 256 * 64 * 2;
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV bf16_t* head_base(int col) const {
     const int r = col >> 11, isv = (col >> 10) & 1, h = (col >> 6) & 15;
@@ -108,7 +107,10 @@ struct EpiKV {
   }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
   DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
-  // K (transposed): image [head][row][kLdK]
+  // K (transposed): image [head][row][64] in 128-byte rows, 16-byte chunk c of
+  // row r at position c ^ (r & 7): the 8-byte writes of 32 consecutive rows and
+  // the 16-byte reads of 8 consecutive rows both spread evenly over the banks
+  DEV static int kpos(int row, int col) { return row * 64 + ((((col >> 3) ^ row) & 7) << 3) + (col & 7); }
   DEV void stage_t(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
     const int h4 = 4 * (lane >> 5);
 #pragma unroll
@@ -117,19 +119,20 @@ struct EpiKV {
       for (int g = 0; g < 4; ++g) {
         const int lc = lc0 + mi * 32 + 8 * g + h4;
         const float4 b = *reinterpret_cast<const float4*>(cst + lc);
-        bf16_t* base = img + (lc >> 6) * (256 * kLdK) + (lc & 63);
+        bf16_t* base = img + (lc >> 6) * (256 * 64);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const f32x16& a = acc[mi][ni];
           uint2 v;
           v.x = pack_bf16x2(a[4 * g] + b.x, a[4 * g + 1] + b.y);
           v.y = pack_bf16x2(a[4 * g + 2] + b.z, a[4 * g + 3] + b.w);
-          *reinterpret_cast<uint2*>(base + (lr0 + ni * 32 + (lane & 31)) * kLdK) = v;
+          *reinterpret_cast<uint2*>(base + kpos(lr0 + ni * 32 + (lane & 31), lc & 63)) = v;
         }
       }
   }
   // V (plain): image [head][row block][64][32] in memory order; 16-byte chunk c
-  // of a 64-byte feature row f sits at c ^ (f & 3) to spread LDS banks
+  // of a 64-byte feature row f sits at c ^ ((f >> 2) & 3), so 16 consecutive
+  // feature rows cover all 16 bank groups
   DEV void stage(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
     const int hh = lane >> 5;
 #pragma unroll
@@ -150,7 +153,7 @@ struct EpiKV {
           v.y = pack_bf16x2(a[e + 2] + b, a[e + 3] + b);
           v.z = pack_bf16x2(a[e + 4] + b, a[e + 5] + b);
           v.w = pack_bf16x2(a[e + 6] + b, a[e + 7] + b);
-          *reinterpret_cast<uint4*>(blk + 8 * ((2 * q + hh) ^ (f & 3))) = v;
+          *reinterpret_cast<uint4*>(blk + 8 * ((2 * q + hh) ^ ((f >> 2) & 3))) = v;
         }
       }
     }
@@ -162,7 +165,7 @@ struct EpiKV {
         const int hh = i >> 11, r = (i >> 3) & 255, ch = i & 7;
         bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)orow0 * 64;
         *reinterpret_cast<uint4*>(dst + r * 64 + ch * 8) =
-            *reinterpret_cast<const uint4*>(img + (hh * 256 + r) * kLdK + ch * 8);
+            *reinterpret_cast<const uint4*>(img + hh * (256 * 64) + kpos(r, ch * 8));
       }
     } else {
 #pragma unroll 8
@@ -170,7 +173,7 @@ struct EpiKV {
         const int hh = i >> 11, j = i & 2047, f = (j >> 2) & 63, c = j & 3;
         bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)(orow0 >> 5) * 2048;
         *reinterpret_cast<uint4*>(dst + j * 8) =
-            *reinterpret_cast<const uint4*>(img + hh * 16384 + (j >> 2) * 32 + 8 * (c ^ (f & 3)));
+            *reinterpret_cast<const uint4*>(img + hh * 16384 + (j >> 2) * 32 + 8 * (c ^ ((f >> 2) & 3)));
       }
     }
   }
