@@ -1,5 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (padded layout, one clef_head_forward over the whole batch).
+benchmark times (padded layout, one clef_head_forward over the whole batch;
+for the online-serving batch also two heads sharing weights with batches in
+flight on two streams, as the benchmark runs them).
 
 Records are independent, so the fp64 oracle checks the batch record by
 record (every record with questions).  Config 4 is also run as a varlen batch
@@ -64,3 +66,30 @@ def test_full_size_h5120_padded_and_varlen(torch_gpu):
     for a, c in zip(out_p, out_v):
         assert np.array_equal(a, c)
     _check(case, out_p, case.spec.name)
+
+
+def test_full_size_two_in_flight(torch_gpu):
+    """Two heads over one weight blob, forwards alternating on two streams
+    (the benchmark's timed loop): every head returns exactly what one head
+    returns alone, and two records are checked against the oracle."""
+    from structured_decision_head_amd.runner import HeadRunner
+    case = synth.config_case(1)
+    say(f"case {case.spec.name} full size, two batches in flight")
+    r1 = HeadRunner(case)
+    r1.set_batch()
+    r1.forward()
+    ref = r1.outputs()
+    r2 = HeadRunner(case, share=r1)
+    r2.set_batch()
+    streams = [torch_gpu.cuda.Stream(), torch_gpu.cuda.Stream()]
+    for i in range(8):
+        (r1, r2)[i % 2].forward(streams[i % 2])
+    torch_gpu.cuda.synchronize()
+    for r in (r1, r2):
+        assert all(np.array_equal(a, b) for a, b in zip(r.outputs(), ref))
+    b = case.batch
+    recs = [0, b.B - 1]
+    compare("two in flight (records 0 and last)", select(b, recs, *r2.outputs()),
+            oracle_outputs(case, records=recs), local_offsets(b, recs))
+    r2.close()
+    r1.close()
