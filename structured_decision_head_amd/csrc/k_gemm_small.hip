@@ -54,9 +54,11 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
   // the current chunk's MFMAs, so each workgroup pays one memory round trip
   // per launch instead of one per chunk.
   typename Ld::Raw ra[4];
+  typename Ld::Cst cq;                   // per-column constants of this thread's 8 columns
   uint4 bq[2][4];
 #define SG_FETCH(K0)                                                                     \
   {                                                                                      \
+    cq = ld.cst((K0) + (tid & 15) * 8);                                                  \
     _Pragma("unroll") for (int cb = 0; cb < 2; ++cb)                                     \
       _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                   \
         bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (K0) + kk * 32);           \
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
       const int r = v >> 4, c = v & 15;
       float x[8];
       if (m0 + r < M) {
-        ld.finish(ra[i], m0 + r, k0 + c * 8, x);
+        ld.finish(ra[i], cq, m0 + r, k0 + c * 8, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;

@@ -35,9 +35,11 @@ void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntile
 // small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue
 // ---------------------------------------------------------------------------
 // A loaders: fetch() issues the global loads of 8 consecutive A elements
-// (row m, columns k..k+7) into a Raw value; finish() turns them into floats.
-// Splitting the two lets the GEMM keep the next chunk's loads in flight while
-// it multiplies the current one.
+// (row m, columns k..k+7) into a Raw value; cst() issues the loads of any
+// per-column constants of those 8 columns (the same for every row a thread
+// handles); finish() turns them into floats.  Splitting the steps lets the
+// GEMM keep the next chunk's loads in flight while it multiplies the current
+// one, with no load left to wait for in finish().
 DEV void f4x2(float4 a, float4 b, float* x) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -47,11 +49,13 @@ struct LdRows {          // A[m] = src[rows ? rows[m] : m]
   int ld;
   const int* rows;
   struct Raw { float4 a, b; };
+  struct Cst {};
   DEV Raw fetch(int m, int k) const {
     const float* p = src + (size_t)(rows ? rows[m] : m) * ld + k;
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
-  DEV void finish(const Raw& r, int, int, float* x) const { f4x2(r.a, r.b, x); }
+  DEV Cst cst(int) const { return {}; }
+  DEV void finish(const Raw& r, const Cst&, int, int, float* x) const { f4x2(r.a, r.b, x); }
 };
 
 struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
@@ -61,15 +65,22 @@ struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
   const float* g;
   const float* b;
   struct Raw { float4 a, c; float2 s; };
+  struct Cst { float4 g0, g1, b0, b1; };   // gamma and beta of the 8 columns
   DEV Raw fetch(int m, int k) const {
     const float* p = src + (size_t)m * ld + k;
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4), stats[m]};
   }
-  DEV void finish(const Raw& r, int, int k, float* x) const {
-    float v[8];
+  DEV Cst cst(int k) const {
+    return Cst{*reinterpret_cast<const float4*>(g + k), *reinterpret_cast<const float4*>(g + k + 4),
+               *reinterpret_cast<const float4*>(b + k), *reinterpret_cast<const float4*>(b + k + 4)};
+  }
+  DEV void finish(const Raw& r, const Cst& c, int, int, float* x) const {
+    float v[8], gg[8], bb[8];
     f4x2(r.a, r.c, v);
+    f4x2(c.g0, c.g1, gg);
+    f4x2(c.b0, c.b1, bb);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (v[i] - r.s.x) * r.s.y * g[k + i] + b[k + i];
+    for (int i = 0; i < 8; ++i) x[i] = (v[i] - r.s.x) * r.s.y * gg[i] + bb[i];
   }
 };
 
@@ -78,11 +89,13 @@ struct LdSeg2 {          // A[m] = [p0[m] | p1[m]], each H wide
   const float* p1;
   int H;
   struct Raw { float4 a, b; };
+  struct Cst {};
   DEV Raw fetch(int m, int k) const {
     const float* p = k < H ? p0 + (size_t)m * H + k : p1 + (size_t)m * H + (k - H);
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
-  DEV void finish(const Raw& r, int, int, float* x) const { f4x2(r.a, r.b, x); }
+  DEV Cst cst(int) const { return {}; }
+  DEV void finish(const Raw& r, const Cst&, int, int, float* x) const { f4x2(r.a, r.b, x); }
 };
 
 struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m], each 1024 wide
@@ -90,6 +103,8 @@ struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m]
   const float* U;
   const int* fq;
   struct Raw { float4 f0, f1, u0, u1; };
+  struct Cst {};
+  DEV Cst cst(int) const { return {}; }
   DEV Raw fetch(int m, int k) const {
     const int c = k & 1023;
     const float* fp = F + (size_t)fq[m] * 1024 + c;
@@ -97,7 +112,7 @@ struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m]
     return Raw{*reinterpret_cast<const float4*>(fp), *reinterpret_cast<const float4*>(fp + 4),
                *reinterpret_cast<const float4*>(up), *reinterpret_cast<const float4*>(up + 4)};
   }
-  DEV void finish(const Raw& r, int, int k, float* x) const {
+  DEV void finish(const Raw& r, const Cst&, int, int k, float* x) const {
     const int seg = k >> 10;
     float f[8], u[8];
     f4x2(r.f0, r.f1, f);
