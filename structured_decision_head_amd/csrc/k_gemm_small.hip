@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (stats == nullptr && i >= (size_t)M * N) return;
   const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
-  // all slices in flight at once, summed in slice order
+  // the epilogue's own loads and all slices in flight at once, summed in slice order
+  const typename Epi::Pre pre = epi.pre4(m, n);
   float4 t[kMaxSplit];
 #pragma unroll
   for (int q = 0; q < kMaxSplit; ++q)
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 #pragma unroll
   for (int q = 1; q < kMaxSplit; ++q)
     if (q < nsplit) { s.x += t[q].x; s.y += t[q].y; s.z += t[q].z; s.w += t[q].w; }
-  const float a = epi(m, n, s.x), b = epi(m, n + 1, s.y), c = epi(m, n + 2, s.z), d = epi(m, n + 3, s.w);
+  const float4 o = epi.apply4(m, n, s, pre);
+  const float a = o.x, b = o.y, c = o.z, d = o.w;
   if (stats != nullptr) {
     const float mu = block_sum<4>((a + b) + (c + d), sm) * (1.0f / 1024);
     const float va = block_sum<4>((a - mu) * (a - mu) + (b - mu) * (b - mu) + (c - mu) * (c - mu) + (d - mu) * (d - mu),

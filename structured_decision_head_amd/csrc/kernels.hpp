@@ -123,7 +123,14 @@ struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m]
   }
 };
 
-// Epilogues store one output and return the stored value.
+// Epilogues store one output and return the stored value.  The reduction pass
+// uses the 4-wide form: pre4() issues the loads an epilogue needs for 4
+// consecutive outputs (bias, residual, gathered row) next to the slice loads,
+// apply4() finishes them with one 16-byte store.
+DEV float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+DEV float4 add_f4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+DEV void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+
 struct EpStore {         // C = acc + bias
   float* C;
   int ldc;
@@ -131,6 +138,13 @@ struct EpStore {         // C = acc + bias
   DEV float operator()(int m, int n, float v) const {
     const float r = v + bias[n];
     C[(size_t)m * ldc + n] = r;
+    return r;
+  }
+  struct Pre { float4 b; };
+  DEV Pre pre4(int, int n) const { return Pre{ld_f4(bias + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {
+    const float4 r = add_f4(v, p.b);
+    st_f4(C + (size_t)m * ldc + n, r);
     return r;
   }
 };
@@ -142,6 +156,14 @@ struct EpGelu {          // C = GELU(acc + bias)
   DEV float operator()(int m, int n, float v) const {
     const float r = gelu_erf(v + bias[n]);
     C[(size_t)m * ldc + n] = r;
+    return r;
+  }
+  struct Pre { float4 b; };
+  DEV Pre pre4(int, int n) const { return Pre{ld_f4(bias + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {
+    const float4 r = make_float4(gelu_erf(v.x + p.b.x), gelu_erf(v.y + p.b.y), gelu_erf(v.z + p.b.z),
+                                 gelu_erf(v.w + p.b.w));
+    st_f4(C + (size_t)m * ldc + n, r);
     return r;
   }
 };
@@ -156,6 +178,14 @@ struct EpAddRow {        // C = acc + bias + add[idx[m]] (a per-row gathered ter
     C[(size_t)m * 1024 + n] = r;
     return r;
   }
+  struct Pre { float4 b, a; };
+  DEV Pre pre4(int m, int n) const { return Pre{ld_f4(bias + n), ld_f4(add + (size_t)idx[m] * 1024 + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {
+    const float4 r = make_float4(v.x + p.b.x + p.a.x, v.y + p.b.y + p.a.y, v.z + p.b.z + p.a.z,
+                                 v.w + p.b.w + p.a.w);
+    st_f4(C + (size_t)m * 1024 + n, r);
+    return r;
+  }
 };
 
 struct EpSplit2 {        // columns [0, 1024) -> C0, [1024, 2048) -> C1, plus bias
@@ -165,6 +195,13 @@ struct EpSplit2 {        // columns [0, 1024) -> C0, [1024, 2048) -> C1, plus bi
   DEV float operator()(int m, int n, float v) const {
     const float r = v + bias[n];
     if (n < 1024) C0[(size_t)m * 1024 + n] = r; else C1[(size_t)m * 1024 + (n - 1024)] = r;
+    return r;
+  }
+  struct Pre { float4 b; };
+  DEV Pre pre4(int, int n) const { return Pre{ld_f4(bias + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {   // the 4 columns never straddle 1024
+    const float4 r = add_f4(v, p.b);
+    st_f4(n < 1024 ? C0 + (size_t)m * 1024 + n : C1 + (size_t)m * 1024 + (n - 1024), r);
     return r;
   }
 };
@@ -177,6 +214,14 @@ struct EpResid {         // C += acc + bias (residual stream)
     float* p = C + (size_t)m * ldc + n;
     const float r = *p + (v + bias[n]);
     *p = r;
+    return r;
+  }
+  struct Pre { float4 b, c; };
+  DEV Pre pre4(int m, int n) const { return Pre{ld_f4(bias + n), ld_f4(C + (size_t)m * ldc + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {
+    const float4 r = make_float4(p.c.x + (v.x + p.b.x), p.c.y + (v.y + p.b.y), p.c.z + (v.z + p.b.z),
+                                 p.c.w + (v.w + p.b.w));
+    st_f4(C + (size_t)m * ldc + n, r);
     return r;
   }
 };
