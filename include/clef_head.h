@@ -147,6 +147,38 @@ CLEF_API int clef_head_create_sharing(const clef_head *src, clef_head **out);
 CLEF_API int clef_head_forward(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
                       int32_t *argmax, void *hip_stream);
 
+/* Answer outputs of clef_head_forward_answers (CoreML conversion metadata page
+ * of clef-flash, "decision.response" and "decision.option_order").  Every
+ * member is a caller-owned DEVICE fp32 buffer or NULL (then not written):
+ *   value          [NQ]  noul: probability of "true" (option 0, the order
+ *                        [true, false]); choice: probability of the argmax
+ *                        option (the answer itself is argmax[q]); score: the
+ *                        probability-weighted mean level, levels 0..n-1
+ *   confidence     [NQ]  largest probability of the question (for noul the
+ *                        response omits it)
+ *   value_4dp, confidence_4dp [NQ], probs_4dp [NO]
+ *                        the same numbers and every probability rounded half
+ *                        to even at the 4th decimal ("4 decimals"): the fp32
+ *                        nearest to k / 10^4, k = the integer nearest to
+ *                        x * 10^4 with ties to even, x the fp32 unrounded value.
+ * usage.input_tokens of a record is its valid length n_b and output_tokens is
+ * 0 (no decoding): both are known to the caller and not written here. */
+typedef struct {
+  float *value;
+  float *confidence;
+  float *value_4dp;
+  float *confidence_4dp;
+  float *probs_4dp;
+} clef_head_answers;
+
+/* clef_head_forward plus the answer mapping above, computed in the scoring
+ * kernel from the same fp32 probabilities (logits, probs and argmax are
+ * bit-identical to clef_head_forward's).  answers must not be NULL
+ * (CLEF_E_ARG); otherwise arguments, errors and ownership are those of
+ * clef_head_forward. */
+CLEF_API int clef_head_forward_answers(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
+                                       int32_t *argmax, const clef_head_answers *answers, void *hip_stream);
+
 /* Release everything the handle owns.  NULL is ignored. */
 CLEF_API void clef_head_destroy(clef_head *h);
 

@@ -23,7 +23,8 @@ CLEF_PADDED, CLEF_VARLEN = 0, 1
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
 
-EXPORTS = ("clef_head_create", "clef_head_create_sharing", "clef_head_forward", "clef_head_destroy", "clef_head_last_error",
+EXPORTS = ("clef_head_create", "clef_head_create_sharing", "clef_head_forward", "clef_head_forward_answers",
+           "clef_head_destroy", "clef_head_last_error",
            "clef_head_check_batch", "clef_head_span_rows", "clef_head_weight_count", "clef_head_weight_info",
            "clef_head_set_trace", "clef_head_trace", "clef_head_set_profiling", "clef_head_stage_times")
 STAGES = ("rowstats", "pool", "lexical", "memory_gemm", "kv_gemm", "query_proj", "route_dense", "route_attn",
@@ -57,6 +58,12 @@ class clef_head_batch(ctypes.Structure):
                 ("o_offsets", _P), ("o_span", _P), ("o_ids", _P)]
 
 
+class clef_head_answers(ctypes.Structure):
+    """Device fp32 buffers (addresses, 0 = not written): value, confidence [NQ];
+    their 4-decimal copies [NQ]; 4-decimal probabilities [NO]."""
+    _fields_ = [("value", _P), ("confidence", _P), ("value_4dp", _P), ("confidence_4dp", _P), ("probs_4dp", _P)]
+
+
 _lib = None
 
 
@@ -71,6 +78,8 @@ def load() -> ctypes.CDLL:
     L.clef_head_create.argtypes = [ctypes.POINTER(clef_head_config), ctypes.POINTER(clef_head_weight), ctypes.c_int32,
                                    _P, ctypes.POINTER(_P)]
     L.clef_head_forward.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P, _P]
+    L.clef_head_forward_answers.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P,
+                                            ctypes.POINTER(clef_head_answers), _P]
     L.clef_head_create_sharing.argtypes = [_P, ctypes.POINTER(_P)]
     L.clef_head_destroy.argtypes = [_P]
     L.clef_head_destroy.restype = None
@@ -192,6 +201,15 @@ def clef_head_forward(handle: int, batch_args: BatchArgs, logits_ptr: int, probs
                       stream_ptr: int = 0):
     _check(load().clef_head_forward(handle, ctypes.byref(batch_args.struct), logits_ptr, probs_ptr, argmax_ptr,
                                     stream_ptr or None))
+
+
+def clef_head_forward_answers(handle: int, batch_args: BatchArgs, logits_ptr: int, probs_ptr: int, argmax_ptr: int,
+                              value_ptr: int = 0, confidence_ptr: int = 0, value_4dp_ptr: int = 0,
+                              confidence_4dp_ptr: int = 0, probs_4dp_ptr: int = 0, stream_ptr: int = 0):
+    ans = clef_head_answers(value_ptr or None, confidence_ptr or None, value_4dp_ptr or None,
+                            confidence_4dp_ptr or None, probs_4dp_ptr or None)
+    _check(load().clef_head_forward_answers(handle, ctypes.byref(batch_args.struct), logits_ptr, probs_ptr,
+                                            argmax_ptr, ctypes.byref(ans), stream_ptr or None))
 
 
 def clef_head_destroy(handle: int):

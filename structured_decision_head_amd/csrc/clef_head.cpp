@@ -875,8 +875,8 @@ int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) 
   return CLEF_OK;
 }
 
-int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
-                      void* hip_stream) {
+static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
+                        const clef_head_answers* answers, void* hip_stream) {
   if (!h) return fail(CLEF_E_ARG, "handle is NULL");
   const clef_head_config& c = h->cfg;
   Plan p;
@@ -956,6 +956,9 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   const int* optrec = dtab + p.off_optrec;
   const int* qrec = dtab + p.off_qrec;
   const int* qtype = dtab + p.off_qtype;
+  const AnswerOut ans = answers ? AnswerOut{answers->value, answers->confidence, answers->value_4dp,
+                                            answers->confidence_4dp, answers->probs_4dp}
+                                : AnswerOut{nullptr, nullptr, nullptr, nullptr, nullptr};
   const int* ooff = dtab + p.off_ooff;
   const int4* items = reinterpret_cast<const int4*>(dtab + p.off_items);
 
@@ -1100,7 +1103,7 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
   }
   launch_score(st, u, f, part, gs.nsplit, (size_t)gs.mtiles * kSgemmRows * D, W.bs1, W.ws2, W.bs2, prior, W.gate,
                W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
-               h->trace && joint ? h->tr_jcos : nullptr, h->trace && joint ? h->tr_mlp : nullptr);
+               h->trace && joint ? h->tr_jcos : nullptr, h->trace && joint ? h->tr_mlp : nullptr, qtype, ans);
   MARK(CLEF_STAGE_SCORE);
 #undef MARK
   HIPCHK(hipGetLastError());
@@ -1127,6 +1130,17 @@ int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits,
     h->tr_u = h->tr_f0 = h->tr_f = h->tr_jcos = h->tr_mlp = nullptr;
   }
   return CLEF_OK;
+}
+
+int clef_head_forward(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
+                      void* hip_stream) {
+  return forward_impl(h, batch, logits, probs, argmax, nullptr, hip_stream);
+}
+
+int clef_head_forward_answers(clef_head* h, const clef_head_batch* batch, float* logits, float* probs,
+                              int32_t* argmax, const clef_head_answers* answers, void* hip_stream) {
+  if (!answers) return fail(CLEF_E_ARG, "answers is NULL");
+  return forward_impl(h, batch, logits, probs, argmax, answers, hip_stream);
 }
 
 }  // extern "C"

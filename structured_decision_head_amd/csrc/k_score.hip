@@ -8,7 +8,10 @@
 // Logit (clef-4bit page §三 step 4; architecture page §3.2): prior +
 // sigmoid(gate) * (joint_scale * cos(u_k, f_q) + MLP(k)); then a softmax over
 // each question's options (CoreML metadata page, "softmax": fp32, T = 1) and
-// the index of the first maximal logit.
+// the index of the first maximal logit.  Optionally the kernel also maps each
+// question's softmax to its answer (metadata page "decision.response"): the
+// value and confidence per question and 4-decimal copies of them and of every
+// probability.
 #include "kernels.hpp"
 
 namespace clef {
@@ -16,6 +19,15 @@ namespace clef {
 namespace {
 DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 DEV float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+// Round half to even at the fourth decimal (the response's "4 decimals").  For an
+// fp32 x the product x * 10^4 is exact in double (24 + 10 significant bits), rint
+// breaks ties to even, and k / 10^4 is the double nearest the decimal k * 10^-4,
+// narrowed to fp32.
+DEV float round_4dp(float x) {
+  const double k = rint((double)x * 10000.0);
+  return (float)(k / 10000.0);
+}
 }  // namespace
 
 constexpr int kQW = 8;                 // waves per question block
@@ -98,7 +110,8 @@ __global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, cons
                                                const float* __restrict__ prior, float gate, float lam, int joint,
                                                const int* __restrict__ o_off, float* __restrict__ logits,
                                                float* __restrict__ probs, int* __restrict__ amax,
-                                               float* __restrict__ jcos, float* __restrict__ mlp) {
+                                               float* __restrict__ jcos, float* __restrict__ mlp,
+                                               const int* __restrict__ q_type, AnswerOut ans) {
   __shared__ float sm[kQW];
   __shared__ int si[kQW];
   __shared__ float sl[kMaxOptions];
@@ -163,19 +176,43 @@ __global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, cons
   float z = 0.f;
   for (int k = threadIdx.x; k < no; k += kQT) z += expf(sl[k] - m);
   z = block_sum<kQW>(z, sm);
+  if (best == 0x7fffffff) best = 0;   // no comparable value: index 0
   for (int k = threadIdx.x; k < no; k += kQT) {
+    const float p = expf(sl[k] - m) / z;
     logits[o0 + k] = sl[k];
-    probs[o0 + k] = expf(sl[k] - m) / z;
+    probs[o0 + k] = p;
+    if (ans.probs_4dp) ans.probs_4dp[o0 + k] = round_4dp(p);
+    sl[k] = p;                        // each thread rewrites only the entries it read
   }
-  if (threadIdx.x == 0) amax[q] = best == 0x7fffffff ? 0 : best;   // no comparable value: index 0
+  if (threadIdx.x == 0) amax[q] = best;
+  if (!ans.value && !ans.confidence && !ans.value_4dp && !ans.confidence_4dp) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // answer of the question (metadata page "decision.response"): noul -> p(true), option 0 by the
+    // noul option order [true, false]; choice -> p of the answer; score -> mean level, levels 0..n-1
+    const int t = q_type[q];
+    const float conf = sl[best];
+    float v = conf;
+    if (t == 0) {
+      v = sl[0];
+    } else if (t == 2) {
+      v = 0.f;
+      for (int k = 1; k < no; ++k) v += (float)k * sl[k];
+    }
+    if (ans.value) ans.value[q] = v;
+    if (ans.confidence) ans.confidence[q] = conf;
+    if (ans.value_4dp) ans.value_4dp[q] = round_4dp(v);
+    if (ans.confidence_4dp) ans.confidence_4dp[q] = round_4dp(conf);
+  }
 }
 
 void launch_score(hipStream_t st, const float* U, const float* F, const float* hpart, int nsplit, size_t hstride,
                   const float* b1, const float* w2, float b2, const float* prior, float gate, float lam, int joint,
-                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp) {
+                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp,
+                  const int* q_type, const AnswerOut& ans) {
   if (NQ == 0) return;
   hipLaunchKernelGGL(k_score, dim3(NQ), dim3(kQT), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
-                     joint, o_off, logits, probs, amax, jcos, mlp);
+                     joint, o_off, logits, probs, amax, jcos, mlp, q_type, ans);
 }
 
 }  // namespace clef

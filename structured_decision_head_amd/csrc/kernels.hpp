@@ -294,9 +294,19 @@ void launch_field_attn(hipStream_t, const float* qkv_part, int nsplit, size_t st
 void launch_field_agg(hipStream_t, const float* U, const int* o_off, const float* sw, float sb, const float* qv,
                       const float* gp, const int* q_rec, const int* q_type, const float* temb, int NQ, float* F,
                       float2* fstats, float eps);
+// Answer outputs of the scoring kernel, each optional (null = not written):
+// value / confidence fp32 [NQ], their 4-decimal copies, 4-decimal probs [NO].
+struct AnswerOut {
+  float* value;
+  float* confidence;
+  float* value_4dp;
+  float* confidence_4dp;
+  float* probs_4dp;
+};
 // hpart: split-K slices of W1 z (nsplit, slice stride in floats), b1 its bias
 void launch_score(hipStream_t, const float* U, const float* F, const float* hpart, int nsplit, size_t hstride,
                   const float* b1, const float* w2, float b2, const float* prior, float gate, float lam, int joint,
-                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp);
+                  const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp,
+                  const int* q_type, const AnswerOut& ans);
 
 }  // namespace clef

@@ -64,6 +64,23 @@ class HeadRunner:
         C.clef_head_forward(self.handle, self.args, self.logits.data_ptr(), self.probs.data_ptr(),
                             self.argmax.data_ptr(), s.cuda_stream)
 
+    def forward_answers(self, stream: Optional[torch.cuda.Stream] = None):
+        """Forward plus the answer mapping; answers() reads the answer buffers."""
+        s = stream if stream is not None else torch.cuda.current_stream()
+        nq, no = max(self.batch.NQ, 1), max(self.batch.NO, 1)
+        if getattr(self, "ans", None) is None or self.ans[0].numel() < nq or self.ans[4].numel() < no:
+            self.ans = [torch.empty(nq, dtype=torch.float32, device=self.device) for _ in range(4)] + \
+                       [torch.empty(no, dtype=torch.float32, device=self.device)]
+        C.clef_head_forward_answers(self.handle, self.args, self.logits.data_ptr(), self.probs.data_ptr(),
+                                    self.argmax.data_ptr(), *[t.data_ptr() for t in self.ans],
+                                    stream_ptr=s.cuda_stream)
+
+    def answers(self):
+        """(value, confidence, value_4dp, confidence_4dp) fp32 [NQ] and probs_4dp fp32 [NO], as numpy."""
+        torch.cuda.synchronize()
+        NO, NQ = self.batch.NO, self.batch.NQ
+        return tuple(t[:NQ].cpu().numpy() for t in self.ans[:4]) + (self.ans[4][:NO].cpu().numpy(),)
+
     def outputs(self):
         torch.cuda.synchronize()
         NO, NQ = self.batch.NO, self.batch.NQ

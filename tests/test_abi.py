@@ -169,3 +169,14 @@ def test_create_sharing_rejects_null_source():
     with pytest.raises(C.ClefError) as e:
         C.clef_head_create_sharing(0)
     assert e.value.code == C.CLEF_E_ARG
+
+
+def test_forward_answers_rejects_null_before_any_work(case1):
+    """NULL answers (or a NULL handle) is refused on the host with CLEF_E_ARG."""
+    args = C.BatchArgs(case1.batch, 0)
+    L = C.load()
+    rc = L.clef_head_forward_answers(None, C.ctypes.byref(args.struct), None, None, None, None, None)
+    assert rc == C.CLEF_E_ARG
+    ans = C.clef_head_answers()
+    rc = L.clef_head_forward_answers(None, C.ctypes.byref(args.struct), None, None, None, C.ctypes.byref(ans), None)
+    assert rc == C.CLEF_E_ARG
