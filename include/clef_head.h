@@ -67,6 +67,13 @@ extern "C" {
 /* batch layouts */
 #define CLEF_PADDED 0           /* hidden is [B, L, H]; key_mask gives the valid prefix of each row */
 #define CLEF_VARLEN 1           /* hidden is [T, H], records back to back; cu_seqlens gives them */
+/* OR'ed into the layout: hidden holds IEEE fp16 elements instead of bf16 (the
+ * CoreML packaging hands the head fp16 hidden states and runs the head in
+ * fp32: CoreML conversion metadata page of clef-flash, "decision.head",
+ * dtype of record).  Row statistics, span pooling and the memory GEMM read
+ * fp16 (the GEMM with an fp16 copy of the folded memory weight, fp16 MFMA,
+ * fp32 accumulation); everything after the memory rows is unchanged. */
+#define CLEF_HIDDEN_F16 0x100
 
 typedef struct clef_head clef_head;   /* opaque handle */
 
@@ -99,10 +106,11 @@ typedef struct {
 /* One batch of encoded records.  Spans are record-relative, half-open
  * [start, end), and index the same positions as the hidden rows. */
 typedef struct {
-  int32_t layout;              /* CLEF_PADDED | CLEF_VARLEN */
+  int32_t layout;              /* CLEF_PADDED | CLEF_VARLEN, optionally | CLEF_HIDDEN_F16 */
   int32_t num_records;         /* B >= 1 */
   int32_t max_len;             /* L (CLEF_PADDED): row stride of hidden in rows */
-  const void *hidden;          /* DEVICE bf16 [B, L, H] (PADDED) or [T, H] (VARLEN); padding rows are never read */
+  const void *hidden;          /* DEVICE bf16 (fp16 with CLEF_HIDDEN_F16) [B, L, H] (PADDED) or [T, H] (VARLEN);
+                                  padding rows are never read */
   const uint8_t *key_mask;     /* HOST [B, L], 1 = valid; each row must be a prefix mask (PADDED) */
   const int32_t *cu_seqlens;   /* HOST [B+1], cu_seqlens[0] = 0, increasing (VARLEN) */
   int32_t num_questions;       /* NQ >= 0 */

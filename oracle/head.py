@@ -66,6 +66,19 @@ def from_bf16(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def from_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE half-precision bit patterns (uint16) -> float64, exactly."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def hidden_rows(batch, b: int, n: int) -> np.ndarray:
+    """The first n hidden rows of record b as float64.  The backbone hands the
+    head bf16 rows, or fp16 rows in the CoreML packaging (CoreML conversion
+    metadata page, "decision.head": the head reads fp16 hidden in fp32)."""
+    bits = batch.hidden[b, :n]
+    return from_f16(bits) if getattr(batch, "hidden_dtype", "bf16") == "f16" else from_bf16(bits)
+
+
 def load_params(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     """Convert named head tensors to float64 (bf16 tensors exactly; fp32 scalars as is)."""
     out = {}
@@ -238,7 +251,7 @@ def forward(weights: Dict[str, np.ndarray], head, batch, table_rows: Callable[[n
     question / option order.
 
     weights: named tensors (bf16 bit patterns or fp32); batch: a padded batch
-    (hidden [B, L, H] bf16 bits + lengths + span tables); table_rows(ids) returns
+    (hidden [B, L, H] bf16 or fp16 bits + lengths + span tables); table_rows(ids) returns
     the bf16 bit patterns of those lexical-table rows.  ``records`` restricts the
     evaluation to a subset (outputs for those records only)."""
     p = params if params is not None else load_params(weights)
@@ -250,7 +263,7 @@ def forward(weights: Dict[str, np.ndarray], head, batch, table_rows: Callable[[n
         n = int(batch.lengths[b])
         q0, q1 = int(batch.q_offsets[b]), int(batch.q_offsets[b + 1])
         o0, o1 = int(batch.o_offsets[q0]), int(batch.o_offsets[q1])
-        hid = from_bf16(batch.hidden[b, :n])
+        hid = hidden_rows(batch, b, n)
         o_rows = [from_bf16(table_rows(batch.o_ids[id_off[k]: id_off[k + 1]])) for k in range(o0, o1)]
         lg, pr, am = forward_record(p, head, hid, batch.q_type[q0:q1], batch.q_span[q0:q1],
                                     batch.o_offsets[q0: q1 + 1] - o0, batch.o_span[o0:o1], o_rows)

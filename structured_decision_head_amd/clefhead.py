@@ -20,6 +20,7 @@ CLEF_OK, CLEF_E_ARG, CLEF_E_LENGTH, CLEF_E_SPAN, CLEF_E_ID, CLEF_E_SCHEMA, CLEF_
     CLEF_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7, -8
 CLEF_BF16, CLEF_F32 = 1, 2
 CLEF_PADDED, CLEF_VARLEN = 0, 1
+CLEF_HIDDEN_F16 = 0x100
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
 
@@ -126,7 +127,8 @@ class BatchArgs:
             return a
 
         s = clef_head_batch()
-        s.layout = layout
+        # the element type of the hidden rows travels as a flag in the layout
+        s.layout = layout | (CLEF_HIDDEN_F16 if getattr(batch, "hidden_dtype", "bf16") == "f16" else 0)
         s.num_records = batch.B
         s.max_len = batch.L if layout == CLEF_PADDED else 0
         s.hidden = hidden_ptr

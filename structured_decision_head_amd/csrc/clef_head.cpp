@@ -148,6 +148,7 @@ struct Plan {
   int B = 0, NQ = 0, NO = 0, nact = 0;
   int64_t T = 0, Tpad = 0, Ptot = 0, nids = 0;
   int ntiles = 0, npool = 0, nitems = 0, kchunk = 128;
+  bool f16 = false;           // hidden rows are fp16 (CLEF_HIDDEN_F16), else bf16
   std::vector<int32_t> tab;   // all int32 tables, back to back
   size_t off_rec = 0, off_tiles = 0, off_kvtiles = 0, off_pool = 0, off_lex = 0, off_ids = 0, off_optq = 0,
          off_optrec = 0, off_qrec = 0, off_qtype = 0, off_ooff = 0, off_items = 0;
@@ -156,7 +157,9 @@ struct Plan {
 
 int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, bool tables) {
   if (!b) return fail(CLEF_E_ARG, "batch is NULL");
-  if (b->layout != CLEF_PADDED && b->layout != CLEF_VARLEN) return fail(CLEF_E_ARG, "unknown layout %d", b->layout);
+  const int layout = b->layout & ~CLEF_HIDDEN_F16;
+  if (layout != CLEF_PADDED && layout != CLEF_VARLEN) return fail(CLEF_E_ARG, "unknown layout %d", b->layout);
+  p.f16 = (b->layout & CLEF_HIDDEN_F16) != 0;
   const int B = b->num_records;
   if (B < 1) return fail(CLEF_E_ARG, "num_records must be >= 1");
   if (b->num_questions < 0 || b->num_options < 0) return fail(CLEF_E_ARG, "negative question / option count");
@@ -167,7 +170,7 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
 
   // record lengths and first hidden rows
   std::vector<int64_t> len(B), src0(B);
-  if (b->layout == CLEF_PADDED) {
+  if (layout == CLEF_PADDED) {
     if (b->max_len < 1) return fail(CLEF_E_LENGTH, "max_len must be >= 1");
     if (!b->key_mask) return fail(CLEF_E_ARG, "key_mask is NULL");
     for (int r = 0; r < B; ++r) {
@@ -365,8 +368,8 @@ struct Layer {
 };
 
 struct Weights {
-  const float *lnin_g, *lnin_b, *cmem, *dmem, *ba7, *bqq, *bg, *temb, *sw, *bkv, *bs1, *ws2;
-  const bf16_t *Wmem, *Wa7, *Wqq, *Wg, *Wkv, *Ws1;
+  const float *lnin_g, *lnin_b, *cmem, *dmem, *cmem16, *ba7, *bqq, *bg, *temb, *sw, *bkv, *bs1, *ws2;
+  const bf16_t *Wmem, *Wmem16, *Wa7, *Wqq, *Wg, *Wkv, *Ws1;   // Wmem16 holds fp16 bits
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -488,22 +491,29 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
   {
     const uint16_t* Wm = bf("mem.w");
     const std::vector<float> bm = tof("mem.b");
-    std::vector<uint16_t> Wp((size_t)D * H);
-    std::vector<float> cm(D), dm(D);
+    std::vector<uint16_t> Wp((size_t)D * H), Wp16((size_t)D * H);
+    std::vector<float> cm(D), cm16(D), dm(D);
     for (int j = 0; j < D; ++j) {
-      double cs = 0, ds = bm[j];
+      double cs = 0, cs16 = 0, ds = bm[j];
       for (int k = 0; k < H; ++k) {
         const float wv = bf16_to_f(Wm[(size_t)j * H + k]);
         const uint16_t wp = f_to_bf16(wv * g[k]);
         Wp[(size_t)j * H + k] = wp;
         cs += bf16_to_f(wp);
+        // fp16 copy for fp16 hidden rows (round to nearest even)
+        const _Float16 wh = (_Float16)(wv * g[k]);
+        Wp16[(size_t)j * H + k] = __builtin_bit_cast(uint16_t, wh);
+        cs16 += (double)(float)wh;
         ds += (double)wv * be[k];
       }
       cm[j] = (float)cs;
+      cm16[j] = (float)cs16;
       dm[j] = (float)ds;
     }
     put_bf(Wp.data(), Wp.size(), &W.Wmem);
     put_f(cm, &W.cmem);
+    put_bf(Wp16.data(), Wp16.size(), &W.Wmem16);
+    put_f(cm16, &W.cmem16);
     put_f(dm, &W.dmem);
   }
   // option-query projection: [W_c | W_l] along K with the three biases summed; the
@@ -1013,13 +1023,13 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   hipStream_t s2 = fork ? h->side.get() : st;
 
   // step 1: row statistics, pooled vectors, lexical vectors and prior
-  launch_rowstats_bf16(st, X, (int)H, tiles, p.ntiles, stats, eps);
+  launch_rowstats(st, X, (int)H, p.f16, tiles, p.ntiles, stats, eps);
   MARK(CLEF_STAGE_ROWSTATS);
   if (fork) {
     HIPCHK(hipEventRecord(h->ev_fork, st));
     HIPCHK(hipStreamWaitEvent(s2, h->ev_fork, 0));
   }
-  launch_pool(s2, X, (int)H, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
+  launch_pool(s2, X, (int)H, p.f16, pool, p.npool, stats, W.lnin_g, W.lnin_b, pooled);
   MARK(CLEF_STAGE_POOL);
   launch_lex_prior(s2, h->table, (int)H, lex, NO, ids, pooled, ebar, prior);
   MARK(CLEF_STAGE_LEXICAL);
@@ -1033,7 +1043,8 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         std::lock_guard<std::mutex> lk(g.mu);
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
-      launch_gemm_mem(st, X, (int)H, tiles, p.ntiles, W.Wmem, stats, W.cmem, W.dmem, mem);
+      launch_gemm_mem(st, X, (int)H, p.f16, tiles, p.ntiles, p.f16 ? W.Wmem16 : W.Wmem, stats,
+                      p.f16 ? W.cmem16 : W.cmem, W.dmem, mem);
       MARK(CLEF_STAGE_MEMORY_GEMM);
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
       MARK(CLEF_STAGE_KV_GEMM);

@@ -65,6 +65,26 @@ DEV void split8(const float* f, uint4& hi, uint4& lo) {
 DEV bf16x8 as_bf16x8(const uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 DEV bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// IEEE half precision: hidden states may arrive as fp16 instead of bf16.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));               // MFMA operand
+DEV f16x8 as_f16x8(const u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Unpack 8 fp16 held in a uint4 into floats (exact).
+DEV void unpack8_f16(const uint4 v, float* f) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 a = __builtin_bit_cast(h2, v.x), b = __builtin_bit_cast(h2, v.y);
+  const h2 c = __builtin_bit_cast(h2, v.z), d = __builtin_bit_cast(h2, v.w);
+  f[0] = (float)a.x; f[1] = (float)a.y; f[2] = (float)b.x; f[3] = (float)b.y;
+  f[4] = (float)c.x; f[5] = (float)c.y; f[6] = (float)d.x; f[7] = (float)d.y;
+}
+
+// Unpack 8 16-bit values of the hidden element type (fp16 if F16, else bf16).
+template <bool F16>
+DEV void unpack8_hidden(const uint4 v, float* f) {
+  if constexpr (F16) unpack8_f16(v, f);
+  else unpack8(v, f);
+}
+
 DEV float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -12,6 +12,8 @@
 //
 // Tile: 256 x 256 outputs per workgroup, 4 waves in a 2 x 2 grid each owning
 // 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16 blocks, accumulators in AGPRs).
+// With fp16 hidden rows the memory GEMM multiplies fp16 operands (an fp16 copy
+// of W') with v_mfma_f32_32x32x16_f16 instead.
 #include "kernels.hpp"
 
 namespace clef {
@@ -40,6 +42,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   const float* c;
   const float* d;
   bf16_t* out;           // [rows][1024]
+  static constexpr bool kF16 = false;                  // operands bf16
   static constexpr bool kHasPlain = false;
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
   static constexpr int kImageBytes = 256 * kLd * 2;
@@ -94,10 +97,16 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
 // transposed, [layer][head][row / 32][64][32] with the 32 keys of a block in
 // vblock_pos() order (plain tiles: a lane's accumulators e = 8 q .. 8 q + 7
 // land on 8 consecutive key positions, one 16-byte run).
+// The same with fp16 hidden rows and an fp16 copy of W' (fp16 MFMA).
+struct EpiMem16 : EpiMem {
+  static constexpr bool kF16 = true;
+};
+
 struct EpiKV {
   const float* bias;
   bf16_t* kv;          // layer r: K at kv + (2r) * 16 * Tpad * 64, V at kv + (2r+1) * 16 * Tpad * 64
   long long Tpad;
+  static constexpr bool kF16 = false;
   static constexpr bool kHasPlain = true;
   static constexpr int kImageBytes = 4 * 256 * 64 * 2;
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
@@ -202,6 +211,13 @@ DEV void tile_order(int b, int ntm, int ntn, int& tm, int& tn) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// One 32x32x16 MFMA step on 16-byte operand fragments of either 16-bit type.
+template <bool F16>
+DEV f32x16 mfma32(const u32x4 a, const u32x4 b, const f32x16 c) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter constrained to <= n
 #define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // s_waitcnt lgkmcnt(0) only
@@ -279,14 +295,14 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   {                                                                              \
     const int ph_ = (2 * (kk) + hl) ^ fsw, sb_ = (stage) * (2 * BM * 8) + ph_;   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                              \
-      F##a[i] = as_bf16x8(smem[0][0][sb_ + fa0 + i * 256]);                      \
-      F##b[i] = as_bf16x8(smem[0][0][sb_ + fb0 + i * 256]);                      \
+      F##a[i] = smem[0][0][sb_ + fa0 + i * 256];                                 \
+      F##b[i] = smem[0][0][sb_ + fb0 + i * 256];                                 \
     }                                                                            \
   }
 #define MULTIPLY(F)                                                                       \
   _Pragma("unroll") for (int mi = 0; mi < 4; ++mi)                                        \
   _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                        \
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[mi], F##b[ni], acc[mi][ni], 0, 0, 0);
+    acc[mi][ni] = mfma32<Epi::kF16>(F##a[mi], F##b[ni], acc[mi][ni]);
 #define INTERLEAVE_DS(id)                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i) {                             \
     __builtin_amdgcn_sched_group_barrier(0x008, 2, id);   /* 2 MFMA */        \
@@ -303,7 +319,7 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  bf16x8 Xa[4], Xb[4], Ya[4], Yb[4];
+  u32x4 Xa[4], Xb[4], Ya[4], Yb[4];
 
   const int nk = K / KS;                 // >= 2 (K a multiple of 128)
   COPY_STAGE(0, 0)
@@ -359,12 +375,18 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 
 }  // namespace
 
-void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, const int4* tiles, int ntiles,
+void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
                      const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem) {
   if (ntiles == 0) return;
   const int ntn = 1024 / BN;
   EpiMem epi{stats, c, d, mem};
-  hipLaunchKernelGGL(k_gemm256<EpiMem>, dim3(ntiles * ntn), dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, epi);
+  if (f16) {
+    EpiMem16 e16;
+    static_cast<EpiMem&>(e16) = epi;
+    hipLaunchKernelGGL(k_gemm256<EpiMem16>, dim3(ntiles * ntn), dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, e16);
+  } else {
+    hipLaunchKernelGGL(k_gemm256<EpiMem>, dim3(ntiles * ntn), dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, epi);
+  }
 }
 
 void launch_gemm_kv(hipStream_t st, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,

@@ -15,10 +15,12 @@ namespace clef {
 // ---------------------------------------------------------------------------
 // mu / rstd of every row of a 256-row tile (one wave per row, 4 rows per
 // block; grid = (tiles, 64)).  Rows past the tile's valid count get (0, 0) so
-// that padded rows of the packed row space stay finite downstream.
+// that padded rows of the packed row space stay finite downstream.  Hidden
+// elements are bf16, or fp16 when F16 (the CoreML packaging feeds fp16 hidden
+// states to the head, CoreML conversion metadata page "decision.head").
 // ---------------------------------------------------------------------------
-template <int NCH>
-__global__ __launch_bounds__(256) void k_rowstats_bf16(const bf16_t* __restrict__ X,
+template <int NCH, bool F16>
+__global__ __launch_bounds__(256) void k_rowstats(const bf16_t* __restrict__ X,
                                                        const int4* __restrict__ tiles,
                                                        float2* __restrict__ stats, float eps) {
   constexpr int H = NCH * 512;
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(256) void k_rowstats_bf16(const bf16_t* __restrict_
   for (int c = 0; c < NCH; ++c) q[c] = row[c * 64 + lane];
   float v[NCH * 8];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) unpack8(q[c], v + 8 * c);
+  for (int c = 0; c < NCH; ++c) unpack8_hidden<F16>(q[c], v + 8 * c);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH * 8; ++i) s += v[i];
@@ -50,11 +52,15 @@ __global__ __launch_bounds__(256) void k_rowstats_bf16(const bf16_t* __restrict_
   if (lane == 0) stats[t.y + r] = make_float2(mu, 1.0f / sqrtf(var + eps));
 }
 
-void launch_rowstats_bf16(hipStream_t st, const bf16_t* X, int H, const int4* tiles, int ntiles,
-                          float2* stats, float eps) {
+void launch_rowstats(hipStream_t st, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles,
+                     float2* stats, float eps) {
   const dim3 grid(ntiles, 64), block(256);
   switch (H / 512) {
-#define CASE(n) case n: hipLaunchKernelGGL(k_rowstats_bf16<n>, grid, block, 0, st, X, tiles, stats, eps); break;
+#define CASE(n)                                                                              \
+  case n:                                                                                    \
+    if (f16) hipLaunchKernelGGL((k_rowstats<n, true>), grid, block, 0, st, X, tiles, stats, eps); \
+    else hipLaunchKernelGGL((k_rowstats<n, false>), grid, block, 0, st, X, tiles, stats, eps);    \
+    break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
     CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
@@ -66,7 +72,7 @@ void launch_rowstats_bf16(hipStream_t st, const bf16_t* X, int H, const int4* ti
 // slot): out[slot] = gamma * mean_t((x_t - mu_t) * rstd_t) + beta, which is
 // the mean of the LayerNorm-ed rows.  One block per entry.
 // ---------------------------------------------------------------------------
-template <int NV>
+template <int NV, bool F16>
 __global__ __launch_bounds__(256) void k_pool(const bf16_t* __restrict__ X, int H,
                                               const int4* __restrict__ ent,
                                               const float2* __restrict__ stats,
@@ -87,7 +93,7 @@ __global__ __launch_bounds__(256) void k_pool(const bf16_t* __restrict__ X, int 
       const int v = threadIdx.x + 256 * j;
       if (v < nvec) {
         float x[8];
-        unpack8(row[v], x);
+        unpack8_hidden<F16>(row[v], x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] += (x[i] - s.x) * s.y;
       }
@@ -108,12 +114,16 @@ __global__ __launch_bounds__(256) void k_pool(const bf16_t* __restrict__ X, int 
   }
 }
 
-void launch_pool(hipStream_t st, const bf16_t* X, int H, const int4* ent, int nent, const float2* stats,
+void launch_pool(hipStream_t st, const bf16_t* X, int H, bool f16, const int4* ent, int nent, const float2* stats,
                  const float* gamma, const float* beta, float* out) {
   if (nent == 0) return;
   const int nv = (H / 8 + 255) / 256;
   switch (nv) {
-#define CASE(n) case n: hipLaunchKernelGGL(k_pool<n>, dim3(nent), dim3(256), 0, st, X, H, ent, stats, gamma, beta, out); break;
+#define CASE(n)                                                                                            \
+  case n:                                                                                                  \
+    if (f16) hipLaunchKernelGGL((k_pool<n, true>), dim3(nent), dim3(256), 0, st, X, H, ent, stats, gamma, beta, out); \
+    else hipLaunchKernelGGL((k_pool<n, false>), dim3(nent), dim3(256), 0, st, X, H, ent, stats, gamma, beta, out);    \
+    break;
     CASE(1) CASE(2) CASE(3) CASE(4)
 #undef CASE
   }

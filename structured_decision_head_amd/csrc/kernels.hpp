@@ -13,11 +13,12 @@ DEV int vblock_pos(int k) { return (k & 16) | ((k & 4) << 1) | ((k & 8) >> 1) | 
 // ---------------------------------------------------------------------------
 // row kernels
 // ---------------------------------------------------------------------------
+// X holds 16-bit hidden elements: bf16, or fp16 when f16 is set.
 // tiles: int4 (first hidden row, first packed row, valid rows <= 256, record)
-void launch_rowstats_bf16(hipStream_t, const bf16_t* X, int H, const int4* tiles, int ntiles, float2* stats,
-                          float eps);
+void launch_rowstats(hipStream_t, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles, float2* stats,
+                     float eps);
 // entries: int4 (first hidden row, length, first stats row, output slot)
-void launch_pool(hipStream_t, const bf16_t* X, int H, const int4* ent, int nent, const float2* stats,
+void launch_pool(hipStream_t, const bf16_t* X, int H, bool f16, const int4* ent, int nent, const float2* stats,
                  const float* gamma, const float* beta, float* out);
 // entries: int4 (first id, count, question slot, global slot)
 void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int nent, const int* ids,
@@ -26,8 +27,9 @@ void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int 
 // ---------------------------------------------------------------------------
 // big GEMMs (rows of the packed row space)
 // ---------------------------------------------------------------------------
-void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, const int4* tiles, int ntiles, const bf16_t* Wm,
-                     const float2* stats, const float* c, const float* d, bf16_t* mem);
+// f16: hidden and Wm are fp16 (fp16 MFMA), else both bf16
+void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
+                     const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
                     const float* bkv, int n_layers, bf16_t* kv, long long Tpad);
 

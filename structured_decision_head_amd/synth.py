@@ -166,6 +166,7 @@ class Batch:
     o_offsets: np.ndarray        # int32 [NQ+1] questions -> options
     o_span: np.ndarray           # int32 [NO, 2]
     o_ids: np.ndarray            # int32 [sum of option span lengths]
+    hidden_dtype: str = "bf16"   # element type of the hidden bits: "bf16" | "f16"
 
     @property
     def B(self) -> int:
@@ -215,7 +216,8 @@ class Batch:
                      q_span=self.q_span[q0:q1].copy(),
                      o_offsets=(self.o_offsets[q0: q1 + 1] - o0).astype(np.int32),
                      o_span=self.o_span[o0:o1].copy(),
-                     o_ids=self.o_ids[ido[o0]: ido[o1]].copy())
+                     o_ids=self.o_ids[ido[o0]: ido[o1]].copy(),
+                     hidden_dtype=self.hidden_dtype)
 
 
 @dataclass
@@ -242,6 +244,7 @@ class CaseSpec:
     prefix: int = PREFIX_TOKENS
     suffix: int = SUFFIX_TOKENS
     filler: Tuple[int, int, int, int, int] = (6, 4, 2, 2, 1)   # block, field header, options header, per option, end
+    hidden_dtype: str = "bf16"           # "bf16" | "f16": rounding of the hidden draws
 
 
 @dataclass
@@ -382,9 +385,12 @@ def make_batch(spec: CaseSpec) -> Batch:
         g = np.random.Generator(np.random.Philox(kids[b]))
         rows = L if spec.pad_fill == "normal" else n
         x = g.standard_normal(rows * H, dtype=np.float32).reshape(rows, H)
-        hidden[b, :rows] = f32_to_bf16_bits(x)
+        if spec.hidden_dtype == "f16":
+            hidden[b, :rows] = x.astype(np.float16).view(np.uint16)   # round to nearest even
+        else:
+            hidden[b, :rows] = f32_to_bf16_bits(x)
         if rows < L:
-            hidden[b, rows:] = np.uint16(0x7FC0)   # quiet NaN
+            hidden[b, rows:] = np.uint16(0x7E00 if spec.hidden_dtype == "f16" else 0x7FC0)   # quiet NaN
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(spec.B)))
@@ -393,7 +399,7 @@ def make_batch(spec: CaseSpec) -> Batch:
                  q_offsets=np.array(q_off, np.int32), q_type=np.array(q_types, np.int32),
                  q_span=np.array(q_spans, np.int32).reshape(-1, 2),
                  o_offsets=np.concatenate([[0], np.cumsum(o_counts)]).astype(np.int32),
-                 o_span=o_span, o_ids=o_ids)
+                 o_span=o_span, o_ids=o_ids, hidden_dtype=spec.hidden_dtype)
 
 
 def make_case(spec: CaseSpec, with_table: bool = True) -> Case:
