@@ -638,8 +638,8 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 
 // workspace layout for one plan
 struct WsLayout {
-  size_t tab, stats, pooled, ebar, prior, mem, kv, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats, fattn, pm,
-      pl, po, part, total;
+  size_t tab, stats, pooled, ebar, prior, mem, kv, bigpart, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats,
+      fattn, pm, pl, po, part, total;
 };
 
 WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
@@ -654,6 +654,13 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.prior = take(NO * 4);
   L.mem = take(Tp * D * 2);
   L.kv = take(NR * 2 * NH * Tp * 64 * 2);
+  // split-K partial sums of the big GEMMs (few row tiles only; the memory and
+  // K/V GEMMs run one after the other on one stream and share the region)
+  {
+    const size_t sm = big_gemm_split(p.ntiles, D / 256, (int)H), skv = big_gemm_split(p.ntiles, (int)NR * 8, D);
+    const size_t bytes = std::max(sm > 1 ? sm * Tp * D * 4 : 0, (NR > 0 && skv > 1) ? skv * Tp * NR * 2 * D * 4 : 0);
+    L.bigpart = take(bytes);
+  }
   L.u = take(NO * D * 4);
   L.ustats = take(NO * 8);
   L.qbuf = take(NO * D * 4);
@@ -978,6 +985,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   float* prior = reinterpret_cast<float*>(ws + L.prior);
   bf16_t* mem = reinterpret_cast<bf16_t*>(ws + L.mem);
   bf16_t* kv = reinterpret_cast<bf16_t*>(ws + L.kv);
+  float* bigpart = reinterpret_cast<float*>(ws + L.bigpart);
   float* u = reinterpret_cast<float*>(ws + L.u);
   float2* ustats = reinterpret_cast<float2*>(ws + L.ustats);
   float* qbuf = reinterpret_cast<float*>(ws + L.qbuf);
@@ -1044,9 +1052,9 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
       launch_gemm_mem(st, X, (int)H, p.f16, tiles, p.ntiles, p.f16 ? W.Wmem16 : W.Wmem, stats,
-                      p.f16 ? W.cmem16 : W.cmem, W.dmem, mem);
+                      p.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, p.Tpad);
       MARK(CLEF_STAGE_MEMORY_GEMM);
-      launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad);
+      launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad, bigpart);
       MARK(CLEF_STAGE_KV_GEMM);
       if (fork) {
         std::lock_guard<std::mutex> lk(g.mu);

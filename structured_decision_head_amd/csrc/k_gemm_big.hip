@@ -43,6 +43,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   const float* d;
   bf16_t* out;           // [rows][1024]
   static constexpr bool kF16 = false;                  // operands bf16
+  static constexpr bool kDirect = false;               // output staged through LDS
   static constexpr bool kHasPlain = false;
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
   static constexpr int kImageBytes = 256 * kLd * 2;
@@ -107,6 +108,7 @@ struct EpiKV {
   bf16_t* kv;          // layer r: K at kv + (2r) * 16 * Tpad * 64, V at kv + (2r+1) * 16 * Tpad * 64
   long long Tpad;
   static constexpr bool kF16 = false;
+  static constexpr bool kDirect = false;
   static constexpr bool kHasPlain = true;
   static constexpr int kImageBytes = 4 * 256 * 64 * 2;
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
@@ -188,6 +190,41 @@ struct EpiKV {
   }
 };
 
+// Split-K partial sums: K slice s of a tile writes its raw fp32 accumulators to
+// part[s][row][col] (row in the packed row space, N columns); a reduction
+// kernel sums the slices in order and applies the memory or K/V epilogue.
+// Transposed tiles: a lane owns one output row and runs of 4 columns.
+template <bool F16>
+struct EpiPart {
+  float* part;
+  long long Tpad;
+  int N;
+  static constexpr bool kF16 = F16;
+  static constexpr bool kDirect = true;
+  static constexpr bool kHasPlain = false;
+  static constexpr int kImageBytes = 0;
+  DEV bool transposed(int) const { return true; }
+  DEV void load_consts(int, int, int, float (&)[4]) const {}
+  DEV void put_consts(float*, int, const float (&)[4]) const {}
+  // orow / ocol: first output row / column of the wave's 128 x 128 block
+  DEV void store_acc(const f32x16 (&acc)[4][4], int orow, int ocol, int s, int lane) const {
+    float* base = part + ((size_t)s * Tpad + orow + (lane & 31)) * N + ocol + 4 * (lane >> 5);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[mi][ni];
+          *reinterpret_cast<float4*>(base + (size_t)ni * 32 * N + mi * 32 + 8 * g) =
+              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        }
+  }
+  DEV void stage_t(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
+  DEV void stage(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
+  DEV void store(const bf16_t*, int, int, bool, int) const {}
+};
+
 // Output tile of workgroup b.  Workgroups are dealt to the 8 XCDs round-robin
 // (b % 8), each XCD with its own L2.  Column tiles are grouped in fours
 // (256 x 4 W rows: 2 MB at K = 1024, 8 MB at K = 4096); XCD x works on column
@@ -238,7 +275,7 @@ DEV f32x16 mfma32(const u32x4 a, const u32x4 b, const f32x16 c) {
 template <class Epi>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
-               const bf16_t* __restrict__ W, int K, Epi epi) {
+               const bf16_t* __restrict__ W, int K, int nsplit, Epi epi) {
   constexpr int KS = 64, NST = 2;
   constexpr int kRingBytes = NST * 2 * BM * 8 * 16;
   constexpr int kSpan = Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
@@ -248,8 +285,12 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   u32x4 (*smem)[2][BM * 8] = reinterpret_cast<u32x4 (*)[2][BM * 8]>(lds);
   float* cst = reinterpret_cast<float*>(lds + kSpan);
 
+  // nsplit > 1: workgroup b multiplies K slice b / (tiles) of length K / nsplit
+  const int ntiles_mn = gridDim.x / nsplit;
+  const int ks = blockIdx.x / ntiles_mn;
+  const int kbase = ks * (K / nsplit);
   int tm, tn;
-  tile_order(blockIdx.x, gridDim.x / ntile_n, ntile_n, tm, tn);
+  tile_order(blockIdx.x - ks * ntiles_mn, ntiles_mn / ntile_n, ntile_n, tm, tn);
   const int4 T = tiles[tm];              // (first A row, first output row, valid rows, record)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -285,11 +326,11 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 #define COPY_A(stage, k0)                                                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? aoffO : aoffE) + i * astep, (k0) * 2, 0, 0);
+                                             ((i & 1) ? aoffO : aoffE) + i * astep, (kbase + (k0)) * 2, 0, 0);
 #define COPY_B(stage, k0)                                                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? woffO : woffE) + i * wstep, (k0) * 2, 0, 0);
+                                             ((i & 1) ? woffO : woffE) + i * wstep, (kbase + (k0)) * 2, 0, 0);
 #define COPY_STAGE(stage, k0) COPY_A(stage, k0) COPY_B(stage, k0)
 #define LOAD_FRAGS(F, stage, kk)                                                 \
   {                                                                              \
@@ -321,7 +362,7 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   u32x4 Xa[4], Xb[4], Ya[4], Yb[4];
 
-  const int nk = K / KS;                 // >= 2 (K a multiple of 128)
+  const int nk = K / nsplit / KS;        // >= 2 (K / nsplit a multiple of 128)
   COPY_STAGE(0, 0)
   WAIT_VM(0);
   __builtin_amdgcn_s_barrier();
@@ -361,6 +402,10 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 
   // All 256 rows are stored: rows past the valid count come from clamped
   // (finite) inputs and keep the padded part of the row space finite.
+  if constexpr (Epi::kDirect) {
+    epi.store_acc(acc, T.y + wb * 128, tn * BN + wa * 128, ks, lane);
+    return;
+  }
   bf16_t* img = reinterpret_cast<bf16_t*>(lds);
   __syncthreads();                       // every wave is done with the operand ring
   if constexpr (Epi::kHasPlain) {
@@ -373,28 +418,133 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   epi.store(img, T.y, tn * BN, tr, tid);
 }
 
+
+// Sum of the split-K slices of the memory GEMM, then the folded-LayerNorm
+// epilogue m = rstd (sum - mu c) + d (the same arithmetic as the unsplit
+// epilogue); every row of the packed row space is written.  8 columns per thread.
+__global__ __launch_bounds__(256) void k_mem_reduce(const float* __restrict__ part, int nsplit, long long Tpad,
+                                                    const float2* __restrict__ stats, const float* __restrict__ c,
+                                                    const float* __restrict__ d, bf16_t* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;   // 8-column group
+  const long long row = i >> 7;
+  const int col = (int)(i & 127) * 8;
+  if (row >= Tpad) return;
+  float a[8];
+  const float* p = part + row * 1024 + col;
+  {
+    const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
+    a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w; a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+  }
+  for (int s = 1; s < nsplit; ++s) {
+    const float* q = p + (size_t)s * Tpad * 1024;
+    const float4 x = *reinterpret_cast<const float4*>(q), y = *reinterpret_cast<const float4*>(q + 4);
+    a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w; a[4] += y.x; a[5] += y.y; a[6] += y.z; a[7] += y.w;
+  }
+  const float2 st = stats[row];
+  uint4 v;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = pack_bf16x2(st.y * (a[2 * k] - st.x * c[col + 2 * k]) + d[col + 2 * k],
+                       st.y * (a[2 * k + 1] - st.x * c[col + 2 * k + 1]) + d[col + 2 * k + 1]);
+  *reinterpret_cast<uint4*>(out + row * 1024 + col) = v;
+}
+
+// Sum of the split-K slices of the K/V GEMM plus bias, written in the routing
+// attention's layouts (K head-major [layer][head][row][64]; V per 32-row block
+// [layer][head][row / 32][64][32] with keys at vblock_pos()).  One block per
+// (32-row block, head of one K or V): the sums are staged in LDS, then
+// written as 4 KB of contiguous memory.
+__global__ __launch_bounds__(256) void k_kv_reduce(const float* __restrict__ part, int nsplit, long long Tpad,
+                                                   const float* __restrict__ bias, bf16_t* __restrict__ kv) {
+  __shared__ float tile[32][65];
+  const long long row0 = (long long)blockIdx.x * 32;
+  const int hc = blockIdx.y;                 // 64-column group: layer r = hc / 32, V if (hc / 16) & 1
+  const int N = gridDim.y * 64;
+  const int t = threadIdx.x, r = t >> 3, c8 = (t & 7) * 8;
+  const float* p = part + (row0 + r) * N + hc * 64 + c8;
+  float a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = p[k];
+  for (int s = 1; s < nsplit; ++s) {
+    const float* q = p + (size_t)s * Tpad * N;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] += q[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) tile[r][c8 + k] = a[k] + bias[hc * 64 + c8 + k];
+  __syncthreads();
+  const bool isv = (hc >> 4) & 1;
+  bf16_t* head = kv + (size_t)hc * (size_t)Tpad * 64;   // hc = (2 layer + isv) * 16 + head
+  uint4 v;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+  if (!isv) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(tile[r][c8 + 2 * k], tile[r][c8 + 2 * k + 1]);
+    *reinterpret_cast<uint4*>(head + (row0 + r) * 64 + c8) = v;
+  } else {
+    const int f = t >> 2, p0 = (t & 3) * 8;  // feature row f, key positions p0 .. p0 + 7
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = pack_bf16x2(tile[vblock_pos(p0 + 2 * k)][f], tile[vblock_pos(p0 + 2 * k + 1)][f]);
+    *reinterpret_cast<uint4*>(head + (row0 >> 5) * 2048 + f * 32 + p0) = v;
+  }
+}
+
 }  // namespace
 
+int big_gemm_split(int ntiles, int ntn, int K) {
+  const int base = ntiles * ntn;
+  if (base > 64) return 1;
+  int s = 1;
+  while (s < 16 && 2 * s * base <= 256 && K / (2 * s) >= 256 && (K / (2 * s)) % 128 == 0) s *= 2;
+  return s;
+}
+
 void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
-                     const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem) {
+                     const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
+                     float* part, long long Tpad) {
   if (ntiles == 0) return;
   const int ntn = 1024 / BN;
+  const int S = part ? big_gemm_split(ntiles, ntn, H) : 1;
+  const dim3 grid(ntiles * ntn * S);
+  if (S > 1) {
+    if (f16) {
+      hipLaunchKernelGGL(k_gemm256<EpiPart<true>>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, S,
+                         EpiPart<true>{part, Tpad, 1024});
+    } else {
+      hipLaunchKernelGGL(k_gemm256<EpiPart<false>>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, S,
+                         EpiPart<false>{part, Tpad, 1024});
+    }
+    hipLaunchKernelGGL(k_mem_reduce, dim3((unsigned)((Tpad * 128 + 255) / 256)), dim3(256), 0, st, part, S, Tpad,
+                       stats, c, d, mem);
+    return;
+  }
   EpiMem epi{stats, c, d, mem};
   if (f16) {
     EpiMem16 e16;
     static_cast<EpiMem&>(e16) = epi;
-    hipLaunchKernelGGL(k_gemm256<EpiMem16>, dim3(ntiles * ntn), dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, e16);
+    hipLaunchKernelGGL(k_gemm256<EpiMem16>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, 1, e16);
   } else {
-    hipLaunchKernelGGL(k_gemm256<EpiMem>, dim3(ntiles * ntn), dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, epi);
+    hipLaunchKernelGGL(k_gemm256<EpiMem>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, 1, epi);
   }
 }
 
 void launch_gemm_kv(hipStream_t st, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
-                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad) {
+                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part) {
   if (ntiles == 0 || n_layers == 0) return;
   const int ntn = n_layers * 2048 / BN;
+  const int S = part ? big_gemm_split(ntiles, ntn, 1024) : 1;
+  if (S > 1) {
+    hipLaunchKernelGGL(k_gemm256<EpiPart<false>>, dim3(ntiles * ntn * S), dim3(256), 0, st, mem, 1024, tiles, ntn,
+                       Wkv, 1024, S, EpiPart<false>{part, Tpad, n_layers * 2048});
+    hipLaunchKernelGGL(k_kv_reduce, dim3((unsigned)(Tpad / 32), n_layers * 32), dim3(256), 0, st, part, S, Tpad, bkv,
+                       kv);
+    return;
+  }
   EpiKV epi{bkv, kv, Tpad};
-  hipLaunchKernelGGL(k_gemm256<EpiKV>, dim3(ntiles * ntn), dim3(256), 0, st, mem, 1024, tiles, ntn, Wkv, 1024, epi);
+  hipLaunchKernelGGL(k_gemm256<EpiKV>, dim3(ntiles * ntn), dim3(256), 0, st, mem, 1024, tiles, ntn, Wkv, 1024, 1,
+                     epi);
 }
 
 }  // namespace clef

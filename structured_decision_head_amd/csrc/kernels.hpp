@@ -27,11 +27,19 @@ void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int 
 // ---------------------------------------------------------------------------
 // big GEMMs (rows of the packed row space)
 // ---------------------------------------------------------------------------
-// f16: hidden and Wm are fp16 (fp16 MFMA), else both bf16
+// Number of K slices (1 = no split) for a big GEMM of ntiles row tiles x ntn
+// 256-column tiles over depth K: a batch of few row tiles leaves most CUs
+// idle, so its K is split until about 256 workgroups run (at most 16 slices,
+// each at least 256 deep).  The slices' fp32 partial sums need
+// split * Tpad * N floats of workspace.
+int big_gemm_split(int ntiles, int ntn, int K);
+// f16: hidden and Wm are fp16 (fp16 MFMA), else both bf16.  part: split-K
+// workspace (null: never split); Tpad = ntiles * 256 rows.
 void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
-                     const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem);
+                     const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
+                     float* part, long long Tpad);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
-                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad);
+                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part);
 
 // ---------------------------------------------------------------------------
 // small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue
