@@ -494,10 +494,15 @@ __global__ __launch_bounds__(256) void k_kv_reduce(const float* __restrict__ par
 }  // namespace
 
 int big_gemm_split(int ntiles, int ntn, int K) {
+  // Every slice adds 2 * Tpad * N * 4 bytes of partial-sum traffic, so the
+  // split stops at 8 slices (16 were no faster on the single-record batch).
+  // Grids of more than 64 tiles stay whole: the forward's side stream fills
+  // the CUs they leave idle, and splitting them (B=1, L=2048 K/V GEMM; B=2,
+  // L=4096 memory GEMM) made the whole forward slower.
   const int base = ntiles * ntn;
   if (base > 64) return 1;
   int s = 1;
-  while (s < 16 && 2 * s * base <= 256 && K / (2 * s) >= 256 && (K / (2 * s)) % 128 == 0) s *= 2;
+  while (s < 8 && 2 * s * base <= 256 && K / (2 * s) >= 256 && (K / (2 * s)) % 128 == 0) s *= 2;
   return s;
 }
 

@@ -29,7 +29,7 @@ void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int 
 // ---------------------------------------------------------------------------
 // Number of K slices (1 = no split) for a big GEMM of ntiles row tiles x ntn
 // 256-column tiles over depth K: a batch of few row tiles leaves most CUs
-// idle, so its K is split until about 256 workgroups run (at most 16 slices,
+// idle, so its K is split until about 256 workgroups run (at most 8 slices,
 // each at least 256 deep).  The slices' fp32 partial sums need
 // split * Tpad * N floats of workspace.
 int big_gemm_split(int ntiles, int ntn, int K);

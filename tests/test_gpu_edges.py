@@ -134,3 +134,18 @@ def test_tile_multiple_lengths(torch_gpu):
     batch = dataclasses.replace(batch, q_span=q_span, o_span=o_span)
     case = dataclasses.replace(case, batch=batch)
     _check_all(case, _run(case), "tile-multiple")
+
+
+@pytest.mark.parametrize("B,L", [(1, 200), (1, 2048), (2, 4096), (5, 900)])
+def test_split_k_big_gemms(torch_gpu, B, L):
+    """Batches of few 256-row tiles split the K of the memory and K/V GEMMs
+    into slices (1 tile: 8 and 4 slices; 8 tiles: 8 and 1; 5 records of 4
+    tiles: 2 and 1; 32 tiles: none) whose partial sums a reduction kernel
+    adds in order before the epilogue; the result must match the oracle like
+    the unsplit GEMMs do."""
+    spec = _spec(f"split-{B}x{L}", 7200 + B * 10 + L // 100, B=B, L=L, lengths=("fixed", L, L), fields="counts",
+                 counts=(2, 2, 1), choice_opts=(2, 5), instr_len=(2, 6), opt_len=(1, 4))
+    say(f"case split-K big GEMMs: B={B} L={L}")
+    case = synth.make_case(spec)
+    out = _run(case)
+    _check_all(case, out, f"split {B}x{L}")
