@@ -187,6 +187,42 @@ typedef struct {
 CLEF_API int clef_head_forward_answers(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
                                        int32_t *argmax, const clef_head_answers *answers, void *hip_stream);
 
+/* Streamed ingest: the head consumes a batch's hidden rows while the
+ * backbone still produces them (CoreML conversion metadata page of
+ * clef-flash, "decision.readout" and "prefill_chunk": a record runs through
+ * the backbone as consecutive calls of 64 positions, each returning those
+ * positions' final-norm hidden rows), so the head's per-row work (LayerNorm
+ * statistics, memory rows, K/V rows of every routing layer) overlaps the
+ * backbone and only the option / field / scoring chain remains at the end.
+ * The result is bit-identical to clef_head_forward on the same rows.
+ *
+ * clef_head_stream_begin: batch must use CLEF_VARLEN (cu_seqlens gives each
+ *   record's length; CLEF_HIDDEN_F16 may be OR'ed in); batch->hidden is
+ *   ignored.  Validates the batch like clef_head_forward (same error codes),
+ *   sizes the workspace and handle-owned staging rows [T, H], and uploads the
+ *   span tables on hip_stream.  CLEF_E_ARG if a stream is already open.
+ * clef_head_stream_rows: rows [row0, row0 + nrows) of record `record`
+ *   (DEVICE, nrows x H elements of the batch's element type, row stride H).
+ *   Each record's rows arrive in order: row0 must equal the number of its
+ *   rows received so far (CLEF_E_ARG otherwise), and rows past its length
+ *   are CLEF_E_LENGTH.  The rows are copied on hip_stream (they must stay
+ *   valid until the stream reaches the copy); every 256-row tile the chunk
+ *   completes is processed at once on hip_stream.
+ * clef_head_stream_end: batch must describe the same batch as at begin (its
+ *   host tables are read again; CLEF_E_ARG if they differ); every row must
+ *   have arrived (CLEF_E_LENGTH otherwise).  Runs the rest of the forward on
+ *   hip_stream; outputs as clef_head_forward.  The stream is closed on
+ *   success.
+ * clef_head_stream_cancel: closes an open stream without computing outputs.
+ * While a stream is open the handle refuses clef_head_forward (CLEF_E_ARG).
+ * Use one HIP stream for a streamed batch, or order the streams. */
+CLEF_API int clef_head_stream_begin(clef_head *h, const clef_head_batch *batch, void *hip_stream);
+CLEF_API int clef_head_stream_rows(clef_head *h, int32_t record, int32_t row0, int32_t nrows, const void *rows,
+                                   void *hip_stream);
+CLEF_API int clef_head_stream_end(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
+                                  int32_t *argmax, void *hip_stream);
+CLEF_API int clef_head_stream_cancel(clef_head *h);
+
 /* Release everything the handle owns.  NULL is ignored. */
 CLEF_API void clef_head_destroy(clef_head *h);
 

@@ -426,6 +426,21 @@ struct clef_head {
   std::vector<hipEvent_t> ev;
   double stage_ms[CLEF_NUM_STAGES] = {};
   int64_t prof_calls = 0;
+  // streamed ingest (clef_head_stream_*): the batch's rows arrive in chunks
+  struct Stream {
+    bool active = false;
+    std::vector<int32_t> tab;                  // the plan's tables (end must describe the same batch)
+    std::vector<int64_t> cu;                   // first staging row of each record
+    std::vector<int32_t> len, received;        // valid rows and rows received per record
+    std::vector<std::vector<int>> rec_tiles;   // plan tile indices of each record, in row order
+    int64_t ntiles = 0, Tpad = 0;
+    size_t off_tiles = 0, off_kvtiles = 0;     // int32 offsets of the tile tables in tab
+    size_t ws_tab = 0, ws_stats = 0, ws_mem = 0, ws_kv = 0, ws_bigpart = 0;   // workspace offsets
+    int split_mem = 1, split_kv = 1;
+    bool f16 = false, gemms = false;
+    void* rows = nullptr;                      // staging rows [T, H], 16-bit elements
+    size_t rows_bytes = 0;
+  } strm;
 };
 
 namespace {
@@ -838,6 +853,7 @@ void clef_head_destroy(clef_head* h) {
     (void)hipEventDestroy(h->staged);
   }
   if (h->ws) (void)hipFree(h->ws);
+  if (h->strm.rows) (void)hipFree(h->strm.rows);
   if (h->tr) (void)hipFree(h->tr);
   if (h->pinned) (void)hipHostFree(h->pinned);
   h->dweights.reset();
@@ -892,25 +908,9 @@ int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) 
   return CLEF_OK;
 }
 
-static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
-                        const clef_head_answers* answers, void* hip_stream) {
-  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
-  const clef_head_config& c = h->cfg;
-  Plan p;
-  int rc = build_plan(c, batch, p, true);
-  if (rc) return rc;
-  if (p.NQ == 0) return CLEF_OK;
-  if (!logits || !probs || !argmax) return fail(CLEF_E_ARG, "output buffer is NULL");
-  int dev_prev = 0;
-  HIPCHK(hipGetDevice(&dev_prev));
-  if (dev_prev != h->device) HIPCHK(hipSetDevice(h->device));
-  struct Restore {
-    int d, p;
-    ~Restore() { if (d != p) (void)hipSetDevice(p); }
-  } restore{h->device, dev_prev};
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-
-  const WsLayout L = ws_layout(c, p);
+// Grow the workspace and the pinned staging to fit the plan, then upload its
+// tables on st (the caller's device is current).
+static int stage_plan(clef_head* h, const Plan& p, const WsLayout& L, hipStream_t st) {
   if (L.total > h->ws_bytes) {
     if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
     HIPCHK(hipDeviceSynchronize());
@@ -931,6 +931,41 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
     if (hipHostMalloc(&h->pinned, want, hipHostMallocDefault) != hipSuccess)
       return fail(CLEF_E_NOMEM, "pinned staging of %zu bytes failed", want);
     h->pinned_bytes = want;
+  }
+  memcpy(h->pinned, p.tab.data(), tab_bytes);
+  HIPCHK(hipMemcpyAsync(static_cast<uint8_t*>(h->ws) + L.tab, h->pinned, tab_bytes, hipMemcpyHostToDevice, st));
+  HIPCHK(hipEventRecord(h->staged, st));
+  h->staged_pending = true;
+  return CLEF_OK;
+}
+
+// streamed: the row statistics, memory and K/V rows of every tile were
+// computed while the rows streamed in (clef_head_stream_rows); only the rest runs.
+static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
+                        const clef_head_answers* answers, void* hip_stream, bool streamed = false) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  if (h->strm.active && !streamed)
+    return fail(CLEF_E_ARG, "a streamed batch is in progress on this handle (clef_head_stream_end first)");
+  const clef_head_config& c = h->cfg;
+  Plan p;
+  int rc = build_plan(c, batch, p, true);
+  if (rc) return rc;
+  if (p.NQ == 0) return CLEF_OK;
+  if (!logits || !probs || !argmax) return fail(CLEF_E_ARG, "output buffer is NULL");
+  int dev_prev = 0;
+  HIPCHK(hipGetDevice(&dev_prev));
+  if (dev_prev != h->device) HIPCHK(hipSetDevice(h->device));
+  struct Restore {
+    int d, p;
+    ~Restore() { if (d != p) (void)hipSetDevice(p); }
+  } restore{h->device, dev_prev};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  const WsLayout L = ws_layout(c, p);
+  if (streamed && L.total > h->ws_bytes) return fail(CLEF_E_ARG, "streamed batch does not fit the staged workspace");
+  {
+    const int rc2 = stage_plan(h, p, L, st);
+    if (rc2) return rc2;
   }
   const int NR = c.routing_layers, NL = c.layers, NQ = p.NQ, NO = p.NO;
   const size_t H = c.hidden_size;
@@ -956,12 +991,8 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
     h->tr_mlp = reinterpret_cast<float*>(t);
   }
 
-  memcpy(h->pinned, p.tab.data(), tab_bytes);
   uint8_t* ws = static_cast<uint8_t*>(h->ws);
   int32_t* dtab = reinterpret_cast<int32_t*>(ws + L.tab);
-  HIPCHK(hipMemcpyAsync(dtab, h->pinned, tab_bytes, hipMemcpyHostToDevice, st));
-  HIPCHK(hipEventRecord(h->staged, st));
-  h->staged_pending = true;
 
   const int* rec = dtab + p.off_rec;
   const int4* tiles = reinterpret_cast<const int4*>(dtab + p.off_tiles);
@@ -1031,7 +1062,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   hipStream_t s2 = fork ? h->side.get() : st;
 
   // step 1: row statistics, pooled vectors, lexical vectors and prior
-  launch_rowstats(st, X, (int)H, p.f16, tiles, p.ntiles, stats, eps);
+  if (!streamed) launch_rowstats(st, X, (int)H, p.f16, tiles, p.ntiles, stats, eps);
   MARK(CLEF_STAGE_ROWSTATS);
   if (fork) {
     HIPCHK(hipEventRecord(h->ev_fork, st));
@@ -1045,7 +1076,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   if (joint) {
     // step 2: memory and K/V of every routing layer (main stream), after the
     // big GEMMs of the group's previous forward
-    if (NR > 0) {
+    if (NR > 0 && !streamed) {
       HeadGroup& g = *h->group;
       if (fork) {
         std::lock_guard<std::mutex> lk(g.mu);
@@ -1160,6 +1191,166 @@ int clef_head_forward_answers(clef_head* h, const clef_head_batch* batch, float*
                               int32_t* argmax, const clef_head_answers* answers, void* hip_stream) {
   if (!answers) return fail(CLEF_E_ARG, "answers is NULL");
   return forward_impl(h, batch, logits, probs, argmax, answers, hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// Streamed ingest.  The batch is planned exactly as clef_head_forward plans its
+// varlen form; rows are copied into handle-owned staging rows as they arrive,
+// and each 256-row tile's row statistics, memory rows and K/V rows are
+// computed as soon as the tile's last row is in, with the same kernels and the
+// same K split as the whole-batch launch, so the result is bit-identical to
+// clef_head_forward over the same rows.
+// ---------------------------------------------------------------------------
+static int stream_plan(clef_head* h, const clef_head_batch* batch, Plan& p) {
+  if (!batch) return fail(CLEF_E_ARG, "batch is NULL");
+  if ((batch->layout & ~CLEF_HIDDEN_F16) != CLEF_VARLEN)
+    return fail(CLEF_E_ARG, "a streamed batch uses the CLEF_VARLEN layout (cu_seqlens)");
+  clef_head_batch b = *batch;
+  b.hidden = h->strm.rows ? h->strm.rows : reinterpret_cast<const void*>(&h->strm);   // placeholder until staged
+  return build_plan(h->cfg, &b, p, true);
+}
+
+int clef_head_stream_begin(clef_head* h, const clef_head_batch* batch, void* hip_stream) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  if (h->strm.active) return fail(CLEF_E_ARG, "a streamed batch is already in progress on this handle");
+  Plan p;
+  int rc = stream_plan(h, batch, p);
+  if (rc) return rc;
+  int dev_prev = 0;
+  HIPCHK(hipGetDevice(&dev_prev));
+  if (dev_prev != h->device) HIPCHK(hipSetDevice(h->device));
+  struct Restore {
+    int d, p;
+    ~Restore() { if (d != p) (void)hipSetDevice(p); }
+  } restore{h->device, dev_prev};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  auto& S = h->strm;
+  const int B = batch->num_records;
+  const size_t H = h->cfg.hidden_size;
+  const size_t need = (size_t)std::max<int64_t>(batch->cu_seqlens[B], 1) * H * 2;
+  if (need > S.rows_bytes) {
+    HIPCHK(hipDeviceSynchronize());
+    if (S.rows) (void)hipFree(S.rows);
+    S.rows = nullptr;
+    S.rows_bytes = 0;
+    if (hipMalloc(&S.rows, need) != hipSuccess) return fail(CLEF_E_NOMEM, "staging rows hipMalloc of %zu bytes failed", need);
+    S.rows_bytes = need;
+  }
+  const WsLayout L = ws_layout(h->cfg, p);
+  rc = stage_plan(h, p, L, st);
+  if (rc) return rc;
+  S.tab = p.tab;
+  S.cu.assign(batch->cu_seqlens, batch->cu_seqlens + B + 1);
+  S.len.resize(B);
+  for (int r = 0; r < B; ++r) S.len[r] = (int32_t)(S.cu[r + 1] - S.cu[r]);
+  S.received.assign(B, 0);
+  S.rec_tiles.assign(B, {});
+  const int4* tl = reinterpret_cast<const int4*>(p.tab.data() + p.off_tiles);
+  for (int i = 0, r = 0; i < p.ntiles; ++i) {   // tiles run in record order; .x is the first staging row
+    while (tl[i].x >= S.cu[r + 1]) ++r;
+    S.rec_tiles[r].push_back(i);
+  }
+  S.ntiles = p.ntiles;
+  S.off_tiles = p.off_tiles;
+  S.off_kvtiles = p.off_kvtiles;
+  S.ws_tab = L.tab;
+  S.ws_stats = L.stats;
+  S.ws_mem = L.mem;
+  S.ws_kv = L.kv;
+  S.ws_bigpart = L.bigpart;
+  S.Tpad = p.Tpad;
+  S.f16 = p.f16;
+  S.gemms = h->w.gate != 0.0f && h->cfg.routing_layers > 0;
+  S.split_mem = big_gemm_split(p.ntiles, D / 256, (int)H);
+  S.split_kv = big_gemm_split(p.ntiles, h->cfg.routing_layers * 8, D);
+  S.active = true;
+  return CLEF_OK;
+}
+
+int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nrows, const void* rows,
+                          void* hip_stream) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  auto& S = h->strm;
+  if (!S.active) return fail(CLEF_E_ARG, "no streamed batch in progress (clef_head_stream_begin first)");
+  if (record < 0 || record >= (int32_t)S.len.size()) return fail(CLEF_E_ARG, "record %d out of range", record);
+  if (nrows < 1 || !rows) return fail(CLEF_E_ARG, "empty chunk or NULL rows");
+  if (row0 != S.received[record])
+    return fail(CLEF_E_ARG, "record %d: chunk starts at row %d, %d rows received so far (rows arrive in order)", record,
+                row0, S.received[record]);
+  if ((int64_t)row0 + nrows > S.len[record])
+    return fail(CLEF_E_LENGTH, "record %d: rows [%d, %d) past its length %d", record, row0, row0 + nrows,
+                S.len[record]);
+  int dev_prev = 0;
+  HIPCHK(hipGetDevice(&dev_prev));
+  if (dev_prev != h->device) HIPCHK(hipSetDevice(h->device));
+  struct Restore {
+    int d, p;
+    ~Restore() { if (d != p) (void)hipSetDevice(p); }
+  } restore{h->device, dev_prev};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const size_t H = h->cfg.hidden_size;
+  const auto& tl = S.rec_tiles[record];
+  if (!tl.empty()) {   // records without questions take no tiles: their rows are never read
+    bf16_t* X = static_cast<bf16_t*>(S.rows);
+    HIPCHK(hipMemcpyAsync(X + (size_t)(S.cu[record] + row0) * H, rows, (size_t)nrows * H * 2,
+                          hipMemcpyDeviceToDevice, st));
+  }
+  const int32_t before = S.received[record];
+  S.received[record] += nrows;
+  // tiles of this record completed by the chunk: tile j holds rows [256 j, min(256 (j + 1), n))
+  if (tl.empty()) return CLEF_OK;
+  const int n = S.len[record];
+  uint8_t* ws = static_cast<uint8_t*>(h->ws);
+  const int4* htiles = reinterpret_cast<const int4*>(S.tab.data() + S.off_tiles);
+  const int4* dtiles = reinterpret_cast<const int4*>(ws + S.ws_tab + S.off_tiles * 4);
+  const int4* dkvtiles = reinterpret_cast<const int4*>(ws + S.ws_tab + S.off_kvtiles * 4);
+  float2* stats = reinterpret_cast<float2*>(ws + S.ws_stats);
+  bf16_t* mem = reinterpret_cast<bf16_t*>(ws + S.ws_mem);
+  bf16_t* kv = reinterpret_cast<bf16_t*>(ws + S.ws_kv);
+  float* bigpart = reinterpret_cast<float*>(ws + S.ws_bigpart);
+  const bf16_t* X = static_cast<const bf16_t*>(S.rows);
+  const Weights& W = h->w;
+  for (int j = before / 256; j < (int)tl.size(); ++j) {
+    const int end = std::min(256 * (j + 1), n);
+    if (S.received[record] < end) break;
+    if (before >= end) continue;   // completed by an earlier chunk
+    const int i = tl[j];
+    const long long prow = htiles[i].y;
+    launch_rowstats(st, X, (int)H, S.f16, dtiles + i, 1, stats, h->cfg.ln_eps);
+    if (S.gemms) {
+      launch_gemm_mem(st, X, (int)H, S.f16, dtiles + i, 1, S.f16 ? W.Wmem16 : W.Wmem, stats,
+                      S.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, S.Tpad, S.split_mem, prow);
+      launch_gemm_kv(st, mem, dkvtiles + i, 1, W.Wkv, W.bkv, h->cfg.routing_layers, kv, S.Tpad, bigpart, S.split_kv,
+                     prow);
+    }
+  }
+  HIPCHK(hipGetLastError());
+  return CLEF_OK;
+}
+
+int clef_head_stream_end(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
+                         void* hip_stream) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  auto& S = h->strm;
+  if (!S.active) return fail(CLEF_E_ARG, "no streamed batch in progress (clef_head_stream_begin first)");
+  for (size_t r = 0; r < S.len.size(); ++r)
+    if (S.received[r] != S.len[r])
+      return fail(CLEF_E_LENGTH, "record %zu: %d of %d rows received", r, S.received[r], S.len[r]);
+  Plan p;
+  int rc = stream_plan(h, batch, p);
+  if (rc) return rc;
+  if (p.tab != S.tab) return fail(CLEF_E_ARG, "the batch differs from the one clef_head_stream_begin planned");
+  clef_head_batch b = *batch;
+  b.hidden = S.rows;
+  rc = forward_impl(h, &b, logits, probs, argmax, nullptr, hip_stream, true);
+  if (rc == CLEF_OK) S.active = false;
+  return rc;
+}
+
+int clef_head_stream_cancel(clef_head* h) {
+  if (!h) return fail(CLEF_E_ARG, "handle is NULL");
+  h->strm.active = false;
+  return CLEF_OK;
 }
 
 }  // extern "C"

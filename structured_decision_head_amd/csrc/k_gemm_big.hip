@@ -423,12 +423,13 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 // epilogue m = rstd (sum - mu c) + d (the same arithmetic as the unsplit
 // epilogue); every row of the packed row space is written.  8 columns per thread.
 __global__ __launch_bounds__(256) void k_mem_reduce(const float* __restrict__ part, int nsplit, long long Tpad,
+                                                    long long row0, long long nrows,
                                                     const float2* __restrict__ stats, const float* __restrict__ c,
                                                     const float* __restrict__ d, bf16_t* __restrict__ out) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;   // 8-column group
-  const long long row = i >> 7;
+  if ((i >> 7) >= nrows) return;
+  const long long row = row0 + (i >> 7);
   const int col = (int)(i & 127) * 8;
-  if (row >= Tpad) return;
   float a[8];
   const float* p = part + row * 1024 + col;
   {
@@ -456,9 +457,10 @@ __global__ __launch_bounds__(256) void k_mem_reduce(const float* __restrict__ pa
 // (32-row block, head of one K or V): the sums are staged in LDS, then
 // written as 4 KB of contiguous memory.
 __global__ __launch_bounds__(256) void k_kv_reduce(const float* __restrict__ part, int nsplit, long long Tpad,
-                                                   const float* __restrict__ bias, bf16_t* __restrict__ kv) {
+                                                   long long rbase, const float* __restrict__ bias,
+                                                   bf16_t* __restrict__ kv) {
   __shared__ float tile[32][65];
-  const long long row0 = (long long)blockIdx.x * 32;
+  const long long row0 = rbase + (long long)blockIdx.x * 32;
   const int hc = blockIdx.y;                 // 64-column group: layer r = hc / 32, V if (hc / 16) & 1
   const int N = gridDim.y * 64;
   const int t = threadIdx.x, r = t >> 3, c8 = (t & 7) * 8;
@@ -508,10 +510,10 @@ int big_gemm_split(int ntiles, int ntn, int K) {
 
 void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
                      const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
-                     float* part, long long Tpad) {
+                     float* part, long long Tpad, int split, long long row0) {
   if (ntiles == 0) return;
   const int ntn = 1024 / BN;
-  const int S = part ? big_gemm_split(ntiles, ntn, H) : 1;
+  const int S = !part ? 1 : split > 0 ? split : big_gemm_split(ntiles, ntn, H);
   const dim3 grid(ntiles * ntn * S);
   if (S > 1) {
     if (f16) {
@@ -521,8 +523,9 @@ void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, cons
       hipLaunchKernelGGL(k_gemm256<EpiPart<false>>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, S,
                          EpiPart<false>{part, Tpad, 1024});
     }
-    hipLaunchKernelGGL(k_mem_reduce, dim3((unsigned)((Tpad * 128 + 255) / 256)), dim3(256), 0, st, part, S, Tpad,
-                       stats, c, d, mem);
+    const long long nrows = (long long)ntiles * BM;
+    hipLaunchKernelGGL(k_mem_reduce, dim3((unsigned)((nrows * 128 + 255) / 256)), dim3(256), 0, st, part, S, Tpad,
+                       row0, nrows, stats, c, d, mem);
     return;
   }
   EpiMem epi{stats, c, d, mem};
@@ -536,15 +539,16 @@ void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, cons
 }
 
 void launch_gemm_kv(hipStream_t st, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
-                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part) {
+                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part, int split,
+                    long long row0) {
   if (ntiles == 0 || n_layers == 0) return;
   const int ntn = n_layers * 2048 / BN;
-  const int S = part ? big_gemm_split(ntiles, ntn, 1024) : 1;
+  const int S = !part ? 1 : split > 0 ? split : big_gemm_split(ntiles, ntn, 1024);
   if (S > 1) {
     hipLaunchKernelGGL(k_gemm256<EpiPart<false>>, dim3(ntiles * ntn * S), dim3(256), 0, st, mem, 1024, tiles, ntn,
                        Wkv, 1024, S, EpiPart<false>{part, Tpad, n_layers * 2048});
-    hipLaunchKernelGGL(k_kv_reduce, dim3((unsigned)(Tpad / 32), n_layers * 32), dim3(256), 0, st, part, S, Tpad, bkv,
-                       kv);
+    hipLaunchKernelGGL(k_kv_reduce, dim3((unsigned)(ntiles * (BM / 32)), n_layers * 32), dim3(256), 0, st, part, S,
+                       Tpad, row0, bkv, kv);
     return;
   }
   EpiKV epi{bkv, kv, Tpad};

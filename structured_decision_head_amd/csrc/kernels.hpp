@@ -34,12 +34,17 @@ void launch_lex_prior(hipStream_t, const bf16_t* E, int H, const int4* ent, int 
 // split * Tpad * N floats of workspace.
 int big_gemm_split(int ntiles, int ntn, int K);
 // f16: hidden and Wm are fp16 (fp16 MFMA), else both bf16.  part: split-K
-// workspace (null: never split); Tpad = ntiles * 256 rows.
+// workspace (null: never split); Tpad: rows of the packed row space (the
+// partial sums of slice s start at row s * Tpad).  split > 0 forces that
+// many slices (a launch over some of a batch's tiles that must sum like the
+// whole batch's launch); row0: first packed row of the launch's tiles, which
+// must be consecutive.
 void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
                      const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
-                     float* part, long long Tpad);
+                     float* part, long long Tpad, int split = 0, long long row0 = 0);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
-                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part);
+                    const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part, int split = 0,
+                    long long row0 = 0);
 
 // ---------------------------------------------------------------------------
 // small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue

@@ -1,0 +1,142 @@
+"""GPU tests of streamed ingest (clef_head_stream_begin / _rows / _end): rows
+arrive in chunks as the backbone's chunked prefill produces them (CoreML
+conversion metadata page of clef-flash, "decision.readout": a record runs as
+consecutive calls of 64 positions).  Every 256-row tile is processed as soon
+as its rows are in, with the same kernels and K split as the whole-batch
+launch, so the outputs must equal clef_head_forward's on the same rows bit
+for bit; they are also checked against the oracle.  Host-side errors (rows
+out of order, rows missing at the end, a forward while a stream is open) are
+refused before anything runs."""
+import numpy as np
+import pytest
+
+from parity import compare, local_offsets, oracle_outputs, say, select
+from structured_decision_head_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from structured_decision_head_amd import clefhead
+    clefhead.load()
+    return torch
+
+
+def _stream(torch, r, chunk, interleave=True):
+    """Feed r.hidden (varlen [T, H] on the device) in chunks of `chunk` rows:
+    chunk k of every record before chunk k + 1 of any (a batched prefill), or
+    record after record."""
+    from structured_decision_head_amd import clefhead as C
+    b = r.batch
+    st = torch.cuda.current_stream().cuda_stream
+    C.clef_head_stream_begin(r.handle, r.args, st)
+    cu = b.cu_seqlens()
+    H = b.H
+    pos = [0] * b.B
+    base = r.hidden.data_ptr()
+    order = []
+    if interleave:
+        while any(pos[k] < b.lengths[k] for k in range(b.B)):
+            for k in range(b.B):
+                if pos[k] < b.lengths[k]:
+                    n = int(min(chunk, b.lengths[k] - pos[k]))
+                    order.append((k, pos[k], n))
+                    pos[k] += n
+    else:
+        for k in range(b.B):
+            for p0 in range(0, int(b.lengths[k]), chunk):
+                order.append((k, p0, int(min(chunk, b.lengths[k] - p0))))
+    for k, p0, n in order:
+        C.clef_head_stream_rows(r.handle, k, p0, n, base + (int(cu[k]) + p0) * H * 2, st)
+    C.clef_head_stream_end(r.handle, r.args, r.logits.data_ptr(), r.probs.data_ptr(), r.argmax.data_ptr(), st)
+    return r.outputs()
+
+
+def _run(torch, case, chunk=64, interleave=True):
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd.runner import HeadRunner
+    r = HeadRunner(case)
+    r.set_batch(None, C.CLEF_VARLEN)
+    r.forward()
+    ref = r.outputs()
+    out = _stream(torch, r, chunk, interleave)
+    r.close()
+    for a, c in zip(ref, out):
+        assert np.array_equal(a, c), "streamed outputs differ from the whole-batch forward"
+    return out
+
+
+def _check(case, out, name):
+    b = case.batch
+    recs = [k for k in range(b.B) if int(b.q_offsets[k + 1]) > int(b.q_offsets[k])]
+    compare(name, select(b, recs, *out), oracle_outputs(case, records=recs), local_offsets(b, recs))
+
+
+def test_stream_ragged_batch_64_row_chunks(torch_gpu):
+    case = synth.make_case(synth.config_spec(1, B=3, L=1100, lengths=("uniform", 600, 1100),
+                                             head=synth.HeadConfig(vocab_size=4096)))
+    say(f"case streamed ragged batch, 64-row chunks interleaved: lengths={case.batch.lengths.tolist()}")
+    _check(case, _run(torch_gpu, case, 64), "streamed ragged")
+
+
+def test_stream_single_record_split_k(torch_gpu):
+    """One 160-row record: its only tile completes with the last chunk, and
+    the big GEMMs run split (8 and 4 K slices) as in the whole-batch launch."""
+    case = synth.config_case(0)
+    say("case streamed single record, 64-row chunks")
+    _check(case, _run(torch_gpu, case, 64), "streamed single record")
+
+
+def test_stream_fp16_uneven_chunks_record_order(torch_gpu):
+    """fp16 rows, 100-row chunks (tiles complete mid-chunk), record after
+    record, and a record without questions in the middle."""
+    from test_gpu_edges import drop_questions
+    spec = synth.config_spec(1, B=4, L=900, lengths=("uniform", 300, 900), head=synth.HeadConfig(vocab_size=4096),
+                             hidden_dtype="f16")
+    case = synth.make_case(spec)
+    import dataclasses
+    case = dataclasses.replace(case, batch=drop_questions(case.batch, 1))
+    say(f"case streamed fp16, 100-row chunks: lengths={case.batch.lengths.tolist()}")
+    _check(case, _run(torch_gpu, case, 100, interleave=False), "streamed fp16")
+
+
+def test_stream_errors_are_refused(torch_gpu):
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd.runner import HeadRunner
+    case = synth.make_case(synth.config_spec(1, B=2, L=700, lengths=("uniform", 500, 700),
+                                             head=synth.HeadConfig(vocab_size=4096)))
+    say("case streamed errors")
+    r = HeadRunner(case)
+    r.set_batch(None, C.CLEF_VARLEN)
+    st = torch_gpu.cuda.current_stream().cuda_stream
+    H, base = case.batch.H, r.hidden.data_ptr()
+
+    def code(fn, *a):
+        with pytest.raises(C.ClefError) as e:
+            fn(*a)
+        return e.value.code
+
+    assert code(C.clef_head_stream_rows, r.handle, 0, 0, 64, base, st) == C.CLEF_E_ARG        # no stream open
+    padded = C.BatchArgs(case.batch, base, C.CLEF_PADDED)
+    assert code(C.clef_head_stream_begin, r.handle, padded, st) == C.CLEF_E_ARG               # varlen only
+    C.clef_head_stream_begin(r.handle, r.args, st)
+    assert code(C.clef_head_stream_begin, r.handle, r.args, st) == C.CLEF_E_ARG               # already open
+    assert code(C.clef_head_stream_rows, r.handle, 0, 64, 64, base, st) == C.CLEF_E_ARG       # out of order
+    n0 = int(case.batch.lengths[0])
+    assert code(C.clef_head_stream_rows, r.handle, 0, 0, n0 + 1, base, st) == C.CLEF_E_LENGTH  # past the end
+    assert code(C.clef_head_stream_rows, r.handle, 2, 0, 64, base, st) == C.CLEF_E_ARG        # no such record
+    C.clef_head_stream_rows(r.handle, 0, 0, 64, base, st)
+    assert code(C.clef_head_stream_end, r.handle, r.args, r.logits.data_ptr(), r.probs.data_ptr(),
+                r.argmax.data_ptr(), st) == C.CLEF_E_LENGTH                                   # rows missing
+    assert code(r.forward) == C.CLEF_E_ARG                                                    # stream open
+    C.clef_head_stream_cancel(r.handle)
+    r.forward()                                                                               # handle usable again
+    ref = r.outputs()
+    out = _stream(torch_gpu, r, 64)
+    for a, c in zip(ref, out):
+        assert np.array_equal(a, c)
+    r.close()
