@@ -127,13 +127,15 @@ def sigmoid(x: float) -> float:
 
 
 def attention(q_in: np.ndarray, kv_in: np.ndarray, p: Dict[str, np.ndarray], prefix: str,
-              heads: int) -> np.ndarray:
+              heads: int, names=("q", "k", "v", "o")) -> np.ndarray:
     """Multi-head attention of the rows of ``q_in`` over the rows of ``kv_in``:
     Q/K/V projections with biases, per-head softmax(Q K^T / sqrt(d)), V mix,
-    concatenation over heads, output projection with bias."""
-    q = linear(q_in, p[prefix + ".q.w"], p[prefix + ".q.b"])
-    k = linear(kv_in, p[prefix + ".k.w"], p[prefix + ".k.b"])
-    v = linear(kv_in, p[prefix + ".v.w"], p[prefix + ".v.b"])
+    concatenation over heads, output projection with bias.  ``names`` are the
+    four projections' weight names under ``prefix``."""
+    nq_, nk_, nv_, no_ = (prefix + "." + n for n in names)
+    q = linear(q_in, p[nq_ + ".w"], p[nq_ + ".b"])
+    k = linear(kv_in, p[nk_ + ".w"], p[nk_ + ".b"])
+    v = linear(kv_in, p[nv_ + ".w"], p[nv_ + ".b"])
     D = q.shape[-1]
     d = D // heads
     outs = []
@@ -141,7 +143,7 @@ def attention(q_in: np.ndarray, kv_in: np.ndarray, p: Dict[str, np.ndarray], pre
         sl = slice(j * d, (j + 1) * d)
         a = softmax(q[:, sl] @ k[:, sl].T / math.sqrt(d))
         outs.append(a @ v[:, sl])
-    return linear(np.concatenate(outs, axis=1), p[prefix + ".o.w"], p[prefix + ".o.b"])
+    return linear(np.concatenate(outs, axis=1), p[no_ + ".w"], p[no_ + ".b"])
 
 
 def ffn(x: np.ndarray, p: Dict[str, np.ndarray], prefix: str) -> np.ndarray:
@@ -163,10 +165,19 @@ def routing_layer(u: np.ndarray, memory: np.ndarray, p: Dict[str, np.ndarray], p
 
 
 def field_layer(f: np.ndarray, p: Dict[str, np.ndarray], prefix: str, heads: int,
-                eps: float) -> np.ndarray:
-    """Field transformer layer ([P4] step 3): fields of one record see each other."""
+                eps: float, memory: np.ndarray = None) -> np.ndarray:
+    """Field transformer layer ([P4] step 3): fields of one record see each other.
+
+    With ``memory`` (the decoder-layer reading of the field stack: [P4] §三
+    step 3 and [P3] §3.2 call the field layers transformer decoder layers) a
+    pre-LN cross-attention of the fields over the record's memory rows sits
+    between the self-attention and the FFN, as in a standard decoder layer;
+    its weights are ``xln`` (norm) and ``xq, xk, xv, xo`` (projections)."""
     a = layer_norm(f, p[prefix + ".ln1.w"], p[prefix + ".ln1.b"], eps)
     f = f + attention(a, a, p, prefix, heads)
+    if memory is not None:
+        a = layer_norm(f, p[prefix + ".xln.w"], p[prefix + ".xln.b"], eps)
+        f = f + attention(a, memory, p, prefix, heads, names=("xq", "xk", "xv", "xo"))
     a = layer_norm(f, p[prefix + ".ln2.w"], p[prefix + ".ln2.b"], eps)
     return f + ffn(a, p, prefix)
 
@@ -222,8 +233,9 @@ def forward_record(p: Dict[str, np.ndarray], head, hidden: np.ndarray,
         beta = softmax(s[o0:o1])
         f[i] = qv[i] + beta @ u[o0:o1] + gp + p["type_emb"][int(q_type[i])]
     f0 = f.copy()
+    cross = memory if getattr(head, "field_cross_attention", 0) else None
     for l in range(head.layers):
-        f = field_layer(f, p, f"field.{l}", heads, eps)
+        f = field_layer(f, p, f"field.{l}", heads, eps, cross)
 
     # step 4: scoring
     fo = f[opt_q]

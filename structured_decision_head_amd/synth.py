@@ -76,6 +76,7 @@ class HeadConfig:
     vocab_size: int = 248320
     num_types: int = 3
     ln_eps: float = 1e-5
+    field_cross_attention: int = 0   # 1: field layers also cross-attend over the record's memory rows
 
 
 def weight_specs(c: HeadConfig) -> List[Tuple[str, Tuple[int, ...], str, int]]:
@@ -100,6 +101,12 @@ def weight_specs(c: HeadConfig) -> List[Tuple[str, Tuple[int, ...], str, int]]:
     s += [("score.w1", (D, 4 * D), "lin", 4 * D), ("score.b1", (D,), "lin", 4 * D),
           ("score.w2", (D,), "lin", D), ("score.b2", (1,), "lin", D),
           ("gate_logit", (1,), "gate", 1), ("joint_scale", (1,), "scale", 1)]
+    if c.field_cross_attention:   # appended, so every other tensor keeps its seed
+        for l in range(c.layers):
+            p = f"field.{l}"
+            s += [(p + ".xln.w", (D,), "ln_w", D), (p + ".xln.b", (D,), "ln_b", D)]
+            for m in ("xq", "xk", "xv", "xo"):
+                s += [(f"{p}.{m}.w", (D, D), "lin", D), (f"{p}.{m}.b", (D,), "lin", D)]
     return s
 
 

@@ -69,10 +69,10 @@ def _softmax(v):
     return [x / s for x in e]
 
 
-def _mha(qrows, kvrows, P, pre, heads):
-    Q = [_lin(r, P[pre + ".q.w"], P[pre + ".q.b"]) for r in qrows]
-    K = [_lin(r, P[pre + ".k.w"], P[pre + ".k.b"]) for r in kvrows]
-    V = [_lin(r, P[pre + ".v.w"], P[pre + ".v.b"]) for r in kvrows]
+def _mha(qrows, kvrows, P, pre, heads, nm=("q", "k", "v", "o")):
+    Q = [_lin(r, P[f"{pre}.{nm[0]}.w"], P[f"{pre}.{nm[0]}.b"]) for r in qrows]
+    K = [_lin(r, P[f"{pre}.{nm[1]}.w"], P[f"{pre}.{nm[1]}.b"]) for r in kvrows]
+    V = [_lin(r, P[f"{pre}.{nm[2]}.w"], P[f"{pre}.{nm[2]}.b"]) for r in kvrows]
     D = len(Q[0])
     d = D // heads
     out = []
@@ -91,14 +91,18 @@ def _mha(qrows, kvrows, P, pre, heads):
                 for i in range(len(V)):
                     acc += a[i] * V[i][t]
                 cat.append(acc)
-        out.append(_lin(cat, P[pre + ".o.w"], P[pre + ".o.b"]))
+        out.append(_lin(cat, P[f"{pre}.{nm[3]}.w"], P[f"{pre}.{nm[3]}.b"]))
     return out
 
 
-def _block(rows, mem, P, pre, heads, eps):
+def _block(rows, mem, P, pre, heads, eps, xmem=None):
     a = [_ln(r, P[pre + ".ln1.w"], P[pre + ".ln1.b"], eps) for r in rows]
     att = _mha(a, a if mem is None else mem, P, pre, heads)
     rows = [[rows[i][t] + att[i][t] for t in range(len(rows[i]))] for i in range(len(rows))]
+    if xmem is not None:   # decoder-layer variant: cross-attention over the memory rows
+        a = [_ln(r, P[pre + ".xln.w"], P[pre + ".xln.b"], eps) for r in rows]
+        att = _mha(a, xmem, P, pre, heads, ("xq", "xk", "xv", "xo"))
+        rows = [[rows[i][t] + att[i][t] for t in range(len(rows[i]))] for i in range(len(rows))]
     out = []
     for r in rows:
         a = _ln(r, P[pre + ".ln2.w"], P[pre + ".ln2.b"], eps)
@@ -172,8 +176,9 @@ def brute_record(weights, head, hidden_bits, q_type, q_span, o_offsets, o_span, 
                 s += beta[j] * U[k][t]
             row.append(qv[t] + s + gp[t] + te[t])
         Fv.append(row)
+    xmem = MEM if getattr(head, "field_cross_attention", 0) else None
     for l in range(head.layers):
-        Fv = _block(Fv, None, P, f"field.{l}", heads, eps)
+        Fv = _block(Fv, None, P, f"field.{l}", heads, eps, xmem)
     gate = 1.0 / (1.0 + math.exp(-P["gate_logit"][0])) if P["gate_logit"][0] > -745 else 0.0
     lam = P["joint_scale"][0]
     logits = []
