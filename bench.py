@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--in-flight", type=int, default=2, help="batches in flight (heads sharing weights)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--field-cross-attention", action="store_true",
+                    help="decoder-layer reading of the field layers (cross-attention over the memory rows)")
     ap.add_argument("--hidden", choices=("bf16", "f16"), default="bf16",
                     help="element type of the hidden states (f16: the CoreML packaging's fp16 hidden)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,7 +109,8 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
         return
     t = time.time()
-    case = synth.config_case(args.config, hidden_dtype=args.hidden)
+    case = synth.config_case(args.config, hidden_dtype=args.hidden,
+                             field_cross_attention=int(args.field_cross_attention))
     b = case.batch
     H, D = case.head.hidden_size, case.head.width
     T = int(b.lengths.sum())
@@ -256,7 +259,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if args.hidden == "bf16" else "f16 hidden, bf16 weights",
         "data": "synthetic (seeded; random-init head weights, N(0,1) hidden states, N(0,0.02) lexical table)",
-        "config": {"workload": WORKLOADS[args.config] + ("" if args.hidden == "bf16" else ", fp16 hidden states"),
+        "config": {"workload": WORKLOADS[args.config] + ("" if args.hidden == "bf16" else ", fp16 hidden states")
+                   + (", decoder-layer fields" if args.field_cross_attention else ""),
                    "global_batch": int(b.B),
                    "seq_len": int(b.L), "valid_rows": T, "questions": int(b.NQ), "options": int(b.NO)},
         "roofline": roofline,

@@ -80,10 +80,18 @@ typedef struct clef_head clef_head;   /* opaque handle */
 /* Head hyper-parameters (the keys of joint_head_config.json the pages list).
  * The kernels are built for width 1024, 16 heads, feedforward 4096,
  * num_types 3, hidden_size a multiple of 512 up to 8192; routing_layers and
- * layers may be any count >= 0.  ln_eps is the epsilon of every LayerNorm. */
+ * layers may be any count >= 0.  ln_eps is the epsilon of every LayerNorm.
+ * field_cross_attention selects the reading of the field layers: 0 = pre-LN
+ * self-attention across the record's fields + FFN; 1 = the decoder-layer
+ * reading (clef-4bit page §三 step 3 and the architecture page §3.2 call them
+ * transformer decoder layers): a pre-LN cross-attention of the fields over
+ * the record's memory rows between the self-attention and the FFN, with the
+ * extra weights P.xln.{w,b}[D], P.{xq,xk,xv,xo}.w[D,D], .b[D] per field layer
+ * P, listed after all others. */
 typedef struct {
   int32_t hidden_size, width, heads, routing_layers, layers, feedforward, vocab_size, num_types;
   float ln_eps;
+  int32_t field_cross_attention;
 } clef_head_config;
 
 /* One named head tensor in host memory.  Linear weights use the [out, in]

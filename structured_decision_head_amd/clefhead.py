@@ -42,7 +42,8 @@ class ClefError(RuntimeError):
 class clef_head_config(ctypes.Structure):
     _fields_ = [("hidden_size", ctypes.c_int32), ("width", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("routing_layers", ctypes.c_int32), ("layers", ctypes.c_int32), ("feedforward", ctypes.c_int32),
-                ("vocab_size", ctypes.c_int32), ("num_types", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+                ("vocab_size", ctypes.c_int32), ("num_types", ctypes.c_int32), ("ln_eps", ctypes.c_float),
+                ("field_cross_attention", ctypes.c_int32)]
 
 
 class clef_head_weight(ctypes.Structure):
@@ -117,7 +118,8 @@ def _ptr(a: Optional[np.ndarray]):
 def make_config(head) -> clef_head_config:
     """From any object with the config attribute names (e.g. synth.HeadConfig)."""
     return clef_head_config(head.hidden_size, head.width, head.heads, head.routing_layers, head.layers,
-                            head.feedforward, head.vocab_size, head.num_types, head.ln_eps)
+                            head.feedforward, head.vocab_size, head.num_types, head.ln_eps,
+                            int(getattr(head, "field_cross_attention", 0)))
 
 
 class BatchArgs:

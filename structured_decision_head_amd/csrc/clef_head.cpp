@@ -123,6 +123,16 @@ std::vector<WSpec> weight_list(const clef_head_config& c) {
   add("score.b2", 1);
   add("gate_logit", 1, CLEF_F32);
   add("joint_scale", 1, CLEF_F32);
+  if (c.field_cross_attention)   // decoder-layer field variant: appended after everything else
+    for (int l = 0; l < c.layers; ++l) {
+      const std::string p = "field." + std::to_string(l);
+      add(p + ".xln.w", d);
+      add(p + ".xln.b", d);
+      for (const char* m : {"xq", "xk", "xv", "xo"}) {
+        add(p + "." + m + ".w", d * d);
+        add(p + "." + m + ".b", d);
+      }
+    }
   return s;
 }
 
@@ -131,6 +141,8 @@ int check_config(const clef_head_config* c) {
   if (c->hidden_size <= 0 || c->width <= 0 || c->heads <= 0 || c->feedforward <= 0 || c->vocab_size <= 0 ||
       c->num_types <= 0 || c->routing_layers < 0 || c->layers < 0 || !(c->ln_eps > 0.f))
     return fail(CLEF_E_ARG, "config has a non-positive size or epsilon");
+  if (c->field_cross_attention != 0 && c->field_cross_attention != 1)
+    return fail(CLEF_E_ARG, "field_cross_attention must be 0 or 1 (got %d)", c->field_cross_attention);
   if (c->width != D || c->heads != NH || c->feedforward != F)
     return fail(CLEF_E_UNSUPPORTED, "kernels are built for width 1024, 16 heads, feedforward 4096 (got %d, %d, %d)",
                 c->width, c->heads, c->feedforward);
@@ -152,6 +164,10 @@ struct Plan {
   std::vector<int32_t> tab;   // all int32 tables, back to back
   size_t off_rec = 0, off_tiles = 0, off_kvtiles = 0, off_pool = 0, off_lex = 0, off_ids = 0, off_optq = 0,
          off_optrec = 0, off_qrec = 0, off_qtype = 0, off_ooff = 0, off_items = 0;
+  // decoder-layer field variant: cross-attention work of the fields over the memory rows
+  int64_t Ptot_f = 0;
+  int nfitems = 0;
+  size_t off_frec = 0, off_fitems = 0;
   std::vector<int32_t> span_rows;   // [NQ + NO + B][2] packed-row ranges (for clef_head_span_rows)
 };
 
@@ -260,9 +276,9 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
   if (!tables || NQ == 0) return CLEF_OK;
 
   // active records (with questions), their padded row bases and chunking
-  std::vector<int32_t> rec, tiles, kvtiles, pool, lex, ids, optq, optrec, qrec, qtype, ooff, items;
+  std::vector<int32_t> rec, tiles, kvtiles, pool, lex, ids, optq, optrec, qrec, qtype, ooff, items, frec, fitems;
   std::vector<int> act_of(B, -1);
-  int64_t kv0 = 0, pbase = 0;
+  int64_t kv0 = 0, pbase = 0, pbase_f = 0;
   int nact = 0;
   auto attn_waves = [&](int64_t ch) {
     int64_t w = 0;
@@ -290,10 +306,18 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
     }
     for (int ch = 0; ch < nc; ++ch)
       for (int qb = 0; qb < no; qb += 32) items.insert(items.end(), {nact, ch, qb, 0});
+    if (c.field_cross_attention) {   // the record's fields as the queries of the same attention kernels
+      frec.insert(frec.end(), {int32_t(kv0), int32_t(len[r]), q0, nq, int32_t(pbase_f), nc, q0, nq});
+      for (int ch = 0; ch < nc; ++ch)
+        for (int qb = 0; qb < nq; qb += 32) fitems.insert(fitems.end(), {nact, ch, qb, 0});
+      pbase_f += (int64_t)nq * nc;
+    }
     kv0 += ceil_div(len[r], TILE) * TILE;
     pbase += (int64_t)no * nc;
     ++nact;
   }
+  p.Ptot_f = pbase_f;
+  p.nfitems = (int)fitems.size() / 4;
   if (kv0 > INT32_MAX / 2 || pbase * 64 * NH > INT64_C(1) << 40)
     return fail(CLEF_E_UNSUPPORTED, "batch too large for 32-bit row indices");
   p.nact = nact;
@@ -355,6 +379,8 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
   p.off_qtype = put(qtype);
   p.off_ooff = put(ooff);
   p.off_items = put(items);
+  p.off_frec = put(frec);
+  p.off_fitems = put(fitems);
   while (p.tab.size() % 4) p.tab.push_back(0);
   return CLEF_OK;
 }
@@ -365,11 +391,16 @@ int build_plan(const clef_head_config& c, const clef_head_batch* b, Plan& p, boo
 struct Layer {
   const float *ln1g, *ln1b, *ln2g, *ln2b, *bq, *bo, *b1, *b2, *bqkv;
   const bf16_t *Wq, *Wo, *W1, *W2, *Wqkv;
+  // decoder-layer field variant: cross-attention norm, query and output maps
+  const float *xlng = nullptr, *xlnb = nullptr, *bxq = nullptr, *bxo = nullptr;
+  const bf16_t *Wxq = nullptr, *Wxo = nullptr;
 };
 
 struct Weights {
   const float *lnin_g, *lnin_b, *cmem, *dmem, *cmem16, *ba7, *bqq, *bg, *temb, *sw, *bkv, *bs1, *ws2;
   const bf16_t *Wmem, *Wmem16, *Wa7, *Wqq, *Wg, *Wkv, *Ws1;   // Wmem16 holds fp16 bits
+  const bf16_t* Wfkv = nullptr;   // decoder-layer field variant: cross K/V of every field layer, stacked
+  const float* bfkv = nullptr;
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -436,8 +467,9 @@ struct clef_head {
     int64_t ntiles = 0, Tpad = 0;
     size_t off_tiles = 0, off_kvtiles = 0;     // int32 offsets of the tile tables in tab
     size_t ws_tab = 0, ws_stats = 0, ws_mem = 0, ws_kv = 0, ws_bigpart = 0;   // workspace offsets
-    int split_mem = 1, split_kv = 1;
-    bool f16 = false, gemms = false;
+    int split_mem = 1, split_kv = 1, split_fkv = 1;
+    size_t ws_fkv = 0;
+    bool f16 = false, gemms = false, cross = false;
     void* rows = nullptr;                      // staging rows [T, H], 16-bit elements
     size_t rows_bytes = 0;
   } strm;
@@ -620,6 +652,28 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     put_bf(bf(p + ".ffn2.w"), (size_t)D * F, &L.W2);
     put_f(tof(p + ".ffn2.b"), &L.b2);
   }
+  if (c.field_cross_attention && NL > 0) {
+    // cross K/V of every field layer stacked like the routing ones: [K_0; V_0; K_1; V_1; ...]
+    std::vector<uint16_t> Wf((size_t)NL * 2 * D * D);
+    std::vector<float> bfv((size_t)NL * 2 * D);
+    for (int l = 0; l < NL; ++l) {
+      const std::string p = "field." + std::to_string(l);
+      memcpy(&Wf[(size_t)(2 * l) * D * D], bf(p + ".xk.w"), (size_t)D * D * 2);
+      memcpy(&Wf[(size_t)(2 * l + 1) * D * D], bf(p + ".xv.w"), (size_t)D * D * 2);
+      const auto bk = tof(p + ".xk.b"), bv = tof(p + ".xv.b");
+      std::copy(bk.begin(), bk.end(), bfv.begin() + (size_t)(2 * l) * D);
+      std::copy(bv.begin(), bv.end(), bfv.begin() + (size_t)(2 * l + 1) * D);
+      Layer& L = W.field[l];
+      put_f(tof(p + ".xln.w"), &L.xlng);
+      put_f(tof(p + ".xln.b"), &L.xlnb);
+      put_bf(bf(p + ".xq.w"), (size_t)D * D, &L.Wxq);
+      put_f(tof(p + ".xq.b"), &L.bxq);
+      put_bf(bf(p + ".xo.w"), (size_t)D * D, &L.Wxo);
+      put_f(tof(p + ".xo.b"), &L.bxo);
+    }
+    put_bf(Wf.data(), Wf.size(), &W.Wfkv);
+    put_f(bfv, &W.bfkv);
+  }
   put_bf(bf("score.w1"), (size_t)D * 4 * D, &W.Ws1);
   put_f(tof("score.b1"), &W.bs1);
   put_f(tof("score.w2"), &W.ws2);
@@ -653,7 +707,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 
 // workspace layout for one plan
 struct WsLayout {
-  size_t tab, stats, pooled, ebar, prior, mem, kv, bigpart, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats,
+  size_t tab, stats, pooled, ebar, prior, mem, kv, fkv, bigpart, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats,
       fattn, pm, pl, po, part, total;
 };
 
@@ -669,11 +723,15 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.prior = take(NO * 4);
   L.mem = take(Tp * D * 2);
   L.kv = take(NR * 2 * NH * Tp * 64 * 2);
+  const size_t NLx = c.field_cross_attention ? (size_t)c.layers : 0;   // field layers with cross-attention
+  L.fkv = take(NLx * 2 * NH * Tp * 64 * 2);
   // split-K partial sums of the big GEMMs (few row tiles only; the memory and
   // K/V GEMMs run one after the other on one stream and share the region)
   {
     const size_t sm = big_gemm_split(p.ntiles, D / 256, (int)H), skv = big_gemm_split(p.ntiles, (int)NR * 8, D);
-    const size_t bytes = std::max(sm > 1 ? sm * Tp * D * 4 : 0, (NR > 0 && skv > 1) ? skv * Tp * NR * 2 * D * 4 : 0);
+    const size_t sf = big_gemm_split(p.ntiles, (int)NLx * 8, D);
+    size_t bytes = std::max(sm > 1 ? sm * Tp * D * 4 : 0, (NR > 0 && skv > 1) ? skv * Tp * NR * 2 * D * 4 : 0);
+    bytes = std::max(bytes, (NLx > 0 && sf > 1) ? sf * Tp * NLx * 2 * D * 4 : 0);
     L.bigpart = take(bytes);
   }
   L.u = take(NO * D * 4);
@@ -687,9 +745,10 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.f = take(NQ * D * 4);
   L.fstats = take(NQ * 8);
   L.fattn = take(NQ * D * 4);
-  L.pm = take((size_t)NH * p.Ptot * 4);
-  L.pl = take((size_t)NH * p.Ptot * 4);
-  L.po = take((size_t)NH * p.Ptot * 64 * 4);
+  const size_t Pmax = (size_t)std::max(p.Ptot, p.Ptot_f);   // routing and field cross-attention partials
+  L.pm = take(NH * Pmax * 4);
+  L.pl = take(NH * Pmax * 4);
+  L.po = take(NH * Pmax * 64 * 4);
   size_t part = 0;
   const int shapes[][3] = {{p.NO, D, 2 * (int)H}, {p.NQ, 2 * D, (int)H}, {p.nact, D, (int)H}, {p.NO, D, D},
                            {p.NO, F, D},        {p.NO, D, F},        {p.NQ, 3 * D, D},     {p.NQ, D, D},
@@ -1009,6 +1068,8 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
                                 : AnswerOut{nullptr, nullptr, nullptr, nullptr, nullptr};
   const int* ooff = dtab + p.off_ooff;
   const int4* items = reinterpret_cast<const int4*>(dtab + p.off_items);
+  const int* frec = dtab + p.off_frec;
+  const int4* fitems = reinterpret_cast<const int4*>(dtab + p.off_fitems);
 
   float2* stats = reinterpret_cast<float2*>(ws + L.stats);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled);
@@ -1016,6 +1077,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   float* prior = reinterpret_cast<float*>(ws + L.prior);
   bf16_t* mem = reinterpret_cast<bf16_t*>(ws + L.mem);
   bf16_t* kv = reinterpret_cast<bf16_t*>(ws + L.kv);
+  bf16_t* fkv = reinterpret_cast<bf16_t*>(ws + L.fkv);
   float* bigpart = reinterpret_cast<float*>(ws + L.bigpart);
   float* u = reinterpret_cast<float*>(ws + L.u);
   float2* ustats = reinterpret_cast<float2*>(ws + L.ustats);
@@ -1036,6 +1098,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   const Weights& W = h->w;
   const float eps = c.ln_eps;
   const bool joint = W.gate != 0.0f;
+  const bool cross = c.field_cross_attention && NL > 0;   // decoder-layer field variant
 
   // stage timing: an event at every stage boundary, on the forward's stream
   std::vector<int> marks;
@@ -1076,7 +1139,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   if (joint) {
     // step 2: memory and K/V of every routing layer (main stream), after the
     // big GEMMs of the group's previous forward
-    if (NR > 0 && !streamed) {
+    if ((NR > 0 || cross) && !streamed) {
       HeadGroup& g = *h->group;
       if (fork) {
         std::lock_guard<std::mutex> lk(g.mu);
@@ -1086,6 +1149,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
                       p.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, p.Tpad);
       MARK(CLEF_STAGE_MEMORY_GEMM);
       launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad, bigpart);
+      if (cross) launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wfkv, W.bfkv, NL, fkv, p.Tpad, bigpart);
       MARK(CLEF_STAGE_KV_GEMM);
       if (fork) {
         std::lock_guard<std::mutex> lk(g.mu);
@@ -1142,6 +1206,16 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
       const SgemmShape gq = launch_sgemm_partial(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, Ly.Wqkv, NQ, 3 * D, D, part);
       launch_field_attn(st, part, gq.nsplit, (size_t)gq.mtiles * kSgemmRows * 3 * D, Ly.bqkv, rec, p.nact, fattn);
       launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps);
+      if (cross) {
+        // cross-attention of the fields over the record's memory rows (the routing attention kernels with
+        // the fields as queries), pre-LN, residual
+        const bf16_t* FK = fkv + (size_t)(2 * l) * NH * p.Tpad * 64;
+        const bf16_t* FV = fkv + (size_t)(2 * l + 1) * NH * p.Tpad * 64;
+        launch_sgemm(st, LdLN{f, D, fstats, Ly.xlng, Ly.xlnb}, EpStore{qbuf, D, Ly.bxq}, Ly.Wxq, NQ, D, D, part);
+        launch_route_attn(st, qbuf, FK, FV, p.Tpad, fitems, p.nfitems, frec, pm, pl, po, p.Ptot_f, p.kchunk);
+        launch_route_combine(st, pm, pl, po, p.Ptot_f, qrec, frec, NQ, fattn);
+        launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bxo}, Ly.Wxo, NQ, D, D, part, fstats, eps);
+      }
       launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part);
       launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part,
                    l + 1 < NL ? fstats : nullptr, eps);
@@ -1260,9 +1334,12 @@ int clef_head_stream_begin(clef_head* h, const clef_head_batch* batch, void* hip
   S.ws_bigpart = L.bigpart;
   S.Tpad = p.Tpad;
   S.f16 = p.f16;
-  S.gemms = h->w.gate != 0.0f && h->cfg.routing_layers > 0;
+  S.cross = h->cfg.field_cross_attention && h->cfg.layers > 0;
+  S.gemms = h->w.gate != 0.0f && (h->cfg.routing_layers > 0 || S.cross);
   S.split_mem = big_gemm_split(p.ntiles, D / 256, (int)H);
   S.split_kv = big_gemm_split(p.ntiles, h->cfg.routing_layers * 8, D);
+  S.split_fkv = big_gemm_split(p.ntiles, (S.cross ? h->cfg.layers : 0) * 8, D);
+  S.ws_fkv = L.fkv;
   S.active = true;
   return CLEF_OK;
 }
@@ -1322,6 +1399,9 @@ int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nr
                       S.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, S.Tpad, S.split_mem, prow);
       launch_gemm_kv(st, mem, dkvtiles + i, 1, W.Wkv, W.bkv, h->cfg.routing_layers, kv, S.Tpad, bigpart, S.split_kv,
                      prow);
+      if (S.cross)
+        launch_gemm_kv(st, mem, dkvtiles + i, 1, W.Wfkv, W.bfkv, h->cfg.layers,
+                       reinterpret_cast<bf16_t*>(ws + S.ws_fkv), S.Tpad, bigpart, S.split_fkv, prow);
     }
   }
   HIPCHK(hipGetLastError());
