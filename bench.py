@@ -69,6 +69,43 @@ def load_traffic(stage, cfg_index):
     return t.get("bytes_per_launch")
 
 
+def streamed_ingest(args, C, HeadRunner, case, runner, torch, np, H):
+    """The same batch fed as the backbone's chunked prefill emits it (varlen, 64-row
+    chunks, chunk k of every record before chunk k + 1); returns the median time the
+    head needs after the last chunk (clef_head_stream_end) and for the whole stream."""
+    b = case.batch
+    sr = HeadRunner(case, share=runner)
+    sr.set_batch(None, C.CLEF_VARLEN)
+    sst = torch.cuda.Stream()
+    cu = b.cu_seqlens()
+    chunks = []
+    pos = [0] * b.B
+    while any(pos[k] < b.lengths[k] for k in range(b.B)):
+        for k in range(b.B):
+            if pos[k] < b.lengths[k]:
+                n = int(min(64, b.lengths[k] - pos[k]))
+                chunks.append((k, pos[k], n, sr.hidden.data_ptr() + (int(cu[k]) + pos[k]) * H * 2))
+                pos[k] += n
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tails, totals = [], []
+    for it in range(args.warmup + max(args.steps // 5, 5)):
+        ev[0].record(sst)
+        C.clef_head_stream_begin(sr.handle, sr.args, sst.cuda_stream)
+        for k, p0, n, ptr in chunks:
+            C.clef_head_stream_rows(sr.handle, k, p0, n, ptr, sst.cuda_stream)
+        ev[1].record(sst)
+        C.clef_head_stream_end(sr.handle, sr.args, sr.logits.data_ptr(), sr.probs.data_ptr(), sr.argmax.data_ptr(),
+                               sst.cuda_stream)
+        ev[2].record(sst)
+        ev[2].synchronize()
+        if it >= args.warmup:
+            tails.append(ev[1].elapsed_time(ev[2]))
+            totals.append(ev[0].elapsed_time(ev[2]))
+    sr.close()
+    return {"chunk_rows": 64, "chunks": len(chunks), "tail_us": round(float(np.median(tails)) * 1e3, 1),
+            "total_us": round(float(np.median(totals)) * 1e3, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +119,7 @@ def main():
     ap.add_argument("--hidden", choices=("bf16", "f16"), default="bf16",
                     help="element type of the hidden states (f16: the CoreML packaging's fp16 hidden)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streamed-ingest measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -157,37 +195,10 @@ def main():
     # streamed ingest of the same batch (varlen, 64-row chunks as the backbone's chunked prefill
     # emits them, chunk k of every record before chunk k + 1): the work left after the last chunk
     # (clef_head_stream_end) is the head's latency once the backbone is done
-    sr = HeadRunner(case, share=runner)
-    sr.set_batch(None, C.CLEF_VARLEN)
-    sst = torch.cuda.Stream()
-    cu = b.cu_seqlens()
-    chunks = []
-    pos = [0] * b.B
-    while any(pos[k] < b.lengths[k] for k in range(b.B)):
-        for k in range(b.B):
-            if pos[k] < b.lengths[k]:
-                n = int(min(64, b.lengths[k] - pos[k]))
-                chunks.append((k, pos[k], n, sr.hidden.data_ptr() + (int(cu[k]) + pos[k]) * H * 2))
-                pos[k] += n
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    tails, totals = [], []
-    for it in range(args.warmup + max(args.steps // 5, 5)):
-        ev[0].record(sst)
-        C.clef_head_stream_begin(sr.handle, sr.args, sst.cuda_stream)
-        for k, p0, n, ptr in chunks:
-            C.clef_head_stream_rows(sr.handle, k, p0, n, ptr, sst.cuda_stream)
-        ev[1].record(sst)
-        C.clef_head_stream_end(sr.handle, sr.args, sr.logits.data_ptr(), sr.probs.data_ptr(), sr.argmax.data_ptr(),
-                               sst.cuda_stream)
-        ev[2].record(sst)
-        ev[2].synchronize()
-        if it >= args.warmup:
-            tails.append(ev[1].elapsed_time(ev[2]))
-            totals.append(ev[0].elapsed_time(ev[2]))
-    sr.close()
-    stream = {"chunk_rows": 64, "chunks": len(chunks), "tail_us": round(float(np.median(tails)) * 1e3, 1),
-              "total_us": round(float(np.median(totals)) * 1e3, 1)}
-    log(f"streamed ingest: {stream}")
+    stream = None
+    if not args.no_stream:
+        stream = streamed_ingest(args, C, HeadRunner, case, runner, torch, np, H)
+        log(f"streamed ingest: {stream}")
     log("stage us: " + ", ".join(f"{k}={v:.1f}" for k, v in stage_us.items()))
     lg, pr, am = runner.outputs()
 
