@@ -180,3 +180,15 @@ def test_forward_answers_rejects_null_before_any_work(case1):
     ans = C.clef_head_answers()
     rc = L.clef_head_forward_answers(None, C.ctypes.byref(args.struct), None, None, None, C.ctypes.byref(ans), None)
     assert rc == C.CLEF_E_ARG
+
+
+def test_weight_list_of_the_decoder_field_variant():
+    head = synth.HeadConfig(field_cross_attention=1)
+    specs = synth.weight_specs(head)
+    assert C.clef_head_weight_count(head) == len(specs) == len(synth.weight_specs(synth.HeadConfig())) + 40
+    for i, (name, shape, kind, _) in enumerate(specs):
+        n, numel, dt = C.clef_head_weight_info(head, i)
+        assert n == name and numel == int(np.prod(shape))
+    with pytest.raises(C.ClefError) as e:
+        C.clef_head_weight_count(synth.HeadConfig(field_cross_attention=2))
+    assert e.value.code == C.CLEF_E_ARG
