@@ -368,12 +368,12 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   __builtin_amdgcn_s_barrier();
   epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
   LOAD_FRAGS(X, 0, 0)
-  // One iteration per 32-deep half h of stage kt (substeps 2 h, 2 h + 1).  The
-  // first half copies stage kt + 1 into the other slot (freed by the previous
-  // stage's barrier); the second half ends with the barrier that hands it over.
-  // Manually interleaved half-steps: 8 groups of (2 MFMAs of the current
-  // fragments, 1 fragment read for the next substep, 1 global->LDS copy),
-  // fenced so the compiler keeps the order.
+  // Stage kt runs its four substeps: the first two copy stage kt + 1 into the
+  // other slot (freed by the previous stage's barrier), A then B; the barrier
+  // before the fourth hands it over.  Each substep is 8 fenced groups of (2
+  // MFMAs of the current fragments, 1 fragment read for the next substep, 1
+  // global->LDS copy in the first two substeps), so the compiler keeps the
+  // order.  The last stage copies nothing.
 #define MFMA2(F, t)                                                                         \
   acc[(t) >> 1][((t) & 1) * 2] =                                                            \
       mfma32<Epi::kF16>(F##a[(t) >> 1], F##b[((t) & 1) * 2], acc[(t) >> 1][((t) & 1) * 2]); \
