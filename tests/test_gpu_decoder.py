@@ -87,3 +87,14 @@ def test_decoder_variant_ragged_varlen_and_streamed(torch_gpu):
     for a, c in zip(op, os_):
         assert np.array_equal(a, c)
     _check(case, op, "decoder fields ragged")
+
+
+def test_decoder_variant_without_routing_layers_fp16(torch_gpu):
+    """routing_layers = 0: the memory rows are still computed for the fields'
+    cross-attention; with fp16 hidden rows."""
+    spec = _variant(synth.config_spec(1, B=2, L=900, lengths=("uniform", 500, 900), routing_layers=0,
+                                      vocab_size=4096, hidden_dtype="f16"))
+    case = synth.make_case(spec)
+    assert case.head.routing_layers == 0 and case.head.field_cross_attention == 1
+    say(f"case decoder-layer fields, no routing layers, fp16: lengths={case.batch.lengths.tolist()}")
+    _check(case, _run(case), "decoder fields, no routing, fp16")
