@@ -103,7 +103,8 @@ typedef struct {
  *     P.ffn1.w[F,D], .b[F]; P.ffn2.w[D,F], .b[D];
  *   score.w1[D,4D]; score.b1[D]; score.w2[D]; score.b2[1];
  *   gate_logit[1] (CLEF_F32); joint_scale[1] (CLEF_F32).
- * All others are CLEF_BF16.  clef_head_weight_name() enumerates them. */
+ * All others are CLEF_BF16.  clef_head_weight_count() and clef_head_weight_info()
+ * enumerate them. */
 typedef struct {
   const char *name;
   const void *host_data;
