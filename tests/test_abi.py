@@ -192,3 +192,14 @@ def test_weight_list_of_the_decoder_field_variant():
     with pytest.raises(C.ClefError) as e:
         C.clef_head_weight_count(synth.HeadConfig(field_cross_attention=2))
     assert e.value.code == C.CLEF_E_ARG
+
+
+def test_question_with_too_many_options_is_refused():
+    spec = synth.CaseSpec(name="too-many", seed=5, head=synth.HeadConfig(vocab_size=512), B=1, L=None,
+                          lengths=("fixed", 3400, 3400), fields="ordered", ordered=((synth.CHOICE, 1025),),
+                          opt_len=(1, 1), instr_len=(2, 4))
+    case = synth.make_case(spec, with_table=False)
+    args = C.BatchArgs(case.batch, 1)
+    with pytest.raises(C.ClefError) as e:
+        C.clef_head_check_batch(case.head, args)
+    assert e.value.code == C.CLEF_E_UNSUPPORTED

@@ -149,3 +149,24 @@ def test_split_k_big_gemms(torch_gpu, B, L):
     case = synth.make_case(spec)
     out = _run(case)
     _check_all(case, out, f"split {B}x{L}")
+
+
+@pytest.mark.parametrize("H", [512, 8192])
+def test_smallest_and_largest_hidden_size(torch_gpu, H):
+    """hidden_size 512 and 8192, the ends of the supported range (row kernels
+    with 1 and 16 chunks per lane, memory GEMM depth 512 and 8192)."""
+    spec = _spec(f"hidden-{H}", 7400 + H // 512, head=synth.HeadConfig(hidden_size=H, vocab_size=4096), B=2,
+                 lengths=("uniform", 700, 1300), fields="counts", counts=(2, 2, 1), choice_opts=(2, 5))
+    say(f"case hidden size {H}")
+    case = synth.make_case(spec)
+    _check_all(case, _run(case), f"H={H}")
+
+
+def test_question_with_the_most_options(torch_gpu):
+    """A question with 1024 options, the most the per-question kernels hold."""
+    spec = _spec("max-options", 7501, B=1, lengths=("fixed", 3400, 3400), fields="ordered",
+                 ordered=((synth.CHOICE, 1024), (synth.NOUL, 2)), opt_len=(1, 1), instr_len=(2, 4))
+    say("case question with 1024 options")
+    case = synth.make_case(spec)
+    assert int(np.diff(case.batch.o_offsets).max()) == 1024
+    _check_all(case, _run(case), "1024 options")
