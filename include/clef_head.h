@@ -220,8 +220,9 @@ CLEF_API int clef_head_forward_answers(clef_head *h, const clef_head_batch *batc
  * clef_head_stream_end: batch must describe the same batch as at begin (its
  *   host tables are read again; CLEF_E_ARG if they differ); every row must
  *   have arrived (CLEF_E_LENGTH otherwise).  Runs the rest of the forward on
- *   hip_stream; outputs as clef_head_forward.  The stream is closed on
- *   success.
+ *   hip_stream; outputs as clef_head_forward, plus the answer mapping of
+ *   clef_head_forward_answers when answers is not NULL.  The stream is closed
+ *   on success.
  * clef_head_stream_cancel: closes an open stream without computing outputs.
  * While a stream is open the handle refuses clef_head_forward (CLEF_E_ARG).
  * Use one HIP stream for a streamed batch, or order the streams. */
@@ -229,7 +230,7 @@ CLEF_API int clef_head_stream_begin(clef_head *h, const clef_head_batch *batch, 
 CLEF_API int clef_head_stream_rows(clef_head *h, int32_t record, int32_t row0, int32_t nrows, const void *rows,
                                    void *hip_stream);
 CLEF_API int clef_head_stream_end(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
-                                  int32_t *argmax, void *hip_stream);
+                                  int32_t *argmax, const clef_head_answers *answers, void *hip_stream);
 CLEF_API int clef_head_stream_cancel(clef_head *h);
 
 /* Release everything the handle owns.  NULL is ignored. */

@@ -85,7 +85,8 @@ def load() -> ctypes.CDLL:
                                             ctypes.POINTER(clef_head_answers), _P]
     L.clef_head_stream_begin.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P]
     L.clef_head_stream_rows.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
-    L.clef_head_stream_end.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P, _P]
+    L.clef_head_stream_end.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P,
+                                       ctypes.POINTER(clef_head_answers), _P]
     L.clef_head_stream_cancel.argtypes = [_P]
     L.clef_head_create_sharing.argtypes = [_P, ctypes.POINTER(_P)]
     L.clef_head_destroy.argtypes = [_P]
@@ -230,9 +231,13 @@ def clef_head_stream_rows(handle: int, record: int, row0: int, nrows: int, rows_
 
 
 def clef_head_stream_end(handle: int, batch_args: BatchArgs, logits_ptr: int, probs_ptr: int, argmax_ptr: int,
-                         stream_ptr: int = 0):
+                         stream_ptr: int = 0, answer_ptrs=None):
+    """answer_ptrs: optional (value, confidence, value_4dp, confidence_4dp, probs_4dp) device addresses."""
+    ans = None
+    if answer_ptrs is not None:
+        ans = ctypes.byref(clef_head_answers(*[a or None for a in answer_ptrs]))
     _check(load().clef_head_stream_end(handle, ctypes.byref(batch_args.struct), logits_ptr, probs_ptr, argmax_ptr,
-                                       stream_ptr or None))
+                                       ans, stream_ptr or None))
 
 
 def clef_head_stream_cancel(handle: int):

@@ -1409,7 +1409,7 @@ int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nr
 }
 
 int clef_head_stream_end(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
-                         void* hip_stream) {
+                         const clef_head_answers* answers, void* hip_stream) {
   if (!h) return fail(CLEF_E_ARG, "handle is NULL");
   auto& S = h->strm;
   if (!S.active) return fail(CLEF_E_ARG, "no streamed batch in progress (clef_head_stream_begin first)");
@@ -1422,7 +1422,7 @@ int clef_head_stream_end(clef_head* h, const clef_head_batch* batch, float* logi
   if (p.tab != S.tab) return fail(CLEF_E_ARG, "the batch differs from the one clef_head_stream_begin planned");
   clef_head_batch b = *batch;
   b.hidden = S.rows;
-  rc = forward_impl(h, &b, logits, probs, argmax, nullptr, hip_stream, true);
+  rc = forward_impl(h, &b, logits, probs, argmax, answers, hip_stream, true);
   if (rc == CLEF_OK) S.active = false;
   return rc;
 }

@@ -140,3 +140,37 @@ def test_stream_errors_are_refused(torch_gpu):
     for a, c in zip(ref, out):
         assert np.array_equal(a, c)
     r.close()
+
+
+def test_stream_end_with_answers(torch_gpu):
+    """clef_head_stream_end with answer buffers returns the answer mapping of
+    clef_head_forward_answers bit for bit."""
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd.runner import HeadRunner
+    case = synth.make_case(synth.config_spec(1, B=2, L=800, lengths=("uniform", 500, 800),
+                                             head=synth.HeadConfig(vocab_size=4096)))
+    say("case streamed with answers")
+    r = HeadRunner(case)
+    r.set_batch(None, C.CLEF_VARLEN)
+    r.forward_answers()
+    ref = r.answers()
+    ref_out = r.outputs()
+    for t in r.ans:
+        t.fill_(-1.0)
+    b = r.batch
+    st = torch_gpu.cuda.current_stream().cuda_stream
+    C.clef_head_stream_begin(r.handle, r.args, st)
+    cu = b.cu_seqlens()
+    for k in range(b.B):
+        for p0 in range(0, int(b.lengths[k]), 64):
+            n = int(min(64, b.lengths[k] - p0))
+            C.clef_head_stream_rows(r.handle, k, p0, n, r.hidden.data_ptr() + (int(cu[k]) + p0) * b.H * 2, st)
+    C.clef_head_stream_end(r.handle, r.args, r.logits.data_ptr(), r.probs.data_ptr(), r.argmax.data_ptr(), st,
+                           answer_ptrs=[t.data_ptr() for t in r.ans])
+    got = r.answers()
+    out = r.outputs()
+    r.close()
+    for a, c in zip(ref, got):
+        assert np.array_equal(a, c)
+    for a, c in zip(ref_out, out):
+        assert np.array_equal(a, c)
