@@ -364,13 +364,15 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
 
   const int nk = K / nsplit / KS;        // >= 2 (K / nsplit a multiple of 128)
   COPY_STAGE(0, 0)
-  WAIT_VM(0);
+  COPY_STAGE(1, KS)                      // nk >= 2: the second stage is in flight while the first is waited for
+  WAIT_VM(16);                           // the tile constants and the first stage have landed
   __builtin_amdgcn_s_barrier();
   epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
   LOAD_FRAGS(X, 0, 0)
-  // Stage kt runs its four substeps: the first two copy stage kt + 1 into the
-  // other slot (freed by the previous stage's barrier), A then B; the barrier
-  // before the fourth hands it over.  Each substep is 8 fenced groups of (2
+  // The prologue copies the first two stages and waits for the first only.
+  // Stage kt (from 1 on) runs its four substeps: the first two copy stage
+  // kt + 1 into the other slot (freed by the previous stage's barrier), A then
+  // B; the barrier before the fourth hands it over.  Each substep is 8 fenced groups of (2
   // MFMAs of the current fragments, 1 fragment read for the next substep, 1
   // global->LDS copy in the first two substeps), so the compiler keeps the
   // order.  The last stage copies nothing.
@@ -404,7 +406,24 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
     FRAG1(G, gst, gkk, t)                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  {
+    // stage 0: stage 1 was copied by the prologue
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(X, Y, 0, 1)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(Y, X, 0, 2)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(X, Y, 0, 3)
+    WAIT_LDS();
+    WAIT_VM(0);                          // stage 1 has landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(Y, X, 1, 0)
+  }
+  for (int kt = 1; kt + 1 < nk; ++kt) {
     const int cur = kt & 1, nxt = cur ^ 1, kn = (kt + 1) * KS;
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
