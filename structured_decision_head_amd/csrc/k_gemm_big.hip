@@ -362,7 +362,7 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   u32x4 Xa[4], Xb[4], Ya[4], Yb[4];
 
-  const int nk = K / nsplit / KS;        // >= 2 (K / nsplit a multiple of 128)
+  const int nk = K / nsplit / KS;        // >= 4 (K / nsplit a multiple of 128, at least 256)
   COPY_STAGE(0, 0)
   COPY_STAGE(1, KS)                      // nk >= 2: the second stage is in flight while the first is waited for
   WAIT_VM(16);                           // the tile constants and the first stage have landed
@@ -370,9 +370,12 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
   LOAD_FRAGS(X, 0, 0)
   // The prologue copies the first two stages and waits for the first only.
-  // Stage kt (from 1 on) runs its four substeps: the first two copy stage
-  // kt + 1 into the other slot (freed by the previous stage's barrier), A then
-  // B; the barrier before the fourth hands it over.  Each substep is 8 fenced groups of (2
+  // Each stage runs four substeps; the barrier before the fourth hands the
+  // next stage over and frees the current stage's slot, into which the fourth
+  // substep already copies the A tile of the stage after next, while the B
+  // tile of the next stage is copied in the first substep.  So both operand
+  // copies get three to four substeps to land.  Needs nk >= 3 (the host keeps
+  // K / nsplit >= 256).  Each substep is 8 fenced groups of (2
   // MFMAs of the current fragments, 1 fragment read for the next substep, 1
   // global->LDS copy in the first two substeps), so the compiler keeps the
   // order.  The last stage copies nothing.
@@ -407,7 +410,6 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
   {
-    // stage 0: stage 1 was copied by the prologue
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
     HALF(X, Y, 0, 1)
@@ -418,24 +420,41 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
     __builtin_amdgcn_sched_barrier(0);
     HALF(X, Y, 0, 3)
     WAIT_LDS();
-    WAIT_VM(0);                          // stage 1 has landed
+    WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, 1, 0)
+    HALF_CP(Y, X, 1, 0, CPA1, 0, 2 * KS)
   }
-  for (int kt = 1; kt + 1 < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1, kn = (kt + 1) * KS;
+  for (int kt = 1; kt + 2 < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(X, Y, cur, 1, CPA1, nxt, kn)
+    HALF_CP(X, Y, cur, 1, CPB1, nxt, (kt + 1) * KS)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(Y, X, cur, 2, CPB1, nxt, kn)
+    HALF(Y, X, cur, 2)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
     HALF(X, Y, cur, 3)
     WAIT_LDS();
-    WAIT_VM(0);                          // the next stage has landed
+    WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF_CP(Y, X, nxt, 0, CPA1, cur, (kt + 2) * KS)
+  }
+  {
+    const int kt = nk - 2, cur = kt & 1, nxt = cur ^ 1;
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF_CP(X, Y, cur, 1, CPB1, nxt, (kt + 1) * KS)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(Y, X, cur, 2)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(X, Y, cur, 3)
+    WAIT_LDS();
+    WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     HALF(Y, X, nxt, 0)
@@ -580,6 +599,7 @@ void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, cons
                      const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
                      float* part, long long Tpad, int split, long long row0) {
   if (ntiles == 0) return;
+  // the main loop needs at least 3 stages of 64: H is a multiple of 512 and every slice at least 256 deep
   const int ntn = 1024 / BN;
   const int S = !part ? 1 : split > 0 ? split : big_gemm_split(ntiles, ntn, H);
   const dim3 grid(ntiles * ntn * S);
