@@ -488,6 +488,24 @@ struct Blob {
   size_t add_f32(const std::vector<float>& v) { return add(v.data(), v.size() * 4); }
 };
 
+// Weights of the small GEMMs are stored in MFMA fragment order: the [N, K]
+// matrix is cut into 16 x 32 blocks (16 output columns, 32 K positions),
+// blocks of one 16-column strip follow each other along K, and inside a block
+// lane l of a wave finds its 16-byte B fragment (column l % 16, K positions
+// 8 (l / 16) .. +8) at element 8 l.  A wave then reads a whole block with one
+// fully coalesced 1 KB load instead of touching 16 rows per load.
+std::vector<uint16_t> fragment_order(const uint16_t* src, int N, int K) {
+  std::vector<uint16_t> out((size_t)N * K);
+  const int kb = K / 32;
+  for (int n = 0; n < N; ++n)
+    for (int k8 = 0; k8 < K / 8; ++k8) {   // 8 consecutive K positions stay together
+      const size_t blk = (size_t)(n / 16) * kb + k8 / 4;
+      const int lane = (n % 16) + 16 * (k8 % 4);
+      memcpy(&out[blk * 512 + lane * 8], src + (size_t)n * K + k8 * 8, 16);
+    }
+  return out;
+}
+
 struct NamedW {
   const void* p;
   int64_t n;
@@ -529,6 +547,10 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
   std::vector<std::pair<size_t, const void**>> fix;
   auto put_bf = [&](const uint16_t* src, size_t n, const bf16_t** dst) { fix.push_back({blob.add(src, n * 2), (const void**)dst}); };
   auto put_f = [&](const std::vector<float>& v, const float** dst) { fix.push_back({blob.add_f32(v), (const void**)dst}); };
+  auto put_frag = [&](const uint16_t* src, int N, int K, const bf16_t** dst) {
+    const std::vector<uint16_t> v = fragment_order(src, N, K);
+    put_bf(v.data(), v.size(), dst);
+  };
 
   Weights& W = h->w;
   // input LayerNorm (pooling) and the memory projection with the LayerNorm folded in
@@ -574,7 +596,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
       memcpy(&Wa[(size_t)j * 2 * H], a + (size_t)j * H, H * 2);
       memcpy(&Wa[(size_t)j * 2 * H + H], l + (size_t)j * H, H * 2);
     }
-    put_bf(Wa.data(), Wa.size(), &W.Wa7);
+    put_frag(Wa.data(), D, 2 * H, &W.Wa7);
     const auto b1 = tof("opt_ctx.b"), b2 = tof("opt_lex.b"), b3 = tof("q_opt.b");
     std::vector<float> bs(D);
     for (int j = 0; j < D; ++j) bs[j] = (float)((double)b1[j] + b2[j] + b3[j]);
@@ -582,13 +604,13 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     std::vector<uint16_t> Wq((size_t)2 * D * H);
     memcpy(Wq.data(), bf("q_base.w"), (size_t)D * H * 2);
     memcpy(Wq.data() + (size_t)D * H, bf("q_opt.w"), (size_t)D * H * 2);
-    put_bf(Wq.data(), Wq.size(), &W.Wqq);
+    put_frag(Wq.data(), 2 * D, H, &W.Wqq);
     std::vector<float> bq(2 * D, 0.f);
     const auto bb = tof("q_base.b");
     std::copy(bb.begin(), bb.end(), bq.begin());
     put_f(bq, &W.bqq);
   }
-  put_bf(bf("glob.w"), (size_t)D * H, &W.Wg);
+  put_frag(bf("glob.w"), D, H, &W.Wg);
   put_f(tof("glob.b"), &W.bg);
   put_f(tof("type_emb"), &W.temb);
   put_f(tof("summary.w"), &W.sw);
@@ -626,7 +648,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     put_f(tof(p + ".ln2.w"), &L.ln2g);
     put_f(tof(p + ".ln2.b"), &L.ln2b);
     if (route) {
-      put_bf(bf(p + ".q.w"), (size_t)D * D, &L.Wq);
+      put_frag(bf(p + ".q.w"), D, D, &L.Wq);
       put_f(tof(p + ".q.b"), &L.bq);
       L.Wqkv = nullptr;
       L.bqkv = nullptr;
@@ -640,16 +662,16 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
         std::copy(bb.begin(), bb.end(), bqkv.begin() + (size_t)i * D);
         ++i;
       }
-      put_bf(Wqkv.data(), Wqkv.size(), &L.Wqkv);
+      put_frag(Wqkv.data(), 3 * D, D, &L.Wqkv);
       put_f(bqkv, &L.bqkv);
       L.Wq = nullptr;
       L.bq = nullptr;
     }
-    put_bf(bf(p + ".o.w"), (size_t)D * D, &L.Wo);
+    put_frag(bf(p + ".o.w"), D, D, &L.Wo);
     put_f(tof(p + ".o.b"), &L.bo);
-    put_bf(bf(p + ".ffn1.w"), (size_t)F * D, &L.W1);
+    put_frag(bf(p + ".ffn1.w"), F, D, &L.W1);
     put_f(tof(p + ".ffn1.b"), &L.b1);
-    put_bf(bf(p + ".ffn2.w"), (size_t)D * F, &L.W2);
+    put_frag(bf(p + ".ffn2.w"), D, F, &L.W2);
     put_f(tof(p + ".ffn2.b"), &L.b2);
   }
   if (c.field_cross_attention && NL > 0) {
@@ -666,15 +688,15 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
       Layer& L = W.field[l];
       put_f(tof(p + ".xln.w"), &L.xlng);
       put_f(tof(p + ".xln.b"), &L.xlnb);
-      put_bf(bf(p + ".xq.w"), (size_t)D * D, &L.Wxq);
+      put_frag(bf(p + ".xq.w"), D, D, &L.Wxq);
       put_f(tof(p + ".xq.b"), &L.bxq);
-      put_bf(bf(p + ".xo.w"), (size_t)D * D, &L.Wxo);
+      put_frag(bf(p + ".xo.w"), D, D, &L.Wxo);
       put_f(tof(p + ".xo.b"), &L.bxo);
     }
     put_bf(Wf.data(), Wf.size(), &W.Wfkv);
     put_f(bfv, &W.bfkv);
   }
-  put_bf(bf("score.w1"), (size_t)D * 4 * D, &W.Ws1);
+  put_frag(bf("score.w1"), D, 4 * D, &W.Ws1);
   put_f(tof("score.b1"), &W.bs1);
   put_f(tof("score.w2"), &W.ws2);
   W.bs2 = bf16_to_f(bf("score.b2")[0]);

@@ -46,9 +46,12 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // W is stored in fragment order (16 x 32 blocks of 1 KB, a 16-column strip's
+  // blocks consecutive along K): the block of columns n16 and K step k32 starts
+  // at element (n16 * K / 32 + k32) * 512, and lane l's fragment at 8 l in it.
   const bf16_t* wp[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)(n0 + wc0 + cb * 16 + (lane & 15)) * K + (lane >> 4) * 8;
+  for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)((n0 + wc0 + cb * 16) >> 4) * (K >> 5) * 512 + lane * 8;
 
   // Register double buffer: the next chunk's A and B loads are issued before
   // the current chunk's MFMAs, so each workgroup pays one memory round trip
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
     cq = ld.cst((K0) + (tid & 15) * 8);                                                  \
     _Pragma("unroll") for (int cb = 0; cb < 2; ++cb)                                     \
       _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                   \
-        bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (K0) + kk * 32);           \
+        bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (size_t)(K0) * 16 + kk * 512); \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
       const int v = tid + 256 * i, r = v >> 4, c = v & 15;                               \
       if (m0 + r < M) ra[i] = ld.fetch(m0 + r, (K0) + c * 8);                            \
