@@ -27,15 +27,18 @@ struct KV32 {
   u32x4 v[2][2];
 };
 
-DEV void kv_load(KV32& r, const bf16_t* Kj, const bf16_t* Vj, int row0, int l32, int g) {
-  const bf16_t* kp = Kj + (size_t)(row0 + l32) * 64 + 8 * g;
+// K and V are stored in 4 KB blocks of 32 keys already in fragment order:
+// fragment q of the block holds lane l's 16 bytes at element 512 q + 8 l
+// (K: q = 16-dim group kk; V: q = 2 t + dt), one contiguous 1 KB per load.
+DEV void kv_load(KV32& r, const bf16_t* Kj, const bf16_t* Vj, int row0, int lane) {
+  const bf16_t* kp = Kj + (size_t)(row0 >> 5) * 2048 + lane * 8;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) r.k[kk] = *reinterpret_cast<const u32x4*>(kp + kk * 16);
-  const bf16_t* vp = Vj + (size_t)(row0 >> 5) * 2048 + (size_t)l32 * 32 + 8 * g;
+  for (int kk = 0; kk < 4; ++kk) r.k[kk] = *reinterpret_cast<const u32x4*>(kp + kk * 512);
+  const bf16_t* vp = Vj + (size_t)(row0 >> 5) * 2048 + lane * 8;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) r.v[t][dt] = *reinterpret_cast<const u32x4*>(vp + dt * 1024 + 16 * t);
+    for (int dt = 0; dt < 2; ++dt) r.v[t][dt] = *reinterpret_cast<const u32x4*>(vp + (2 * t + dt) * 512);
 }
 
 // One 32-key step of the online softmax for the wave's 32 queries.
@@ -137,16 +140,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // three 32-key steps per iteration so that the triple buffer has static
     // registers: two steps' K and V are in flight while one is multiplied
     KV32 a, b, c3;
-    kv_load(a, Kj, Vj, kv0 + k_lo, l32, g);
-    if (k_lo + 32 < k_hi) kv_load(b, Kj, Vj, kv0 + k_lo + 32, l32, g);
+    kv_load(a, Kj, Vj, kv0 + k_lo, lane);
+    if (k_lo + 32 < k_hi) kv_load(b, Kj, Vj, kv0 + k_lo + 32, lane);
     for (int kb = k_lo; kb < k_hi; kb += 96) {
-      if (kb + 64 < k_hi) kv_load(c3, Kj, Vj, kv0 + kb + 64, l32, g);
+      if (kb + 64 < k_hi) kv_load(c3, Kj, Vj, kv0 + kb + 64, lane);
       kv_step(a, qf, kb, n, g, scale_log2, m, l, o);
       if (kb + 32 >= k_hi) break;
-      if (kb + 96 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 96, l32, g);
+      if (kb + 96 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 96, lane);
       kv_step(b, qf, kb + 32, n, g, scale_log2, m, l, o);
       if (kb + 64 >= k_hi) break;
-      if (kb + 128 < k_hi) kv_load(b, Kj, Vj, kv0 + kb + 128, l32, g);
+      if (kb + 128 < k_hi) kv_load(b, Kj, Vj, kv0 + kb + 128, lane);
       kv_step(c3, qf, kb + 64, n, g, scale_log2, m, l, o);
     }
     if (qvalid) {

@@ -93,11 +93,18 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
 
 // Columns are [K_0 | V_0 | K_1 | V_1 | ...] (1024 each), so a 256-column tile
 // is four heads of one K or one V, and the tile's 256 rows of one head are a
-// contiguous 32 KB run in either layout.  K is stored head-major
-// [layer][head][row][64] (transposed tiles).  V is stored per 32-row block
-// transposed, [layer][head][row / 32][64][32] with the 32 keys of a block in
-// vblock_pos() order (plain tiles: a lane's accumulators e = 8 q .. 8 q + 7
-// land on 8 consecutive key positions, one 16-byte run).
+// contiguous 32 KB run in either layout.  Both are stored per head in blocks
+// of 32 rows (4 KB), each block in the routing attention's MFMA fragment
+// order, so that a wave reads 1 KB of contiguous memory per operand load:
+//  * K block (key row r, dim d): 16-byte chunk (d / 8) of row r sits at
+//    chunk index 64 (d / 16) + (r + 32 ((d / 8) & 1)) (kchunk());
+//  * V block (dim f, key position p): the block is V^T [64][32] with the 32
+//    keys in vblock_pos() order (plain tiles: a lane's accumulators
+//    e = 8 q .. 8 q + 7 land on 8 consecutive key positions, one 16-byte run),
+//    and 16-byte chunk (p / 8) of feature row f sits at chunk index
+//    64 (2 (p / 16) + f / 32) + (f % 32 + 32 ((p / 8) & 1)) (vchunk()).
+DEV int kchunk(int r, int c) { return 64 * (c >> 1) + (r & 31) + 32 * (c & 1); }
+DEV int vchunk(int f, int c) { return 64 * (2 * (c >> 1) + (f >> 5)) + (f & 31) + 32 * (c & 1); }
 // The same with fp16 hidden rows and an fp16 copy of W' (fp16 MFMA).
 struct EpiMem16 : EpiMem {
   static constexpr bool kF16 = true;
@@ -169,23 +176,26 @@ struct EpiKV {
       }
     }
   }
+  // Both write 4 heads x 32 KB in memory order (consecutive threads, consecutive
+  // 16-byte chunks): thread t writes chunk t of each 32-row block, i.e. row /
+  // feature t % 32 of fragment part t / 32 of the layout above, so its source
+  // position in the image differs from block to block by a constant stride.
   DEV void store(const bf16_t* img, int orow0, int ocol0, bool tr, int tid) const {
+    int src;
     if (tr) {
-#pragma unroll 8
-      for (int i = tid; i < 4 * 2048; i += 256) {          // 4 heads x 256 rows x 8 chunks of 16 B
-        const int hh = i >> 11, r = (i >> 3) & 255, ch = i & 7;
-        bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)orow0 * 64;
-        *reinterpret_cast<uint4*>(dst + r * 64 + ch * 8) =
-            *reinterpret_cast<const uint4*>(img + hh * (256 * 64) + kpos(r, ch * 8));
-      }
+      const int rr = tid & 31, ch = 2 * (tid >> 6) + ((tid >> 5) & 1);   // inverse of kchunk()
+      src = kpos(rr, ch * 8);                // + 2048 per block: the swizzle depends on rr only
     } else {
-#pragma unroll 8
-      for (int i = tid; i < 4 * 2048; i += 256) {          // 4 heads x 32 KB in memory order
-        const int hh = i >> 11, j = i & 2047, f = (j >> 2) & 63, c = j & 3;
-        bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)(orow0 >> 5) * 2048;
-        *reinterpret_cast<uint4*>(dst + j * 8) =
-            *reinterpret_cast<const uint4*>(img + hh * 16384 + (j >> 2) * 32 + 8 * (c ^ ((f >> 2) & 3)));
-      }
+      const int f = 32 * ((tid >> 6) & 1) + (tid & 31), c = 2 * (tid >> 7) + ((tid >> 5) & 1);   // inverse of vchunk()
+      src = f * 32 + 8 * (c ^ ((f >> 2) & 3));
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)orow0 * 64 + tid * 8;
+      const bf16_t* im = img + hh * 16384 + src;
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        *reinterpret_cast<uint4*>(dst + b * 2048) = *reinterpret_cast<const uint4*>(im + b * 2048);
     }
   }
 };
@@ -539,10 +549,9 @@ __global__ __launch_bounds__(256) void k_mem_reduce(const float* __restrict__ pa
 }
 
 // Sum of the split-K slices of the K/V GEMM plus bias, written in the routing
-// attention's layouts (K head-major [layer][head][row][64]; V per 32-row block
-// [layer][head][row / 32][64][32] with keys at vblock_pos()).  One block per
-// (32-row block, head of one K or V): the sums are staged in LDS, then
-// written as 4 KB of contiguous memory.
+// attention's layouts (32-row blocks of one head in fragment order, kchunk()
+// and vchunk(); V keys at vblock_pos()).  One block per (32-row block, head of
+// one K or V): the sums are staged in LDS, then written as one 4 KB block.
 __global__ __launch_bounds__(256) void k_kv_reduce(const float* __restrict__ part, int nsplit, long long Tpad,
                                                    long long rbase, const float* __restrict__ bias,
                                                    bf16_t* __restrict__ kv) {
@@ -570,13 +579,13 @@ __global__ __launch_bounds__(256) void k_kv_reduce(const float* __restrict__ par
   if (!isv) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(tile[r][c8 + 2 * k], tile[r][c8 + 2 * k + 1]);
-    *reinterpret_cast<uint4*>(head + (row0 + r) * 64 + c8) = v;
+    *reinterpret_cast<uint4*>(head + (row0 >> 5) * 2048 + kchunk(r, c8 >> 3) * 8) = v;
   } else {
     const int f = t >> 2, p0 = (t & 3) * 8;  // feature row f, key positions p0 .. p0 + 7
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       w[k] = pack_bf16x2(tile[vblock_pos(p0 + 2 * k)][f], tile[vblock_pos(p0 + 2 * k + 1)][f]);
-    *reinterpret_cast<uint4*>(head + (row0 >> 5) * 2048 + f * 32 + p0) = v;
+    *reinterpret_cast<uint4*>(head + (row0 >> 5) * 2048 + vchunk(f, p0 >> 3) * 8) = v;
   }
 }
 
