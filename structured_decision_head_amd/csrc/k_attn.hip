@@ -49,13 +49,22 @@ DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, flo
   for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(r.k[kk]), qf[kk], s, 0, 0, 0);
-  // lane owns query (lane & 31) and keys kb + 8 (e / 4) + 4 g + (e % 4)
+  // lane owns query (lane & 31) and keys kb + 8 (e / 4) + 4 g + (e % 4); only
+  // the record's last step has keys past its end
   float mx = -INFINITY;
+  if (kb + 32 <= n) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
-    s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, s[e]);
+    for (int e = 0; e < 16; ++e) {
+      s[e] *= scale_log2;
+      mx = fmaxf(mx, s[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
+      s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[e]);
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
