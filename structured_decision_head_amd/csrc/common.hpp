@@ -16,13 +16,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-DEV uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Two floats to two bf16 (round to nearest even, hardware conversion), a in the low half.
 DEV uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -38,27 +31,25 @@ DEV void unpack8(const uint4 v, float* f) {
   f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
 }
 
+// Eight floats to eight bf16 (round to nearest even, hardware conversion, one
+// instruction per pair).
 DEV uint4 pack8(const float* f) {
   uint4 v;
-  v.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
-  v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
-  v.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
-  v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+  v.x = pack_bf16x2(f[0], f[1]);
+  v.y = pack_bf16x2(f[2], f[3]);
+  v.z = pack_bf16x2(f[4], f[5]);
+  v.w = pack_bf16x2(f[6], f[7]);
   return v;
 }
 
 // Split 8 floats into hi = bf16(x) and lo = bf16(x - hi); hi + lo carries
 // about 16 significant bits of x.
 DEV void split8(const float* f, uint4& hi, uint4& lo) {
-  float r[8];
-  uint32_t h[8];
+  hi = pack8(f);
+  float h[8], r[8];
+  unpack8(hi, h);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = f2bf(f[i]);
-    r[i] = f[i] - bf2f(h[i]);
-  }
-  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16);
-  hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
+  for (int i = 0; i < 8; ++i) r[i] = f[i] - h[i];
   lo = pack8(r);
 }
 

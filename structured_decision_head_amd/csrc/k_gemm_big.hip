@@ -148,9 +148,9 @@ struct EpiKV {
         }
       }
   }
-  // V (plain): image [head][row block][64][32] in memory order; 16-byte chunk c
-  // of a 64-byte feature row f sits at c ^ ((f >> 2) & 3), so 16 consecutive
-  // feature rows cover all 16 bank groups
+  // V (plain): image [head][row block][64][32] (V^T blocks; store() puts them
+  // in fragment order); 16-byte chunk c of a 64-byte feature row f sits at
+  // c ^ ((f >> 2) & 3), so 16 consecutive feature rows cover all 16 bank groups
   DEV void stage(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
     const int hh = lane >> 5;
 #pragma unroll
