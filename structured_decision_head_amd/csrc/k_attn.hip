@@ -68,11 +68,14 @@ DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, flo
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
-  const float alpha = exp2f(m - mn);      // m = -inf gives 0
+  // v_exp_f32 directly, without the library's rescaling for results below
+  // 2^-126 (those may come out as zero: no weight that small matters next to
+  // the running maximum's weight of 1)
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf gives 0
   float ls = 0.f, p[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    p[e] = exp2f(s[e] - mn);
+    p[e] = __builtin_amdgcn_exp2f(s[e] - mn);
     ls += p[e];
   }
   ls += __shfl_xor(ls, 32, 64);
