@@ -42,8 +42,9 @@ DEV void kv_load(KV32& r, const bf16_t* Kj, const bf16_t* Vj, int row0, int lane
 }
 
 // One 32-key step of the online softmax for the wave's 32 queries.
-DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, float scale_log2, float& m, float& l,
-                 f32x16 (&o)[2]) {
+// The queries carry the score scale (log2(e) / sqrt(64)), so scores come out
+// in log2 units.
+DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, float& m, float& l, f32x16 (&o)[2]) {
   f32x16 s;
 #pragma unroll
   for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -54,15 +55,12 @@ DEV void kv_step(const KV32& r, const bf16x8 (&qf)[4], int kb, int n, int g, flo
   float mx = -INFINITY;
   if (kb + 32 <= n) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s[e] *= scale_log2;
-      mx = fmaxf(mx, s[e]);
-    }
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
-      s[e] = (key < n) ? s[e] * scale_log2 : -INFINITY;
+      s[e] = (key < n) ? s[e] : -INFINITY;
       mx = fmaxf(mx, s[e]);
     }
   }
@@ -138,9 +136,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float4 a = *reinterpret_cast<const float4*>(qp + kk * 16);
         const float4 b = *reinterpret_cast<const float4*>(qp + kk * 16 + 4);
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        if (!qvalid)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = qvalid ? x[e] * scale_log2 : 0.f;
         qf[kk] = as_bf16x8(pack8(x));
       }
     }
@@ -156,13 +153,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (k_lo + 32 < k_hi) kv_load(b, Kj, Vj, kv0 + k_lo + 32, lane);
     for (int kb = k_lo; kb < k_hi; kb += 96) {
       if (kb + 64 < k_hi) kv_load(c3, Kj, Vj, kv0 + kb + 64, lane);
-      kv_step(a, qf, kb, n, g, scale_log2, m, l, o);
+      kv_step(a, qf, kb, n, g, m, l, o);
       if (kb + 32 >= k_hi) break;
       if (kb + 96 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 96, lane);
-      kv_step(b, qf, kb + 32, n, g, scale_log2, m, l, o);
+      kv_step(b, qf, kb + 32, n, g, m, l, o);
       if (kb + 64 >= k_hi) break;
       if (kb + 128 < k_hi) kv_load(b, Kj, Vj, kv0 + kb + 128, lane);
-      kv_step(c3, qf, kb + 64, n, g, scale_log2, m, l, o);
+      kv_step(c3, qf, kb + 64, n, g, m, l, o);
     }
     if (qvalid) {
       const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
