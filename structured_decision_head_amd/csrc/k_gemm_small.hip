@@ -29,7 +29,8 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
                                                int K, int kchunk, int mtiles, int ntiles, int nsplit,
                                                float* __restrict__ part) {
   constexpr int WC = 4 / WR, SBN = 32 * WC, RB = 4 / WR;
-  __shared__ uint4 sAh[SBM * 16], sAl[SBM * 16];   // [row * 16 + swizzled chunk], KC = 128 bf16 per row
+  // two buffers of the converted A chunk: [buffer][row * 16 + swizzled chunk], KC = 128 bf16 per row
+  __shared__ uint4 sAh[2][SBM * 16], sAl[2][SBM * 16];
 
   const int lt = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = lt % mtiles;
@@ -53,57 +54,71 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) wp[cb] = W + (size_t)((n0 + wc0 + cb * 16) >> 4) * (K >> 5) * 512 + lane * 8;
 
-  // Register double buffer: the next chunk's A and B loads are issued before
-  // the current chunk's MFMAs, so each workgroup pays one memory round trip
-  // per launch instead of one per chunk.
+  // Pipeline: while a chunk's MFMAs run, the next chunk's A rows (loaded one
+  // chunk earlier) are converted into the other LDS buffer, the A rows of the
+  // chunk after that and the next chunk's W fragments are in flight.  The
+  // conversion (LayerNorm, hi/lo split) and the MFMAs are independent, so they
+  // overlap; one barrier per chunk hands the converted buffer over.
   typename Ld::Raw ra[4];
   typename Ld::Cst cq;                   // per-column constants of this thread's 8 columns
   uint4 bq[2][4];
-#define SG_FETCH(K0)                                                                     \
+#define SG_FETCH_A(K0)                                                                   \
   {                                                                                      \
     cq = ld.cst((K0) + (tid & 15) * 8);                                                  \
-    _Pragma("unroll") for (int cb = 0; cb < 2; ++cb)                                     \
-      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                   \
-        bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (size_t)(K0) * 16 + kk * 512); \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
       const int v = tid + 256 * i, r = v >> 4, c = v & 15;                               \
       if (m0 + r < M) ra[i] = ld.fetch(m0 + r, (K0) + c * 8);                            \
     }                                                                                    \
   }
-  SG_FETCH(kb)
+#define SG_FETCH_W(K0)                                                                   \
+  {                                                                                      \
+    _Pragma("unroll") for (int cb = 0; cb < 2; ++cb)                                     \
+      _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                   \
+        bq[cb][kk] = *reinterpret_cast<const uint4*>(wp[cb] + (size_t)(K0) * 16 + kk * 512); \
+  }
+#define SG_CONVERT(BUF, K0)                                                              \
+  {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+      const int v = tid + 256 * i;                                                       \
+      const int r = v >> 4, c = v & 15;                                                  \
+      float x[8];                                                                        \
+      if (m0 + r < M) {                                                                  \
+        ld.finish(ra[i], cq, m0 + r, (K0) + c * 8, x);                                   \
+      } else {                                                                           \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) x[e] = 0.f;                        \
+      }                                                                                  \
+      uint4 hi, lo;                                                                      \
+      split8(x, hi, lo);                                                                 \
+      const int idx = r * 16 + (c ^ (r & 15));                                           \
+      sAh[BUF][idx] = hi;                                                                \
+      sAl[BUF][idx] = lo;                                                                \
+    }                                                                                    \
+  }
+  SG_FETCH_A(kb)
+  SG_FETCH_W(kb)
+  SG_CONVERT(0, kb)
+  if (kb + SKC < ke) SG_FETCH_A(kb + SKC)
+  __syncthreads();
+  int buf = 0;
   for (int k0 = kb; k0 < ke; k0 += SKC) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + 256 * i;
-      const int r = v >> 4, c = v & 15;
-      float x[8];
-      if (m0 + r < M) {
-        ld.finish(ra[i], cq, m0 + r, k0 + c * 8, x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      uint4 hi, lo;
-      split8(x, hi, lo);
-      const int idx = r * 16 + (c ^ (r & 15));
-      sAh[idx] = hi;
-      sAl[idx] = lo;
-    }
     uint4 bc[2][4];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bc[cb][kk] = bq[cb][kk];
-    __syncthreads();
-    if (k0 + SKC < ke) SG_FETCH(k0 + SKC)
+    if (k0 + SKC < ke) {
+      SG_FETCH_W(k0 + SKC)
+      SG_CONVERT(buf ^ 1, k0 + SKC)
+      if (k0 + 2 * SKC < ke) SG_FETCH_A(k0 + 2 * SKC)
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk * 4 + (lane >> 4);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int r = wr0 + rb * 16 + (lane & 15);
-        const bf16x8 ah = as_bf16x8(sAh[r * 16 + (c ^ (r & 15))]);
-        const bf16x8 al = as_bf16x8(sAl[r * 16 + (c ^ (r & 15))]);
+        const bf16x8 ah = as_bf16x8(sAh[buf][r * 16 + (c ^ (r & 15))]);
+        const bf16x8 al = as_bf16x8(sAl[buf][r * 16 + (c ^ (r & 15))]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           const bf16x8 b = as_bf16x8(bc[cb][kk]);
@@ -113,8 +128,11 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
       }
     }
     __syncthreads();
+    buf ^= 1;
   }
-#undef SG_FETCH
+#undef SG_CONVERT
+#undef SG_FETCH_W
+#undef SG_FETCH_A
 
   // 16x16 accumulator layout: lane holds column (lane & 15), rows 4 * (lane / 16) + e.
   if (nsplit == 1) {
