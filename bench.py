@@ -124,8 +124,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only (the head shards by record with no exchange between GPUs, "
-              "so one GPU's throughput times N is the multi-GPU figure); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only (the head shards by record with no exchange between GPUs: "
+              "N GPUs run N independent heads); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
