@@ -3,4 +3,4 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg import this
 package; the library never does.
 """
-from .head import forward, forward_record, load_params, from_bf16, top2_margin  # noqa: F401
+from .head import forward, forward_record, load_params, from_bf16  # noqa: F401

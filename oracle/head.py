@@ -123,7 +123,14 @@ def softmax(s: np.ndarray) -> np.ndarray:
 
 
 def sigmoid(x: float) -> float:
-    return 1.0 / (1.0 + math.exp(-x)) if x > -745 else 0.0
+    """Logistic function of the gate logit ([P4] step 4: the gate is the
+    sigmoid of a learned scalar).  For x < 0 it is evaluated as
+    e^x / (1 + e^x), so that no exponent of a positive argument is ever taken
+    and every finite x (and -inf) gives a finite result."""
+    if x >= 0.0:
+        return 1.0 / (1.0 + math.exp(-x))
+    z = math.exp(x)
+    return z / (1.0 + z)
 
 
 def attention(q_in: np.ndarray, kv_in: np.ndarray, p: Dict[str, np.ndarray], prefix: str,
@@ -284,12 +291,3 @@ def forward(weights: Dict[str, np.ndarray], head, batch, table_rows: Callable[[n
         A_all.append(am)
     return np.concatenate(L_all), np.concatenate(P_all), np.concatenate(A_all)
 
-
-def top2_margin(logits: np.ndarray, o_offsets: np.ndarray) -> np.ndarray:
-    """Gap between the largest and second-largest logit of every question
-    (inf for a question with one option)."""
-    out = []
-    for i in range(len(o_offsets) - 1):
-        s = np.sort(logits[o_offsets[i]: o_offsets[i + 1]])[::-1]
-        out.append(s[0] - s[1] if len(s) > 1 else np.inf)
-    return np.array(out)

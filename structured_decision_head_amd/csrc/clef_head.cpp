@@ -703,8 +703,9 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
   W.gate_logit = scalar("gate_logit");
   W.lam = scalar("joint_scale");
   {
+    // logistic gate; e^x / (1 + e^x) for x < 0 takes no exponent of a large positive argument
     const double gl = W.gate_logit;
-    const double gs = gl < -745.0 ? 0.0 : 1.0 / (1.0 + std::exp(-gl));
+    const double gs = gl >= 0.0 ? 1.0 / (1.0 + std::exp(-gl)) : std::exp(gl) / (1.0 + std::exp(gl));
     W.gate = (float)gs;
   }
 

@@ -179,7 +179,8 @@ def brute_record(weights, head, hidden_bits, q_type, q_span, o_offsets, o_span, 
     xmem = MEM if getattr(head, "field_cross_attention", 0) else None
     for l in range(head.layers):
         Fv = _block(Fv, None, P, f"field.{l}", heads, eps, xmem)
-    gate = 1.0 / (1.0 + math.exp(-P["gate_logit"][0])) if P["gate_logit"][0] > -745 else 0.0
+    # logistic gate through tanh (sigma(x) = (1 + tanh(x / 2)) / 2): bounded for every x, -inf included
+    gate = 0.5 * (1.0 + math.tanh(0.5 * float(P["gate_logit"][0])))
     lam = P["joint_scale"][0]
     logits = []
     for k in range(len(o_span)):

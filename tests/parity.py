@@ -2,9 +2,13 @@
 the same seeded inputs, and compare at the stated tolerances.
 
 Tolerances (bf16 storage, fp32 accumulation): max |d logit| <= 2e-2 and
-max |d prob| <= 2e-3; argmax identical, except that a question may pick the
-other option when the oracle's gap between the two picks is no larger than the
-two options' measured logit errors together (a near tie, reported)."""
+max |d prob| <= 2e-3; argmax identical to the oracle's for every question.
+The GPU's argmax must also be the first maximal index of the GPU's own fp32
+logits (the decision taken in the kernel's precision, compared exactly).
+Questions whose oracle top-2 gap lies within the two options' measured logit
+errors are counted and reported as near ties; only a test that builds such
+ties on purpose may pass allow_near_ties=True, and then a differing pick is
+accepted for those questions alone."""
 import sys
 import time
 
@@ -49,26 +53,50 @@ def local_offsets(batch, records):
     return np.array(offs)
 
 
-def compare(name, gpu, ref, o_offsets, tol_logit=TOL_LOGIT, tol_prob=TOL_PROB):
+def top2_margin(logits: np.ndarray, o_offsets: np.ndarray) -> np.ndarray:
+    """Gap between the largest and the second-largest logit of every question
+    (inf for a question with one option).  A logging helper of the tests."""
+    out = []
+    for i in range(len(o_offsets) - 1):
+        s = np.sort(logits[o_offsets[i]: o_offsets[i + 1]])[::-1]
+        out.append(s[0] - s[1] if len(s) > 1 else np.inf)
+    return np.array(out)
+
+
+def first_argmax(logits: np.ndarray, o_offsets: np.ndarray) -> np.ndarray:
+    """Index of the first maximal logit within each question."""
+    return np.array([int(np.argmax(logits[o_offsets[i]: o_offsets[i + 1]])) for i in range(len(o_offsets) - 1)])
+
+
+def compare(name, gpu, ref, o_offsets, tol_logit=TOL_LOGIT, tol_prob=TOL_PROB, allow_near_ties=False):
     lg, pr, am = gpu
     lo, po, ao = ref
     assert lg.shape == lo.shape and am.shape == ao.shape
     assert np.isfinite(lg).all() and np.isfinite(pr).all()
     dl = np.abs(lg - lo)
     dp = np.abs(pr - po)
-    margins = O.top2_margin(lo, o_offsets)
+    margins = top2_margin(lo, o_offsets)
+    # questions whose oracle pick is within reach of the measured logit error
+    near_q = []
+    for q in range(len(ao)):
+        o0, o1 = int(o_offsets[q]), int(o_offsets[q + 1])
+        if o1 - o0 < 2:
+            continue
+        srt = np.argsort(-lo[o0:o1], kind="stable")
+        if lo[o0 + srt[0]] - lo[o0 + srt[1]] <= dl[o0 + srt[0]] + dl[o0 + srt[1]]:
+            near_q.append(q)
     say(f"  {name}: NO={len(lo)} NQ={len(ao)} max|dlogit|={dl.max():.3e} max|dprob|={dp.max():.3e} "
-        f"min oracle top-2 margin={margins.min():.3e}")
+        f"min oracle top-2 margin={margins.min():.3e} near ties={len(near_q)}")
     assert dl.max() <= tol_logit, f"{name}: max |d logit| {dl.max()}"
     assert dp.max() <= tol_prob, f"{name}: max |d prob| {dp.max()}"
-    near = 0
-    for q in range(len(ao)):
-        if am[q] != ao[q]:
-            o0 = o_offsets[q]
-            gap = lo[o0 + ao[q]] - lo[o0 + am[q]]
-            err = dl[o0 + ao[q]] + dl[o0 + am[q]]
-            assert gap <= err, f"{name}: question {q} argmax {am[q]} != {ao[q]} with oracle gap {gap} > {err}"
-            near += 1
-    if near:
-        say(f"  {name}: {near} near-tie argmax differences (oracle gap within the measured logit error)")
+    own = first_argmax(lg, o_offsets)
+    assert np.array_equal(am, own), f"{name}: argmax is not the first maximal index of the GPU's own logits"
+    bad = [q for q in range(len(ao)) if am[q] != ao[q]]
+    if allow_near_ties:
+        assert all(q in near_q for q in bad), f"{name}: argmax differs outside near ties: {bad}"
+        if bad:
+            say(f"  {name}: {len(bad)} near-tie argmax differences accepted (built on purpose)")
+    else:
+        assert not bad, (f"{name}: argmax differs from the oracle on questions {bad} "
+                         f"(oracle margins {[float(margins[q]) for q in bad]})")
     return dl.max(), dp.max()

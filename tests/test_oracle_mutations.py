@@ -12,7 +12,7 @@ from structured_decision_head_amd import synth
 from test_oracle_pins import _brute
 
 _orig = {k: getattr(O, k) for k in ("layer_norm", "gelu", "cosine", "softmax", "attention", "span_mean",
-                                     "linear", "ffn")}
+                                     "linear", "ffn", "sigmoid")}
 
 
 def _m_attention_scale(q_in, kv_in, p, prefix, heads):
@@ -43,12 +43,13 @@ MUTANTS = {
     "linear_no_bias": ("linear", lambda x, w, b: x @ w.T),
     "ffn_no_gelu": ("ffn", lambda x, p, pre: O.linear(O.linear(x, p[pre + ".ffn1.w"], p[pre + ".ffn1.b"]),
                                                       p[pre + ".ffn2.w"], p[pre + ".ffn2.b"])),
+    "gate_sign": ("sigmoid", lambda x: _orig["sigmoid"](-x)),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
-    case = synth.make_case(tiny_spec(seed=21, ln_random=True))
+    case = synth.make_case(tiny_spec(seed=21, ln_random=True, gate_logit=0.7))
     lb, pb, ab = _brute(case)
     fn, impl = MUTANTS[name]
     monkeypatch.setattr(O, fn, impl)

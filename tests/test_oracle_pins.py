@@ -239,6 +239,39 @@ def test_softmax_per_question_sums_to_one(tiny_case):
         assert am[i] == int(np.argmax(seg))
 
 
+def test_sigmoid_matches_scipy_expit_over_the_whole_range():
+    """The gate's logistic function against SciPy's expit, including gate logits
+    whose naive form exp(-x) would overflow a double (x in (-745, -709.8))."""
+    xs = [-math.inf, -800.0, -744.0, -720.0, -709.9, -100.0, -30.0, -1.0, -1e-3, 0.0, 1e-3, 1.0, 30.0,
+          100.0, 709.9, 720.0, 744.0, 800.0, math.inf]
+    for x in xs:
+        got, want = O.sigmoid(x), float(scipy.special.expit(x))
+        assert math.isfinite(got) and 0.0 <= got <= 1.0, x
+        # SciPy flushes results below the smallest normal double to 0; the oracle keeps subnormals
+        assert got == pytest.approx(want, rel=1e-14, abs=1e-300), (x, got, want)
+    # deep in the negative tail sigma(x) = e^x (1 - e^x + ...) = e^x to double precision (subnormal
+    # results carry fewer significant bits)
+    for x in (-40.0, -100.0, -709.9, -720.0):
+        assert O.sigmoid(x) == pytest.approx(math.exp(x), rel=1e-3 if x < -708 else 1e-15)
+    assert O.sigmoid(720.0) == 1.0 and O.sigmoid(-1.0) + O.sigmoid(1.0) == pytest.approx(1.0, abs=1e-16)
+
+
+@pytest.mark.parametrize("gate_logit", [-720.0, -744.0, 720.0])
+def test_extreme_gate_logits_match_brute_force(gate_logit):
+    """Gate logits far in either tail: the oracle runs, agrees with the scalar
+    evaluator, and reduces to the prior (gate ~ 0) or to the full joint term
+    (gate = 1)."""
+    case = synth.make_case(tiny_spec(seed=21, gate_logit=gate_logit))
+    lo, po, ao = _run(case)
+    lb, pb, ab = _brute(case)
+    np.testing.assert_allclose(lo, lb, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(po, pb, rtol=1e-10, atol=1e-12)
+    assert (ao == ab).all()
+    ref_logit = -math.inf if gate_logit < 0 else 60.0     # sigmoid(60) rounds to 1.0 in double
+    lr, _, _ = _run(synth.make_case(tiny_spec(seed=21, gate_logit=ref_logit)))
+    np.testing.assert_allclose(lo, lr, rtol=0, atol=1e-290)
+
+
 def test_gate_zero_gives_lexical_prior_exactly():
     """sigmoid(-inf) = 0, so logits equal the prior; the prior is recomputed here
     with torch ops: layer_norm, span means, table-row means, cosine_similarity."""

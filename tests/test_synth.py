@@ -104,3 +104,20 @@ def test_weights_shapes_and_init():
             assert abs(x.std() * np.sqrt(fan) - 1) < 0.1
     assert w["gate_logit"].dtype == np.float32 and w["gate_logit"][0] == 0.0
     assert w["joint_scale"][0] == 1.0
+
+
+def test_top2_margin_helper():
+    """The test helper that logs each question's top-2 logit gap, against a
+    partition-based form."""
+    from parity import top2_margin
+    rng = np.random.default_rng(5)
+    offs = np.array([0, 1, 4, 9, 11])
+    x = rng.standard_normal(11)
+    got = top2_margin(x, offs)
+    assert np.isinf(got[0])
+    for i in range(1, 4):
+        seg = x[offs[i]: offs[i + 1]]
+        part = np.partition(seg, len(seg) - 2)
+        assert got[i] == part[-1] - part[-2]
+    x[5] = x[6] = x[4:9].max() + 1.0
+    assert top2_margin(x, offs)[2] == 0.0
