@@ -17,9 +17,9 @@
  *     option-weighted summary + global (last) vector + type embedding; 4
  *     transformer layers across fields; logit = prior + gate * (joint_scale *
  *     cosine + residual MLP over [f, o, f*o, |f-o|]).
- *   - CoreML conversion metadata of clef-flash, "decision.head": LayerNorm over
- *     the hidden width into memory, global vector = last token, spans pool the
- *     LayerNorm-ed rows; "decision.spans": half-open [start, end) spans that
+ *   - CoreML conversion metadata of clef-flash, "decision.head": a LayerNorm
+ *     over the hidden width feeds the memory, the global vector is the row at
+ *     the final position, spans pool normalised rows; "decision.spans": half-open [start, end) spans that
  *     index the hidden rows; "question_types": noul 0, choice 1, score 2;
  *     "option_order": noul options are [true, false]; "softmax": per question,
  *     fp32, temperature 1.
@@ -49,13 +49,22 @@ extern "C" {
 
 #define CLEF_API __attribute__((visibility("default")))
 
-/* status codes */
+/* Status codes.  Input errors are raised before any work starts, as the
+ * pages' own entry points do: the tuning guide's pitfalls section (an encoded
+ * schema longer than the length budget is refused before the state is read)
+ * and the clef-4bit page §六 FAQ (a record over the context limit is refused,
+ * ContextTooLong / HTTP 413, unless truncation is allowed). */
 #define CLEF_OK             0
-#define CLEF_E_ARG         -1  /* null pointer, bad config, missing / mis-sized weight */
-#define CLEF_E_LENGTH      -2  /* record length < 1 or > padded length; mask not a prefix mask */
-#define CLEF_E_SPAN        -3  /* empty span, span outside [0, n_b) */
-#define CLEF_E_ID          -4  /* token id outside [0, vocab_size) */
-#define CLEF_E_SCHEMA      -5  /* bad question type, question without options, noul without 2 options */
+#define CLEF_E_ARG         -1  /* null pointer, bad config, missing / mis-sized weight (architecture page
+                                  §3.2 config table; clef-4bit page §三 names of the head's parts) */
+#define CLEF_E_LENGTH      -2  /* record length < 1 or > padded length; mask not a prefix mask (tuning guide
+                                  tip 1: collate pads every record on the right to the longest one) */
+#define CLEF_E_SPAN        -3  /* empty span, span outside [0, n_b) (CoreML metadata page, decision.spans:
+                                  half-open spans over the record's own positions) */
+#define CLEF_E_ID          -4  /* token id outside [0, vocab_size) (CoreML metadata page, decision.head
+                                  lexical: rows of the untied lm_head table are indexed by the span's ids) */
+#define CLEF_E_SCHEMA      -5  /* bad question type, question without options, noul without 2 options
+                                  (CoreML metadata page, question_types and option_order) */
 #define CLEF_E_NOMEM       -6  /* device or pinned allocation failed */
 #define CLEF_E_HIP         -7  /* HIP runtime error (message in clef_head_last_error) */
 #define CLEF_E_UNSUPPORTED -8  /* configuration outside what the kernels are built for */
@@ -132,10 +141,17 @@ typedef struct {
   const int32_t *o_ids;        /* HOST [sum of option span lengths] token ids of every option span, in order */
 } clef_head_batch;
 
-/* Create a head on the current HIP device.  Weights are copied into
- * handle-owned device memory (repacked bf16).  lexical_table is the DEVICE
- * bf16 [vocab_size, hidden_size] untied lm_head.weight; it is borrowed and
- * must outlive the handle.  On success *out receives the handle. */
+/* Create a head on the current HIP device (architecture page §3.2: the head's
+ * configuration table; clef-4bit page §三: the head's parts, stored in bf16 and
+ * never quantised; CoreML metadata page, decision.head: the lexical table is
+ * the backbone's untied lm_head, not part of the head).  cfg and weights are
+ * HOST memory, read during the call; weights are validated by name, element
+ * count and dtype (CLEF_E_ARG on any mismatch, CLEF_E_UNSUPPORTED for a
+ * configuration the kernels are not built for), then copied into
+ * handle-owned device memory (repacked).  lexical_table is the DEVICE bf16
+ * [vocab_size, hidden_size] untied lm_head.weight; it is borrowed and must
+ * outlive the handle.  On success *out receives the handle; on any error
+ * *out is NULL and nothing is leaked (CLEF_E_NOMEM, CLEF_E_HIP). */
 CLEF_API int clef_head_create(const clef_head_config *cfg, const clef_head_weight *weights, int32_t num_weights,
                      const void *lexical_table, clef_head **out);
 
@@ -155,7 +171,10 @@ CLEF_API int clef_head_create(const clef_head_config *cfg, const clef_head_weigh
  * src / out, CLEF_E_HIP when events cannot be created (nothing is leaked). */
 CLEF_API int clef_head_create_sharing(const clef_head *src, clef_head **out);
 
-/* Forward pass on hip_stream (a hipStream_t, or NULL for the default stream).
+/* Forward pass on hip_stream (a hipStream_t, or NULL for the default stream):
+ * the whole head of the clef-4bit page §三 steps 1-4 (pool, route, aggregate
+ * fields, score), then the per-question softmax of the Clef-Flash overview §四
+ * and of the CoreML metadata page's softmax entry (fp32, temperature 1).
  * Outputs (DEVICE, caller-owned): logits fp32 [NO], probs fp32 [NO] (softmax
  * over each question's options), argmax int32 [NQ] (index of the first
  * maximal logit within its question).  The host tables are copied before
@@ -175,7 +194,8 @@ CLEF_API int clef_head_forward(clef_head *h, const clef_head_batch *batch, float
  *                        response omits it)
  *   value_4dp, confidence_4dp [NQ], probs_4dp [NO]
  *                        the same numbers and every probability rounded half
- *                        to even at the 4th decimal ("4 decimals"): the fp32
+ *                        to even at the 4th decimal (the response rounds to four
+ *                        decimal places): the fp32
  *                        nearest to k / 10^4, k = the integer nearest to
  *                        x * 10^4 with ties to even, x the fp32 unrounded value.
  * usage.input_tokens of a record is its valid length n_b and output_tokens is
@@ -233,10 +253,13 @@ CLEF_API int clef_head_stream_end(clef_head *h, const clef_head_batch *batch, fl
                                   int32_t *argmax, const clef_head_answers *answers, void *hip_stream);
 CLEF_API int clef_head_stream_cancel(clef_head *h);
 
-/* Release everything the handle owns.  NULL is ignored. */
+/* Release everything the handle owns (resource management; no page operation).
+ * Waits for the handle's own pending work first.  NULL is ignored. */
 CLEF_API void clef_head_destroy(clef_head *h);
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none): the text of
+ * the raise-early errors above.  The pointer stays valid until the thread's
+ * next failing call. */
 CLEF_API const char *clef_head_last_error(void);
 
 /* Host-only validation of a batch against a configuration: the same checks

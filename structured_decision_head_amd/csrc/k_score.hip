@@ -20,7 +20,7 @@ namespace {
 DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 DEV float dot4(float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
 
-// Round half to even at the fourth decimal (the response's "4 decimals").  For an
+// Round half to even at the fourth decimal (the response rounds to four places).  For an
 // fp32 x the product x * 10^4 is exact in double (24 + 10 significant bits), rint
 // breaks ties to even, and k / 10^4 is the double nearest the decimal k * 10^-4,
 // narrowed to fp32.
