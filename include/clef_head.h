@@ -216,6 +216,26 @@ typedef struct {
 CLEF_API int clef_head_forward_answers(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
                                        int32_t *argmax, const clef_head_answers *answers, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code that sets up HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of clef_head_forward with no device or pinned allocation.  Its workspace is
+ * a static array of CLEF_NOALLOC_SCRATCH_BYTES bytes in the library's device
+ * code object, which each GPU the library runs on holds from the first such
+ * call until the process ends; the host tables are copied from ordinary
+ * host memory (the handle keeps a host copy; host-side planning uses the
+ * ordinary heap).  Arguments, outputs and errors are those of
+ * clef_head_forward, plus CLEF_E_UNSUPPORTED (nothing launched, outputs
+ * untouched) when the batch needs more workspace than the array holds (about
+ * 16K valid rows at hidden_size 4096: one record at the default max_length
+ * 16384 fits), and CLEF_E_ARG while tracing or stage timing is on.  No
+ * kernel relies on the array's previous contents, which persist from the
+ * last call.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams, or different handles without an
+ * order between their streams) race; calls in order on one stream do not. */
+#define CLEF_NOALLOC_SCRATCH_BYTES (256ull << 20)
+CLEF_API int clef_head_forward_noalloc(clef_head *h, const clef_head_batch *batch, float *logits, float *probs,
+                                       int32_t *argmax, void *hip_stream);
+
 /* Streamed ingest: the head consumes a batch's hidden rows while the
  * backbone still produces them (CoreML conversion metadata page of
  * clef-flash, "decision.readout" and "prefill_chunk": a record runs through

@@ -25,7 +25,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=h
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-disable-promote-alloca-to-lds",
          "-I", INCLUDE, "-I", CSRC, "-Wno-unused-result"]
-SOURCES = ["k_rows.hip", "k_gemm_big.hip", "k_gemm_small.hip", "k_attn.hip", "k_score.hip", "clef_head.cpp"]
+SOURCES = ["k_rows.hip", "k_gemm_big.hip", "k_gemm_small.hip", "k_attn.hip", "k_score.hip", "noalloc.hip", "clef_head.cpp"]
 
 
 def _compile(src: str) -> str:

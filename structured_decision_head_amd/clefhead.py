@@ -21,10 +21,12 @@ CLEF_OK, CLEF_E_ARG, CLEF_E_LENGTH, CLEF_E_SPAN, CLEF_E_ID, CLEF_E_SCHEMA, CLEF_
 CLEF_BF16, CLEF_F32 = 1, 2
 CLEF_PADDED, CLEF_VARLEN = 0, 1
 CLEF_HIDDEN_F16 = 0x100
+CLEF_NOALLOC_SCRATCH_BYTES = 256 << 20
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
 
 EXPORTS = ("clef_head_create", "clef_head_create_sharing", "clef_head_forward", "clef_head_forward_answers",
+           "clef_head_forward_noalloc",
            "clef_head_stream_begin", "clef_head_stream_rows", "clef_head_stream_end", "clef_head_stream_cancel",
            "clef_head_destroy", "clef_head_last_error",
            "clef_head_check_batch", "clef_head_span_rows", "clef_head_weight_count", "clef_head_weight_info",
@@ -83,6 +85,7 @@ def load() -> ctypes.CDLL:
     L.clef_head_forward.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P, _P]
     L.clef_head_forward_answers.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P,
                                             ctypes.POINTER(clef_head_answers), _P]
+    L.clef_head_forward_noalloc.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P, _P]
     L.clef_head_stream_begin.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P]
     L.clef_head_stream_rows.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     L.clef_head_stream_end.argtypes = [_P, ctypes.POINTER(clef_head_batch), _P, _P, _P,
@@ -220,6 +223,12 @@ def clef_head_forward_answers(handle: int, batch_args: BatchArgs, logits_ptr: in
                             confidence_4dp_ptr or None, probs_4dp_ptr or None)
     _check(load().clef_head_forward_answers(handle, ctypes.byref(batch_args.struct), logits_ptr, probs_ptr,
                                             argmax_ptr, ctypes.byref(ans), stream_ptr or None))
+
+
+def clef_head_forward_noalloc(handle: int, batch_args: BatchArgs, logits_ptr: int, probs_ptr: int, argmax_ptr: int,
+                              stream_ptr: int = 0):
+    _check(load().clef_head_forward_noalloc(handle, ctypes.byref(batch_args.struct), logits_ptr, probs_ptr,
+                                            argmax_ptr, stream_ptr or None))
 
 
 def clef_head_stream_begin(handle: int, batch_args: BatchArgs, stream_ptr: int = 0):

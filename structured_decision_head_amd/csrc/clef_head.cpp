@@ -452,6 +452,8 @@ struct clef_head {
   float *pooled = nullptr, *ebar = nullptr, *prior = nullptr;
   bf16_t* mem = nullptr;
   float *tr_u = nullptr, *tr_f0 = nullptr, *tr_f = nullptr, *tr_jcos = nullptr, *tr_mlp = nullptr;
+  // allocation-free forwards: the plan's tables, kept until the next such call
+  std::vector<int32_t> noalloc_tab;
   // stage timing
   bool prof = false;
   std::vector<hipEvent_t> ev;
@@ -1021,10 +1023,28 @@ static int stage_plan(clef_head* h, const Plan& p, const WsLayout& L, hipStream_
   return CLEF_OK;
 }
 
+// Allocation-free staging: the workspace is the static per-device scratch and
+// the tables are copied from ordinary (pageable) host memory, which the HIP
+// runtime reads before the copy call returns; the handle keeps its own copy
+// of them until the next call all the same.
+static int stage_plan_noalloc(clef_head* h, const Plan& p, const WsLayout& L, void* ws, hipStream_t st) {
+  if (L.total > kNoallocScratchBytes)
+    return fail(CLEF_E_UNSUPPORTED,
+                "the batch needs %zu bytes of workspace; the allocation-free entry point holds at most %zu "
+                "(use clef_head_forward for larger batches)",
+                L.total, (size_t)kNoallocScratchBytes);
+  h->noalloc_tab = p.tab;
+  HIPCHK(hipMemcpyAsync(static_cast<uint8_t*>(ws) + L.tab, h->noalloc_tab.data(), h->noalloc_tab.size() * 4,
+                        hipMemcpyHostToDevice, st));
+  return CLEF_OK;
+}
+
 // streamed: the row statistics, memory and K/V rows of every tile were
 // computed while the rows streamed in (clef_head_stream_rows); only the rest runs.
+// noalloc: run in the static scratch and allocate nothing (clef_head_forward_noalloc).
 static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logits, float* probs, int32_t* argmax,
-                        const clef_head_answers* answers, void* hip_stream, bool streamed = false) {
+                        const clef_head_answers* answers, void* hip_stream, bool streamed = false,
+                        bool noalloc = false) {
   if (!h) return fail(CLEF_E_ARG, "handle is NULL");
   if (h->strm.active && !streamed)
     return fail(CLEF_E_ARG, "a streamed batch is in progress on this handle (clef_head_stream_end first)");
@@ -1045,9 +1065,17 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
 
   const WsLayout L = ws_layout(c, p);
   if (streamed && L.total > h->ws_bytes) return fail(CLEF_E_ARG, "streamed batch does not fit the staged workspace");
-  {
+  void* wsbase = nullptr;
+  if (noalloc) {
+    if (h->trace || h->prof)
+      return fail(CLEF_E_ARG, "the allocation-free entry point runs with tracing and stage timing off");
+    HIPCHK(noalloc_scratch(h->device, &wsbase));
+    const int rc2 = stage_plan_noalloc(h, p, L, wsbase, st);
+    if (rc2) return rc2;
+  } else {
     const int rc2 = stage_plan(h, p, L, st);
     if (rc2) return rc2;
+    wsbase = h->ws;
   }
   const int NR = c.routing_layers, NL = c.layers, NQ = p.NQ, NO = p.NO;
   const size_t H = c.hidden_size;
@@ -1073,7 +1101,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
     h->tr_mlp = reinterpret_cast<float*>(t);
   }
 
-  uint8_t* ws = static_cast<uint8_t*>(h->ws);
+  uint8_t* ws = static_cast<uint8_t*>(wsbase);
   int32_t* dtab = reinterpret_cast<int32_t*>(ws + L.tab);
 
   const int* rec = dtab + p.off_rec;
@@ -1269,7 +1297,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   h->last_NO = NO;
   h->last_B = p.nact;
   h->last_Tpad = p.Tpad;
-  h->pooled = pooled;
+  h->pooled = noalloc ? nullptr : pooled;   // no snapshots of the shared scratch
   h->ebar = ebar;
   h->prior = prior;
   h->mem = (joint && NR > 0) ? mem : nullptr;
@@ -1288,6 +1316,11 @@ int clef_head_forward_answers(clef_head* h, const clef_head_batch* batch, float*
                               int32_t* argmax, const clef_head_answers* answers, void* hip_stream) {
   if (!answers) return fail(CLEF_E_ARG, "answers is NULL");
   return forward_impl(h, batch, logits, probs, argmax, answers, hip_stream);
+}
+
+int clef_head_forward_noalloc(clef_head* h, const clef_head_batch* batch, float* logits, float* probs,
+                              int32_t* argmax, void* hip_stream) {
+  return forward_impl(h, batch, logits, probs, argmax, nullptr, hip_stream, false, true);
 }
 
 // ---------------------------------------------------------------------------

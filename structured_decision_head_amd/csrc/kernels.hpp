@@ -6,6 +6,12 @@ namespace clef {
 
 constexpr int kMaxOptions = 1024;   // options of one question (LDS arrays in the per-question kernels)
 
+// Static scratch of the allocation-free entry point: its size, and the device
+// address of the array on `device` (which must be the current device; looked
+// up on the first call per device).
+constexpr size_t kNoallocScratchBytes = size_t(256) << 20;
+hipError_t noalloc_scratch(int device, void** out);
+
 // Position of key k (0..31) inside a 32-key V block: the eight keys one lane
 // feeds to a V^T P^T MFMA step sit in 16 contiguous bytes.
 DEV int vblock_pos(int k) { return (k & 16) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }

@@ -64,6 +64,12 @@ class HeadRunner:
         C.clef_head_forward(self.handle, self.args, self.logits.data_ptr(), self.probs.data_ptr(),
                             self.argmax.data_ptr(), s.cuda_stream)
 
+    def forward_noalloc(self, stream: Optional[torch.cuda.Stream] = None):
+        """clef_head_forward_noalloc: the same forward in the library's static scratch."""
+        s = stream if stream is not None else torch.cuda.current_stream()
+        C.clef_head_forward_noalloc(self.handle, self.args, self.logits.data_ptr(), self.probs.data_ptr(),
+                                    self.argmax.data_ptr(), s.cuda_stream)
+
     def forward_answers(self, stream: Optional[torch.cuda.Stream] = None):
         """Forward plus the answer mapping; answers() reads the answer buffers."""
         s = stream if stream is not None else torch.cuda.current_stream()
