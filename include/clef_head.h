@@ -101,7 +101,26 @@ typedef struct {
   int32_t hidden_size, width, heads, routing_layers, layers, feedforward, vocab_size, num_types;
   float ln_eps;
   int32_t field_cross_attention;
+  int32_t precision;   /* CLEF_PRECISION_BF16 or CLEF_PRECISION_F32, below */
 } clef_head_config;
+
+/* Arithmetic of the head, chosen at create (clef_head_config.precision).
+ * CLEF_PRECISION_BF16: bf16 storage of the memory rows, K/V rows, routing
+ *   queries and attention probabilities, fp32 accumulation, fp32 residual
+ *   streams and statistics; activations enter the small products as two bf16
+ *   terms (about 16 significant bits).  The head's stored precision (clef-4bit
+ *   page §三: its weights are bf16 and never quantised).
+ * CLEF_PRECISION_F32: fp32 arithmetic throughout, as the CoreML packaging
+ *   runs the head on fp16 hidden states (CoreML conversion metadata page,
+ *   decision.head, dtype_of_record): memory rows and K/V in fp32 with the
+ *   input LayerNorm applied to the rows (not folded into the weights), fp32
+ *   attention, and every fp32 activation entering a product as three bf16
+ *   terms whose sum is exact, against the exact bf16 weights, so that only
+ *   the fp32 accumulation rounds.  Works with bf16 or fp16 (CLEF_HIDDEN_F16)
+ *   hidden rows; streamed ingest (clef_head_stream_*) is CLEF_E_UNSUPPORTED
+ *   in this mode. */
+#define CLEF_PRECISION_BF16 0
+#define CLEF_PRECISION_F32  1
 
 /* One named head tensor in host memory.  Linear weights use the [out, in]
  * layout.  Names (D = width, H = hidden_size, F = feedforward):
@@ -306,8 +325,8 @@ CLEF_API int clef_head_weight_info(const clef_head_config *cfg, int32_t i, char 
  *   CLEF_TRACE_POOLED  fp32 [NQ + NO + B, H]: question means, option-context means, global rows
  *   CLEF_TRACE_LEXICAL fp32 [NO, H]           option lexical vectors
  *   CLEF_TRACE_PRIOR   fp32 [NO]              lexical prior
- *   CLEF_TRACE_MEMORY  bf16 [sum_b ceil(n_b/256)*256, D]: record b's rows start at
- *                      the sum of the earlier records' rounded lengths
+ *   CLEF_TRACE_MEMORY  bf16 (fp32 in CLEF_PRECISION_F32) [sum_b ceil(n_b/256)*256, D]:
+ *                      record b's rows start at the sum of the earlier records' rounded lengths
  *   CLEF_TRACE_U + r   fp32 [NO, D]           option vectors after r routing layers (r = 0: queries)
  *   CLEF_TRACE_F0      fp32 [NQ, D]           field vectors before the field layers
  *   CLEF_TRACE_F       fp32 [NQ, D]           field vectors after the field layers

@@ -21,6 +21,7 @@ CLEF_OK, CLEF_E_ARG, CLEF_E_LENGTH, CLEF_E_SPAN, CLEF_E_ID, CLEF_E_SCHEMA, CLEF_
 CLEF_BF16, CLEF_F32 = 1, 2
 CLEF_PADDED, CLEF_VARLEN = 0, 1
 CLEF_HIDDEN_F16 = 0x100
+CLEF_PRECISION_BF16, CLEF_PRECISION_F32 = 0, 1
 CLEF_NOALLOC_SCRATCH_BYTES = 256 << 20
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
@@ -45,7 +46,7 @@ class clef_head_config(ctypes.Structure):
     _fields_ = [("hidden_size", ctypes.c_int32), ("width", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("routing_layers", ctypes.c_int32), ("layers", ctypes.c_int32), ("feedforward", ctypes.c_int32),
                 ("vocab_size", ctypes.c_int32), ("num_types", ctypes.c_int32), ("ln_eps", ctypes.c_float),
-                ("field_cross_attention", ctypes.c_int32)]
+                ("field_cross_attention", ctypes.c_int32), ("precision", ctypes.c_int32)]
 
 
 class clef_head_weight(ctypes.Structure):
@@ -123,7 +124,7 @@ def make_config(head) -> clef_head_config:
     """From any object with the config attribute names (e.g. synth.HeadConfig)."""
     return clef_head_config(head.hidden_size, head.width, head.heads, head.routing_layers, head.layers,
                             head.feedforward, head.vocab_size, head.num_types, head.ln_eps,
-                            int(getattr(head, "field_cross_attention", 0)))
+                            int(getattr(head, "field_cross_attention", 0)), int(getattr(head, "precision", 0)))
 
 
 class BatchArgs:

@@ -143,6 +143,8 @@ int check_config(const clef_head_config* c) {
     return fail(CLEF_E_ARG, "config has a non-positive size or epsilon");
   if (c->field_cross_attention != 0 && c->field_cross_attention != 1)
     return fail(CLEF_E_ARG, "field_cross_attention must be 0 or 1 (got %d)", c->field_cross_attention);
+  if (c->precision != CLEF_PRECISION_BF16 && c->precision != CLEF_PRECISION_F32)
+    return fail(CLEF_E_ARG, "precision must be CLEF_PRECISION_BF16 or CLEF_PRECISION_F32 (got %d)", c->precision);
   if (c->width != D || c->heads != NH || c->feedforward != F)
     return fail(CLEF_E_UNSUPPORTED, "kernels are built for width 1024, 16 heads, feedforward 4096 (got %d, %d, %d)",
                 c->width, c->heads, c->feedforward);
@@ -401,6 +403,10 @@ struct Weights {
   const bf16_t *Wmem, *Wmem16, *Wa7, *Wqq, *Wg, *Wkv, *Ws1;   // Wmem16 holds fp16 bits
   const bf16_t* Wfkv = nullptr;   // decoder-layer field variant: cross K/V of every field layer, stacked
   const float* bfkv = nullptr;
+  // precision mode fp32: the memory projection unfolded (LayerNorm applied to the rows) with its own bias,
+  // and the stacked K/V projections, all in the small GEMMs' fragment order
+  const float* bmem = nullptr;
+  const bf16_t *Wmem_fr = nullptr, *Wkv_fr = nullptr, *Wfkv_fr = nullptr;
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -583,6 +589,10 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     }
     put_bf(Wp.data(), Wp.size(), &W.Wmem);
     put_f(cm, &W.cmem);
+    if (c.precision == CLEF_PRECISION_F32) {
+      put_frag(Wm, D, H, &W.Wmem_fr);
+      put_f(bm, &W.bmem);
+    }
     put_bf(Wp16.data(), Wp16.size(), &W.Wmem16);
     put_f(cm16, &W.cmem16);
     put_f(dm, &W.dmem);
@@ -634,6 +644,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     if (NR > 0) {
       put_bf(Wkv.data(), Wkv.size(), &W.Wkv);
       put_f(bkv, &W.bkv);
+      if (c.precision == CLEF_PRECISION_F32) put_frag(Wkv.data(), NR * 2 * D, D, &W.Wkv_fr);
     } else {
       W.Wkv = nullptr;
       W.bkv = nullptr;
@@ -697,6 +708,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     }
     put_bf(Wf.data(), Wf.size(), &W.Wfkv);
     put_f(bfv, &W.bfkv);
+    if (c.precision == CLEF_PRECISION_F32) put_frag(Wf.data(), NL * 2 * D, D, &W.Wfkv_fr);
   }
   put_frag(bf("score.w1"), D, 4 * D, &W.Ws1);
   put_f(tof("score.b1"), &W.bs1);
@@ -746,13 +758,24 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.pooled = take((NQ + NO + p.nact) * H * 4);
   L.ebar = take(NO * H * 4);
   L.prior = take(NO * 4);
-  L.mem = take(Tp * D * 2);
-  L.kv = take(NR * 2 * NH * Tp * 64 * 2);
+  // memory rows and K/V: bf16, or fp32 in the fp32 precision mode
+  const bool f32 = c.precision == CLEF_PRECISION_F32;
+  const size_t el = f32 ? 4 : 2;
+  L.mem = take(Tp * D * el);
+  L.kv = take(NR * 2 * NH * Tp * 64 * el);
   const size_t NLx = c.field_cross_attention ? (size_t)c.layers : 0;   // field layers with cross-attention
-  L.fkv = take(NLx * 2 * NH * Tp * 64 * 2);
+  L.fkv = take(NLx * 2 * NH * Tp * 64 * el);
   // split-K partial sums of the big GEMMs (few row tiles only; the memory and
   // K/V GEMMs run one after the other on one stream and share the region)
-  {
+  if (f32) {   // the small-GEMM kernel over the packed rows
+    size_t fl = 0;
+    if (Tp > 0) {
+      fl = sgemm_shape((int)Tp, D, (int)H).part_floats;
+      if (NR > 0) fl = std::max(fl, sgemm_shape((int)Tp, (int)NR * 2 * D, D).part_floats);
+      if (NLx > 0) fl = std::max(fl, sgemm_shape((int)Tp, (int)NLx * 2 * D, D).part_floats);
+    }
+    L.bigpart = take(fl * 4);
+  } else {
     const size_t sm = big_gemm_split(p.ntiles, D / 256, (int)H), skv = big_gemm_split(p.ntiles, (int)NR * 8, D);
     const size_t sf = big_gemm_split(p.ntiles, (int)NLx * 8, D);
     size_t bytes = std::max(sm > 1 ? sm * Tp * D * 4 : 0, (NR > 0 && skv > 1) ? skv * Tp * NR * 2 * D * 4 : 0);
@@ -976,7 +999,10 @@ int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) 
   if (which == CLEF_TRACE_POOLED) { src = h->pooled; n = (NQ + NO + B) * H * 4; }
   else if (which == CLEF_TRACE_LEXICAL) { src = h->ebar; n = NO * H * 4; }
   else if (which == CLEF_TRACE_PRIOR) { src = h->prior; n = NO * 4; }
-  else if (which == CLEF_TRACE_MEMORY) { src = h->mem; n = (size_t)h->last_Tpad * D * 2; }
+  else if (which == CLEF_TRACE_MEMORY) {
+    src = h->mem;
+    n = (size_t)h->last_Tpad * D * (h->cfg.precision == CLEF_PRECISION_F32 ? 4 : 2);
+  }
   else if (which == CLEF_TRACE_F0) { src = h->tr_f0; n = NQ * D * 4; }
   else if (which == CLEF_TRACE_F) { src = h->tr_f; n = NQ * D * 4; }
   else if (which == CLEF_TRACE_JCOS) { src = h->tr_jcos; n = NO * 4; }
@@ -1150,6 +1176,12 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   const float eps = c.ln_eps;
   const bool joint = W.gate != 0.0f;
   const bool cross = c.field_cross_attention && NL > 0;   // decoder-layer field variant
+  // precision mode fp32: memory rows and K/V in fp32, every small GEMM's activations as 3 exact bf16 terms
+  const bool f32 = c.precision == CLEF_PRECISION_F32;
+  const int NT = f32 ? 3 : 2;
+  float* mem32 = reinterpret_cast<float*>(ws + L.mem);
+  float* kv32 = reinterpret_cast<float*>(ws + L.kv);
+  float* fkv32 = reinterpret_cast<float*>(ws + L.fkv);
 
   // stage timing: an event at every stage boundary, on the forward's stream
   std::vector<int> marks;
@@ -1196,12 +1228,31 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         std::lock_guard<std::mutex> lk(g.mu);
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
-      launch_gemm_mem(st, X, (int)H, p.f16, tiles, p.ntiles, p.f16 ? W.Wmem16 : W.Wmem, stats,
-                      p.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, p.Tpad);
-      MARK(CLEF_STAGE_MEMORY_GEMM);
-      launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad, bigpart);
-      if (cross) launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wfkv, W.bfkv, NL, fkv, p.Tpad, bigpart);
-      MARK(CLEF_STAGE_KV_GEMM);
+      if (f32) {
+        // normalised rows times the unfolded memory weight, then K/V into head-major fp32 planes
+        const int Tp = (int)p.Tpad;
+        if (p.f16)
+          launch_sgemm(st, LdHid<true>{X, (int)H, tiles, stats, W.lnin_g, W.lnin_b}, EpStore{mem32, D, W.bmem},
+                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 1);
+        else
+          launch_sgemm(st, LdHid<false>{X, (int)H, tiles, stats, W.lnin_g, W.lnin_b}, EpStore{mem32, D, W.bmem},
+                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 1);
+        MARK(CLEF_STAGE_MEMORY_GEMM);
+        if (NR > 0)
+          launch_sgemm(st, LdRows{mem32, D, nullptr}, EpHeads{kv32, p.Tpad, W.bkv}, W.Wkv_fr, Tp, NR * 2 * D, D,
+                       bigpart, nullptr, 0.f, 3, 1);
+        if (cross)
+          launch_sgemm(st, LdRows{mem32, D, nullptr}, EpHeads{fkv32, p.Tpad, W.bfkv}, W.Wfkv_fr, Tp, NL * 2 * D,
+                       D, bigpart, nullptr, 0.f, 3, 1);
+        MARK(CLEF_STAGE_KV_GEMM);
+      } else {
+        launch_gemm_mem(st, X, (int)H, p.f16, tiles, p.ntiles, p.f16 ? W.Wmem16 : W.Wmem, stats,
+                        p.f16 ? W.cmem16 : W.cmem, W.dmem, mem, bigpart, p.Tpad);
+        MARK(CLEF_STAGE_MEMORY_GEMM);
+        launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv, p.Tpad, bigpart);
+        if (cross) launch_gemm_kv(st, mem, kvtiles, p.ntiles, W.Wfkv, W.bfkv, NL, fkv, p.Tpad, bigpart);
+        MARK(CLEF_STAGE_KV_GEMM);
+      }
       if (fork) {
         std::lock_guard<std::mutex> lk(g.mu);
         HIPCHK(hipEventRecord(g.gemm_done, st));
@@ -1209,16 +1260,18 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
       }
     }
     // step 3: option queries (with the first routing LayerNorm statistics), question base and global projections
-    launch_sgemm(s2, LdRows{pooled, (int)H, nullptr}, EpSplit2{qv, qo, W.bqq}, W.Wqq, NQ, 2 * D, (int)H, part);
+    launch_sgemm(s2, LdRows{pooled, (int)H, nullptr}, EpSplit2{qv, qo, W.bqq}, W.Wqq, NQ, 2 * D, (int)H, part,
+                 nullptr, 0.f, NT);
     launch_sgemm(s2, LdSeg2{pooled + (size_t)NQ * H, ebar, (int)H}, EpAddRow{u, W.ba7, qo, optq}, W.Wa7, NO, D,
-                 2 * (int)H, part, ustats, eps);
+                 2 * (int)H, part, ustats, eps, NT);
     launch_sgemm(s2, LdRows{pooled + (size_t)(NQ + NO) * H, (int)H, nullptr}, EpStore{gp, D, W.bg}, W.Wg, p.nact, D,
-                 (int)H, part);
+                 (int)H, part, nullptr, 0.f, NT);
     MARK(CLEF_STAGE_QUERY_PROJ);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_u, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, s2));
     if (NR > 0) {
       const Layer& Ly = W.route[0];
-      launch_sgemm(s2, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
+      launch_sgemm(s2, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part,
+                   nullptr, 0.f, NT);
       MARK(CLEF_STAGE_ROUTE_DENSE);
     }
   }
@@ -1232,19 +1285,25 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   if (joint) {
     for (int r = 0; r < NR; ++r) {
       const Layer& Ly = W.route[r];
-      const bf16_t* Kl = kv + (size_t)(2 * r) * NH * p.Tpad * 64;
-      const bf16_t* Vl = kv + (size_t)(2 * r + 1) * NH * p.Tpad * 64;
+      const size_t plane = (size_t)NH * p.Tpad * 64;   // elements of one layer's K (or V), all heads
       if (r > 0) {
-        launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part);
+        launch_sgemm(st, LdLN{u, D, ustats, Ly.ln1g, Ly.ln1b}, EpStore{qbuf, D, Ly.bq}, Ly.Wq, NO, D, D, part,
+                     nullptr, 0.f, NT);
         MARK(CLEF_STAGE_ROUTE_DENSE);
       }
-      launch_route_attn(st, qbuf, Kl, Vl, p.Tpad, items, p.nitems, rec, pm, pl, po, p.Ptot, p.kchunk);
+      if (f32)
+        launch_route_attn32(st, qbuf, kv32 + (2 * r) * plane, kv32 + (2 * r + 1) * plane, p.Tpad, items, p.nitems,
+                            rec, pm, pl, po, p.Ptot, p.kchunk);
+      else
+        launch_route_attn(st, qbuf, kv + (2 * r) * plane, kv + (2 * r + 1) * plane, p.Tpad, items, p.nitems, rec,
+                          pm, pl, po, p.Ptot, p.kchunk);
       launch_route_combine(st, pm, pl, po, p.Ptot, optrec, rec, NO, attn);
       MARK(CLEF_STAGE_ROUTE_ATTN);
-      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, ustats, eps);
-      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part);
+      launch_sgemm(st, LdRows{attn, D, nullptr}, EpResid{u, D, Ly.bo}, Ly.Wo, NO, D, D, part, ustats, eps, NT);
+      launch_sgemm(st, LdLN{u, D, ustats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NO, F, D, part, nullptr,
+                   0.f, NT);
       launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{u, D, Ly.b2}, Ly.W2, NO, D, F, part,
-                   r + 1 < NR ? ustats : nullptr, eps);
+                   r + 1 < NR ? ustats : nullptr, eps, NT);
       MARK(CLEF_STAGE_ROUTE_DENSE);
       if (h->trace)
         HIPCHK(hipMemcpyAsync(h->tr_u + (size_t)(r + 1) * NO * D, u, (size_t)NO * D * 4, hipMemcpyDeviceToDevice, st));
@@ -1254,27 +1313,34 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f0, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     for (int l = 0; l < NL; ++l) {
       const Layer& Ly = W.field[l];
-      const SgemmShape gq = launch_sgemm_partial(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, Ly.Wqkv, NQ, 3 * D, D, part);
+      const SgemmShape gq =
+          launch_sgemm_partial(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, Ly.Wqkv, NQ, 3 * D, D, part, NT);
       launch_field_attn(st, part, gq.nsplit, (size_t)gq.mtiles * kSgemmRows * 3 * D, Ly.bqkv, rec, p.nact, fattn);
-      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps);
+      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps, NT);
       if (cross) {
         // cross-attention of the fields over the record's memory rows (the routing attention kernels with
         // the fields as queries), pre-LN, residual
-        const bf16_t* FK = fkv + (size_t)(2 * l) * NH * p.Tpad * 64;
-        const bf16_t* FV = fkv + (size_t)(2 * l + 1) * NH * p.Tpad * 64;
-        launch_sgemm(st, LdLN{f, D, fstats, Ly.xlng, Ly.xlnb}, EpStore{qbuf, D, Ly.bxq}, Ly.Wxq, NQ, D, D, part);
-        launch_route_attn(st, qbuf, FK, FV, p.Tpad, fitems, p.nfitems, frec, pm, pl, po, p.Ptot_f, p.kchunk);
+        const size_t plane = (size_t)NH * p.Tpad * 64;
+        launch_sgemm(st, LdLN{f, D, fstats, Ly.xlng, Ly.xlnb}, EpStore{qbuf, D, Ly.bxq}, Ly.Wxq, NQ, D, D, part,
+                     nullptr, 0.f, NT);
+        if (f32)
+          launch_route_attn32(st, qbuf, fkv32 + (2 * l) * plane, fkv32 + (2 * l + 1) * plane, p.Tpad, fitems,
+                              p.nfitems, frec, pm, pl, po, p.Ptot_f, p.kchunk);
+        else
+          launch_route_attn(st, qbuf, fkv + (2 * l) * plane, fkv + (2 * l + 1) * plane, p.Tpad, fitems, p.nfitems,
+                            frec, pm, pl, po, p.Ptot_f, p.kchunk);
         launch_route_combine(st, pm, pl, po, p.Ptot_f, qrec, frec, NQ, fattn);
-        launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bxo}, Ly.Wxo, NQ, D, D, part, fstats, eps);
+        launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bxo}, Ly.Wxo, NQ, D, D, part, fstats, eps, NT);
       }
-      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part);
+      launch_sgemm(st, LdLN{f, D, fstats, Ly.ln2g, Ly.ln2b}, EpGelu{hbuf, F, Ly.b1}, Ly.W1, NQ, F, D, part, nullptr,
+                   0.f, NT);
       launch_sgemm(st, LdRows{hbuf, F, nullptr}, EpResid{f, D, Ly.b2}, Ly.W2, NQ, D, F, part,
-                   l + 1 < NL ? fstats : nullptr, eps);
+                   l + 1 < NL ? fstats : nullptr, eps, NT);
     }
     MARK(CLEF_STAGE_FIELD);
     if (h->trace) HIPCHK(hipMemcpyAsync(h->tr_f, f, (size_t)NQ * D * 4, hipMemcpyDeviceToDevice, st));
     // step 5: residual-MLP hidden layer over [f, u, f*u, |f-u|]
-    gs = launch_sgemm_partial(st, LdZ{f, u, optq}, W.Ws1, NO, D, 4 * D, part);
+    gs = launch_sgemm_partial(st, LdZ{f, u, optq}, W.Ws1, NO, D, 4 * D, part, NT);
   }
   launch_score(st, u, f, part, gs.nsplit, (size_t)gs.mtiles * kSgemmRows * D, W.bs1, W.ws2, W.bs2, prior, W.gate,
                W.lam, joint ? 1 : 0, ooff, NQ, logits, probs, argmax,
@@ -1343,6 +1409,8 @@ static int stream_plan(clef_head* h, const clef_head_batch* batch, Plan& p) {
 int clef_head_stream_begin(clef_head* h, const clef_head_batch* batch, void* hip_stream) {
   if (!h) return fail(CLEF_E_ARG, "handle is NULL");
   if (h->strm.active) return fail(CLEF_E_ARG, "a streamed batch is already in progress on this handle");
+  if (h->cfg.precision == CLEF_PRECISION_F32)
+    return fail(CLEF_E_UNSUPPORTED, "streamed ingest runs in the bf16 precision mode only");
   Plan p;
   int rc = stream_plan(h, batch, p);
   if (rc) return rc;

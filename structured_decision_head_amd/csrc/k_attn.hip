@@ -187,6 +187,123 @@ void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const b
                      rec, pm, pl, po, Ptot, chunk, scale_log2);
 }
 
+// fp32 routing attention (precision mode fp32): one 256-thread block per
+// (work item, head).  Thread t owns query t / 8 of the item's 32-query block
+// and 8 of its 64 dims (t % 8); a score is the sum of the 8 parts' dot
+// products (three lane exchanges).  Keys and values are staged in LDS 64 rows
+// at a time; the online softmax takes 8 keys per step (one rescale per step).
+// The queries carry log2(e) / sqrt(64) and the partials are written exactly as
+// k_route_attn writes them, so k_route_combine merges either.
+__global__ __launch_bounds__(256) void k_route_attn32(const float* __restrict__ Q, const float* __restrict__ Kl,
+                                                      const float* __restrict__ Vl, long long Tpad,
+                                                      const int4* __restrict__ items, const int* __restrict__ rec,
+                                                      float* __restrict__ pm, float* __restrict__ pl,
+                                                      float* __restrict__ po, long long Ptot, int chunk,
+                                                      float scale_log2) {
+  __shared__ float4 sK[64][16], sV[64][16];
+  const int j = blockIdx.y;
+  const int4 bc = items[blockIdx.x];     // (record, chunk, first query of the block, -)
+  const int* R = rec + 8 * bc.x;
+  const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
+  const int c = bc.y;
+  const int k_lo = c * chunk, k_hi = min(n, k_lo + chunk);   // every chunk holds at least one key
+  const float* Kj = Kl + (size_t)j * Tpad * 64;
+  const float* Vj = Vl + (size_t)j * Tpad * 64;
+  const int t = threadIdx.x, part = t & 7;
+  const int qi = bc.z + (t >> 3);
+  const bool qvalid = qi < no;
+  float q[8], o[8];
+  {
+    const float* qp = Q + (size_t)(o0 + (qvalid ? qi : 0)) * 1024 + j * 64 + part * 8;
+    const float4 a = *reinterpret_cast<const float4*>(qp), b = *reinterpret_cast<const float4*>(qp + 4);
+    f4x2(a, b, q);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      q[d] = qvalid ? q[d] * scale_log2 : 0.f;
+      o[d] = 0.f;
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int kb = k_lo; kb < k_hi; kb += 64) {
+    const int nk = min(64, k_hi - kb);
+    __syncthreads();   // the previous tile has been read
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int idx = t + 256 * r4, row = idx >> 4, c4 = idx & 15;
+      if (row < nk) {
+        const size_t off = (size_t)(kv0 + kb + row) * 64 + 4 * c4;
+        sK[row][c4] = *reinterpret_cast<const float4*>(Kj + off);
+        sV[row][c4] = *reinterpret_cast<const float4*>(Vj + off);
+      }
+    }
+    __syncthreads();
+    for (int k8 = 0; k8 < nk; k8 += 8) {
+      const int kn = min(8, nk - k8);   // uniform over the block
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s[i] = 0.f;
+        if (i < kn) {
+          float kk[8];
+          f4x2(sK[k8 + i][2 * part], sK[k8 + i][2 * part + 1], kk);
+#pragma unroll
+          for (int d = 0; d < 8; ++d) s[i] += q[d] * kk[d];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s[i] += __shfl_xor(s[i], 1, 64);
+        s[i] += __shfl_xor(s[i], 2, 64);
+        s[i] += __shfl_xor(s[i], 4, 64);
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i)
+        if (i < kn) mx = fmaxf(mx, s[i]);
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);   // m = -inf gives 0
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = i < kn ? exp2f(s[i] - mn) : 0.f;
+        ps += p[i];
+      }
+      l = l * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < kn) {
+          float vv[8];
+          f4x2(sV[k8 + i][2 * part], sV[k8 + i][2 * part + 1], vv);
+#pragma unroll
+          for (int d = 0; d < 8; ++d) o[d] += p[i] * vv[d];
+        }
+      }
+    }
+  }
+  if (qvalid) {
+    const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
+    if (part == 0) {
+      pm[slot] = m;
+      pl[slot] = l;
+    }
+    float* op = po + slot * 64 + part * 8;
+    *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+void launch_route_attn32(hipStream_t st, const float* Q, const float* Kl, const float* Vl, long long Tpad,
+                         const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                         long long Ptot, int chunk) {
+  if (nitems == 0) return;
+  const float scale_log2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
+  hipLaunchKernelGGL(k_route_attn32, dim3(nitems, 16), dim3(256), 0, st, Q, Kl, Vl, Tpad, items, rec, pm, pl, po,
+                     Ptot, chunk, scale_log2);
+}
+
 // Merge the chunk partials of (option, head): one wave.  Lanes split the
 // chunks to find the global max and the softmax denominator; then lane d sums
 // the rescaled unnormalised outputs of every chunk for output dim d, with the

@@ -5,10 +5,13 @@
 // until the grid fills the chip and the partial sums are reduced by the last
 // second kernel that adds the slices in a fixed order (deterministic).
 //
-// Precision: activations are fp32; each 8-element group is split into
-// hi = bf16(x) and lo = bf16(x - hi) and both are multiplied against the exact
-// bf16 weights with v_mfma_f32_16x16x32_bf16, so the product carries about 16
-// significant bits of the activation and fp32 accumulation.
+// Precision: activations are fp32; each 8-element group is split into NT bf16
+// terms (NT = 2: hi = bf16(x), lo = bf16(x - hi), about 16 significant bits of
+// x; NT = 3: a third term bf16(x - hi - lo) makes the sum exact, every fp32
+// value being the sum of three bf16 values) and every term is multiplied
+// against the exact bf16 weights with v_mfma_f32_16x16x32_bf16 into fp32
+// accumulators.  With NT = 3 the products are exact and only the fp32
+// accumulation rounds: the accuracy of an fp32 GEMM.
 //
 // Prologues (how A rows are formed) and epilogues (what is done with each
 // output) are small functors; see kernels.hpp.
@@ -20,21 +23,45 @@ namespace {
 
 constexpr int SBM = kSgemmRows, SKC = 128;
 
+// Split 8 floats into NT bf16 terms whose sum approximates (NT = 2) or equals
+// (NT = 3) each float: t0 = bf16(x), t1 = bf16(x - t0), t2 = bf16(x - t0 - t1).
+// Every difference is exact in fp32 (x - bf16(x) needs at most 16 significant
+// bits, and the next remainder at most 8).
+template <int NT>
+DEV void split_terms(const float* f, uint4 (&t)[NT]) {
+  float r[8], h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = f[i];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    t[j] = pack8(r);
+    if (j + 1 < NT) {
+      unpack8(t[j], h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] -= h[i];
+    }
+  }
+}
+
 // Tile: 64 rows x (32 * 4 / WR) columns.  The 4 waves form a WR x (4 / WR)
 // grid; each wave owns 64 / WR rows and 32 columns.  Narrow tiles (WR = 2, 4)
 // give more workgroups for narrow outputs, so that the whole chip streams
 // the weights.
-template <int WR, class Ld, class Epi>
+// order = 0: consecutive workgroups walk the row tiles of one column tile (the
+// weights of that column tile stay in the XCD's L2); order = 1: they walk the
+// column tiles of one row tile (that row tile's A rows stay in L2), for
+// products with many row tiles and few weights.
+template <int WR, int NT, class Ld, class Epi>
 __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __restrict__ W, int M, int N,
-                                               int K, int kchunk, int mtiles, int ntiles, int nsplit,
+                                               int K, int kchunk, int mtiles, int ntiles, int nsplit, int order,
                                                float* __restrict__ part) {
   constexpr int WC = 4 / WR, SBN = 32 * WC, RB = 4 / WR;
-  // two buffers of the converted A chunk: [buffer][row * 16 + swizzled chunk], KC = 128 bf16 per row
-  __shared__ uint4 sAh[2][SBM * 16], sAl[2][SBM * 16];
+  // two buffers of each converted A term: [term][buffer][row * 16 + swizzled chunk], KC = 128 bf16 per row
+  __shared__ uint4 sA[NT][2][SBM * 16];
 
   const int lt = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = lt % mtiles;
-  const int tn = (lt / mtiles) % ntiles;
+  const int tm = order ? (lt / ntiles) % mtiles : lt % mtiles;
+  const int tn = order ? lt % ntiles : (lt / mtiles) % ntiles;
   const int ks = lt / (mtiles * ntiles);
   const int m0 = tm * SBM, n0 = tn * SBN;
   const int kb = ks * kchunk, ke = min(K, kb + kchunk);
@@ -87,11 +114,10 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
       } else {                                                                           \
         _Pragma("unroll") for (int e = 0; e < 8; ++e) x[e] = 0.f;                        \
       }                                                                                  \
-      uint4 hi, lo;                                                                      \
-      split8(x, hi, lo);                                                                 \
+      uint4 tt[NT];                                                                      \
+      split_terms<NT>(x, tt);                                                            \
       const int idx = r * 16 + (c ^ (r & 15));                                           \
-      sAh[BUF][idx] = hi;                                                                \
-      sAl[BUF][idx] = lo;                                                                \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) sA[j][BUF][idx] = tt[j];            \
     }                                                                                    \
   }
   SG_FETCH_A(kb)
@@ -117,13 +143,15 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int r = wr0 + rb * 16 + (lane & 15);
-        const bf16x8 ah = as_bf16x8(sAh[buf][r * 16 + (c ^ (r & 15))]);
-        const bf16x8 al = as_bf16x8(sAl[buf][r * 16 + (c ^ (r & 15))]);
+        bf16x8 a[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) a[j] = as_bf16x8(sA[j][buf][r * 16 + (c ^ (r & 15))]);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           const bf16x8 b = as_bf16x8(bc[cb][kk]);
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[rb][cb], 0, 0, 0);
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[rb][cb], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, acc[rb][cb], 0, 0, 0);
         }
       }
     }
@@ -227,27 +255,34 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce, bool consumer_sums
   return s;
 }
 
-template <class Ld, class Epi>
-static void launch_tile(const SgemmShape& s, hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M,
-                        int N, int K, float* part) {
+template <int NT, class Ld, class Epi>
+static void launch_tile_nt(const SgemmShape& s, hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W,
+                           int M, int N, int K, int order, float* part) {
   const dim3 grid(s.mtiles * s.ntiles * s.nsplit);
   if (s.wr == 1)
-    hipLaunchKernelGGL((k_sgemm<1, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
-                       s.ntiles, s.nsplit, part);
+    hipLaunchKernelGGL((k_sgemm<1, NT, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, order, part);
   else if (s.wr == 2)
-    hipLaunchKernelGGL((k_sgemm<2, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
-                       s.ntiles, s.nsplit, part);
+    hipLaunchKernelGGL((k_sgemm<2, NT, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, order, part);
   else
-    hipLaunchKernelGGL((k_sgemm<4, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
-                       s.ntiles, s.nsplit, part);
+    hipLaunchKernelGGL((k_sgemm<4, NT, Ld, Epi>), grid, dim3(256), 0, st, ld, epi, W, M, N, K, s.kchunk, s.mtiles,
+                       s.ntiles, s.nsplit, order, part);
+}
+
+template <class Ld, class Epi>
+static void launch_tile(const SgemmShape& s, hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M,
+                        int N, int K, float* part, int nt, int order) {
+  if (nt == 3) launch_tile_nt<3>(s, st, ld, epi, W, M, N, K, order, part);
+  else launch_tile_nt<2>(s, st, ld, epi, W, M, N, K, order, part);
 }
 
 template <class Ld, class Epi>
 void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W, int M, int N, int K,
-                  float* part, float2* stats, float eps) {
+                  float* part, float2* stats, float eps, int nt, int order) {
   if (M == 0) return;
   const SgemmShape s = sgemm_shape(M, N, K, stats != nullptr);
-  launch_tile(s, st, ld, epi, W, M, N, K, part);
+  launch_tile(s, st, ld, epi, W, M, N, K, part, nt, order);
   if (s.nsplit > 1) {
     const size_t n4 = (size_t)M * N / 4;
     hipLaunchKernelGGL((k_splitk_reduce<Epi>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, s.nsplit,
@@ -256,24 +291,28 @@ void launch_sgemm(hipStream_t st, const Ld& ld, const Epi& epi, const bf16_t* W,
 }
 
 template <class Ld>
-SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, int M, int N, int K, float* part) {
+SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, int M, int N, int K, float* part,
+                                int nt) {
   const SgemmShape s = sgemm_shape(M, N, K, false, true);
   if (M == 0) return s;
-  launch_tile(s, st, ld, EpPart{part, N}, W, M, N, K, part);
+  launch_tile(s, st, ld, EpPart{part, N}, W, M, N, K, part, nt, 0);
   return s;
 }
-template SgemmShape launch_sgemm_partial<LdLN>(hipStream_t, const LdLN&, const bf16_t*, int, int, int, float*);
-template SgemmShape launch_sgemm_partial<LdZ>(hipStream_t, const LdZ&, const bf16_t*, int, int, int, float*);
+template SgemmShape launch_sgemm_partial<LdLN>(hipStream_t, const LdLN&, const bf16_t*, int, int, int, float*, int);
+template SgemmShape launch_sgemm_partial<LdZ>(hipStream_t, const LdZ&, const bf16_t*, int, int, int, float*, int);
 
 #define INST(LD, EP)                                                                                   \
   template void launch_sgemm<LD, EP>(hipStream_t, const LD&, const EP&, const bf16_t*, int, int, int, \
-                                     float*, float2*, float);
+                                     float*, float2*, float, int, int);
 INST(LdRows, EpStore)
 INST(LdRows, EpResid)
 INST(LdLN, EpStore)
 INST(LdLN, EpGelu)
 INST(LdSeg2, EpAddRow)
 INST(LdRows, EpSplit2)
+INST(LdHid<false>, EpStore)
+INST(LdHid<true>, EpStore)
+INST(LdRows, EpHeads)
 #undef INST
 
 }  // namespace clef

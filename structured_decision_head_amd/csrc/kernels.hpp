@@ -105,6 +105,43 @@ struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
   }
 };
 
+// A[m] = LayerNorm(hidden row of packed row m) (precision mode fp32: the
+// memory projection multiplies normalised rows, with nothing folded into the
+// weights).  The packed row space is cut into 256-row tiles, tiles[m / 256] =
+// (first hidden row, first packed row, valid rows, record); rows past a tile's
+// valid count are never read and enter as zeros (their statistics are (0, 0)).
+template <bool F16>
+struct LdHid {
+  const bf16_t* X;
+  int H;
+  const int4* tiles;
+  const float2* stats;
+  const float* g;
+  const float* b;
+  struct Raw { uint4 v; float2 s; };
+  struct Cst { float4 g0, g1, b0, b1; };
+  DEV Raw fetch(int m, int k) const {
+    const int4 t = tiles[m >> 8];
+    const int r = m & 255;
+    Raw raw;
+    raw.s = stats[m];
+    raw.v = r < t.z ? *reinterpret_cast<const uint4*>(X + (size_t)(t.x + r) * H + k) : make_uint4(0u, 0u, 0u, 0u);
+    return raw;
+  }
+  DEV Cst cst(int k) const {
+    return Cst{*reinterpret_cast<const float4*>(g + k), *reinterpret_cast<const float4*>(g + k + 4),
+               *reinterpret_cast<const float4*>(b + k), *reinterpret_cast<const float4*>(b + k + 4)};
+  }
+  DEV void finish(const Raw& r, const Cst& c, int, int, float* x) const {
+    float v[8], gg[8], bb[8];
+    unpack8_hidden<F16>(r.v, v);
+    f4x2(c.g0, c.g1, gg);
+    f4x2(c.b0, c.b1, bb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (v[i] - r.s.x) * r.s.y * gg[i] + bb[i];
+  }
+};
+
 struct LdSeg2 {          // A[m] = [p0[m] | p1[m]], each H wide
   const float* p0;
   const float* p1;
@@ -247,6 +284,25 @@ struct EpResid {         // C += acc + bias (residual stream)
   }
 };
 
+struct EpHeads {         // C = acc + bias into head-major planes: columns [64 p, 64 p + 64) -> plane p of Tpad rows
+  float* C;
+  long long Tpad;
+  const float* bias;
+  DEV float* at(int m, int n) const { return C + ((size_t)(n >> 6) * Tpad + m) * 64 + (n & 63); }
+  DEV float operator()(int m, int n, float v) const {
+    const float r = v + bias[n];
+    *at(m, n) = r;
+    return r;
+  }
+  struct Pre { float4 b; };
+  DEV Pre pre4(int, int n) const { return Pre{ld_f4(bias + n)}; }
+  DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {   // the 4 columns never straddle a plane
+    const float4 r = add_f4(v, p.b);
+    st_f4(at(m, n), r);
+    return r;
+  }
+};
+
 struct EpPart {          // C = acc (one raw split-K slice; the consumer adds the bias)
   float* C;
   int ldc;
@@ -285,14 +341,18 @@ SgemmShape sgemm_shape(int M, int N, int K, bool need_reduce = false, bool consu
 
 // stats != nullptr (N must be 1024): the reduction pass also writes the
 // LayerNorm statistics (mean, 1/sqrt(var + eps)) of every finished output row.
+// nt: bf16 terms per fp32 activation (2: about 16 significant bits; 3: exact,
+// the fp32 precision mode).  order: tile walk (0: row tiles of one column tile
+// consecutive; 1: column tiles of one row tile consecutive).
 template <class Ld, class Epi>
 void launch_sgemm(hipStream_t, const Ld&, const Epi&, const bf16_t* W, int M, int N, int K, float* part,
-                  float2* stats = nullptr, float eps = 0.f);
+                  float2* stats = nullptr, float eps = 0.f, int nt = 2, int order = 0);
 
 // No reduction pass: slice q of A W^T (without bias) is left at
 // part + (q * mtiles * kSgemmRows + m) * N + n for the consumer to sum.
 template <class Ld>
-SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, int N, int K, float* part);
+SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, int N, int K, float* part,
+                                int nt = 2);
 
 // ---------------------------------------------------------------------------
 // attention
@@ -303,6 +363,12 @@ SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, 
 void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16_t* Vl, long long Tpad,
                        const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
                        long long Ptot, int chunk);
+// fp32 form (precision mode fp32): the same items, partials and scaling, over
+// fp32 K and V held in head-major planes of Tpad rows x 64 floats (head j of
+// the layer at Kl + j * Tpad * 64), fp32 arithmetic throughout.
+void launch_route_attn32(hipStream_t, const float* Q, const float* Kl, const float* Vl, long long Tpad,
+                         const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
+                         long long Ptot, int chunk);
 void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
                           const int* opt_rec, const int* rec, int NO, float* out);
 // QKV: split-K slices (nsplit, slice stride in floats, row width 3072) + bias

@@ -77,6 +77,7 @@ class HeadConfig:
     num_types: int = 3
     ln_eps: float = 1e-5
     field_cross_attention: int = 0   # 1: field layers also cross-attend over the record's memory rows
+    precision: int = 0               # arithmetic of the library (0 bf16, 1 fp32); the generated values do not depend on it
 
 
 def weight_specs(c: HeadConfig) -> List[Tuple[str, Tuple[int, ...], str, int]]:

@@ -1,0 +1,156 @@
+"""GPU parity of the fp32 precision mode (CLEF_PRECISION_F32): the head in
+fp32 arithmetic, as the CoreML packaging of clef-flash runs it on fp16 hidden
+states (CoreML conversion metadata page, decision.head, dtype_of_record).
+
+Tolerance (derived from the arithmetic).  Every product of the mode is exact
+(bf16 weights times activations split into three bf16 terms, or fp32 VALU
+products in attention) and only fp32 accumulation rounds, unit roundoff
+u = 2^-24.  A length-K accumulation of O(1) terms then errs by about
+sqrt(K) u relative (K <= 8192: <= 5.4e-6); a logit passes through about 26
+dependent accumulations (option query, 2 routing layers of 4 products, 4
+field layers of 4 products, the scoring layer), so its error stays below
+26 x 5.4e-6 = 1.4e-4 even when those errors add up, and far below when they
+are independent.  Hence max |d logit| <= 1e-4 against the fp64 oracle (at
+logits of size O(1)) and, since a softmax probability moves by at most half
+the largest logit change, max |d prob| <= 5e-5: 200 and 40 times tighter
+than the bf16 mode's 2e-2 and 2e-3.  A float32 evaluation of the oracle's
+own steps lands at |d logit| ~ 2e-6 on these inputs.  Argmax must equal the
+oracle's."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import head as O
+from parity import compare, local_offsets, oracle_outputs, say, select
+from structured_decision_head_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL32_LOGIT = 1e-4
+TOL32_PROB = 5e-5
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from structured_decision_head_amd import clefhead
+    clefhead.load()
+    return torch
+
+
+def f32(spec):
+    return dataclasses.replace(spec, head=dataclasses.replace(spec.head, precision=1))
+
+
+def _run(case, layout=None, trace=False):
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd.runner import HeadRunner
+    r = HeadRunner(case)
+    r.set_trace(trace)
+    r.set_batch(None, C.CLEF_PADDED if layout is None else layout)
+    r.forward()
+    return r, r.outputs()
+
+
+def _check(case, out, name, recs=None):
+    b = case.batch
+    recs = [r for r in range(b.B) if int(b.q_offsets[r + 1]) > int(b.q_offsets[r])] if recs is None else recs
+    ref = oracle_outputs(case, records=recs)
+    compare(f"{name} ({len(recs)} records)", select(b, recs, *out), ref, local_offsets(b, recs),
+            tol_logit=TOL32_LOGIT, tol_prob=TOL32_PROB)
+    return ref
+
+
+@pytest.mark.parametrize("hidden", ["f16", "bf16"])
+def test_f32_single_record_stages(torch_gpu, hidden):
+    """Every traced intermediate of the single record against the oracle's."""
+    from structured_decision_head_amd import clefhead as C
+    case = synth.make_case(f32(dataclasses.replace(synth.config_spec(0), hidden_dtype=hidden)))
+    say(f"case single record, fp32 mode, {hidden} hidden")
+    r, out = _run(case, trace=True)
+    b = case.batch
+    p = O.load_params(case.weights)
+    tr = {}
+    ido = b.o_id_offsets()
+    n = int(b.lengths[0])
+    O.forward_record(p, case.head, O.hidden_rows(b, 0, n), b.q_type, b.q_span, b.o_offsets, b.o_span,
+                     [O.from_bf16(case.table[b.o_ids[ido[k]: ido[k + 1]]]) for k in range(b.NO)], trace=tr)
+    H, D = case.head.hidden_size, case.head.width
+
+    def rel(a, ref):
+        return float(np.abs(a - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+    stages = {"memory": rel(r.trace(C.CLEF_TRACE_MEMORY, (256, D))[:n], tr["memory"])}
+    for i in range(case.head.routing_layers + 1):
+        stages[f"u{i}"] = rel(r.trace(C.CLEF_TRACE_U + i, (b.NO, D)), tr["u_layers"][i])
+    stages["f0"] = rel(r.trace(C.CLEF_TRACE_F0, (b.NQ, D)), tr["f0"])
+    stages["f"] = rel(r.trace(C.CLEF_TRACE_F, (b.NQ, D)), tr["f"])
+    stages["jcos"] = rel(r.trace(C.CLEF_TRACE_JCOS, (b.NO,)), tr["joint_cos"])
+    stages["mlp"] = rel(r.trace(C.CLEF_TRACE_MLP, (b.NO,)), tr["mlp"])
+    say("  stage max relative error: " + ", ".join(f"{k}={v:.2e}" for k, v in stages.items()))
+    for k, v in stages.items():
+        assert v < 2e-5, (k, v)   # bf16 mode: memory rows alone carry ~4e-3
+    r.close()
+    compare("single record fp32", out, oracle_outputs(case), b.o_offsets, tol_logit=TOL32_LOGIT, tol_prob=TOL32_PROB)
+
+
+def test_f32_online_serving_full_size_f16_hidden(torch_gpu):
+    """The online-serving batch (B=8, L=4096) at full size, fp16 hidden rows."""
+    case = synth.make_case(f32(dataclasses.replace(synth.config_spec(1), hidden_dtype="f16")))
+    b = case.batch
+    say(f"case online-serving full size, fp32 mode, fp16 hidden: B={b.B} T={int(b.lengths.sum())} NO={b.NO}")
+    r, out = _run(case)
+    r.close()
+    _check(case, out, "online-serving fp32")
+
+
+def test_f32_h5120_padded_vs_varlen_nan_padding(torch_gpu):
+    """H=5120 with NaN padding rows: the normalised-row loader never reads
+    them; padded and varlen runs agree bit for bit."""
+    from structured_decision_head_amd import clefhead as C
+    spec = f32(synth.config_spec(4, B=5, lengths=("loguniform", 300, 2500), hidden_dtype="f16", vocab_size=4096))
+    case = synth.make_case(spec)
+    b = case.batch
+    say(f"case H=5120 fp32 mode, NaN padding: B={b.B} L={b.L} lengths={b.lengths.tolist()}")
+    r, op = _run(case, C.CLEF_PADDED)
+    r.set_batch(None, C.CLEF_VARLEN)
+    r.forward()
+    ov = r.outputs()
+    r.close()
+    for a, c in zip(op, ov):
+        assert np.array_equal(a, c)
+    _check(case, op, "H=5120 fp32")
+
+
+def test_f32_decoder_fields_and_gate_closed(torch_gpu):
+    """The decoder-layer field variant in fp32 mode on a ragged batch; and the
+    gate closed, where the logits are the prior."""
+    import math
+    spec = f32(synth.config_spec(1, B=3, L=1100, lengths=("uniform", 600, 1100),
+                                 head=synth.HeadConfig(vocab_size=4096, field_cross_attention=1)))
+    case = synth.make_case(spec)
+    say("case mini ragged, decoder-layer fields, fp32 mode")
+    r, out = _run(case)
+    r.close()
+    _check(case, out, "decoder fp32")
+    case = synth.make_case(dataclasses.replace(spec, gate_logit=-math.inf,
+                                               head=dataclasses.replace(spec.head, field_cross_attention=0)))
+    say("case mini ragged, gate closed, fp32 mode")
+    r, out = _run(case)
+    r.close()
+    _check(case, out, "gate closed fp32")
+
+
+def test_f32_refuses_streamed_ingest(torch_gpu):
+    from structured_decision_head_amd import clefhead as C
+    from structured_decision_head_amd.runner import HeadRunner
+    case = synth.make_case(f32(synth.config_spec(0)))
+    r = HeadRunner(case)
+    r.set_batch(None, C.CLEF_VARLEN)
+    with pytest.raises(C.ClefError) as e:
+        C.clef_head_stream_begin(r.handle, r.args)
+    assert e.value.code == C.CLEF_E_UNSUPPORTED
+    r.close()
