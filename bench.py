@@ -10,12 +10,16 @@ of device weights (clef_head_create_sharing), each with its own inputs,
 workspace and stream, and step i runs on head i mod n, so one batch's
 latency-bound small-GEMM chain overlaps the next batch's big GEMMs.  The
 same K steps on a single head and stream are timed too (one batch at a
-time: the per-batch latency).  Prints one JSON line: records/s for the
-whole job, per-stage GPU times from HIP events recorded on the forward's
-stream, the roofline of the dominant kernel, and the fp64 oracle timed on
-the host cores over a bounded sample of the same workload.
+time: the per-batch latency), with HIP events around every forward on its
+stream for the median and p95 latency, once warm (back-to-back) and once
+cold (a 512 MiB buffer written between forwards, so the ~210 MB of weights
+no longer sit in the 256 MB memory-side cache).  Prints one JSON line:
+records/s for the whole job, latency statistics, per-stage GPU times from
+HIP events recorded on the forward's stream with each stage's fraction of
+its roofline, the roofline of the dominant kernel, and the fp64 oracle timed
+on the host cores over a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config 1] [--in-flight 2]
+    python bench.py [--steps K] [--warmup W] [--config 1] [--in-flight 2] [--precision bf16|f32]
 """
 from __future__ import annotations
 
@@ -30,7 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+COLD_BYTES = 512 << 20         # written between forwards for the cold-cache latency
 
 WORKLOADS = {
     0: "single record: B=1, L=160, H=4096, 1 noul + 1 choice field, V=8192",
@@ -67,6 +73,42 @@ def load_traffic(stage, cfg_index):
     if t.get("source_sha") != kernel_sources_sha(t.get("sources", [])):
         return None
     return t.get("bytes_per_launch")
+
+
+def host_info():
+    """Core count, affinity, CPU model and BLAS library of the host the oracle runs on."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"host_cpu_count": os.cpu_count(), "host_affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": model, "blas": ", ".join(blas) or None}, threads
+
+
+def latency(runner, stream, k, torch, np, cold=None):
+    """Median and p95 (us) of k forwards one at a time on one stream, each
+    bracketed by HIP events on that stream; with `cold`, the buffer is written
+    on the same stream before every forward (outside the bracket)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    with torch.cuda.stream(stream):
+        for i in range(k):
+            if cold is not None:
+                cold.fill_(i & 0xff)
+            ev[i][0].record(stream)
+            runner.forward(stream)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    return {"median": round(float(np.median(d)), 1), "p95": round(float(np.percentile(d, 95)), 1), "steps": k}
 
 
 def streamed_ingest(args, C, HeadRunner, case, runner, torch, np, H):
@@ -118,6 +160,9 @@ def main():
                     help="decoder-layer reading of the field layers (cross-attention over the memory rows)")
     ap.add_argument("--hidden", choices=("bf16", "f16"), default="bf16",
                     help="element type of the hidden states (f16: the CoreML packaging's fp16 hidden)")
+    ap.add_argument("--precision", choices=("bf16", "f32"), default="bf16",
+                    help="arithmetic of the head (f32: CLEF_PRECISION_F32)")
+    ap.add_argument("--cold-steps", type=int, default=30, help="forwards of the cold-cache latency (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streamed-ingest measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -147,8 +192,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
         return
     t = time.time()
+    f32 = args.precision == "f32"
     case = synth.config_case(args.config, hidden_dtype=args.hidden,
-                             field_cross_attention=int(args.field_cross_attention))
+                             field_cross_attention=int(args.field_cross_attention), precision=int(f32))
     b = case.batch
     H, D = case.head.hidden_size, case.head.width
     T = int(b.lengths.sum())
@@ -183,6 +229,15 @@ def main():
     ms_per_step = timed(len(runners))
     ms_one = timed(1) if len(runners) > 1 else ms_per_step
     log(f"{ms_per_step * 1e3:.1f} us per forward with {len(runners)} in flight; {ms_one * 1e3:.1f} us one at a time")
+    # latency per forward (HIP events), warm and cold
+    lat = latency(runner, streams[0], args.steps, torch, np)
+    cold = None
+    if args.cold_steps > 0:
+        buf = torch.empty(COLD_BYTES, dtype=torch.uint8, device="cuda")
+        cold = latency(runner, streams[0], args.cold_steps, torch, np, cold=buf)
+        cold["between_forwards"] = "512 MiB written by a fill kernel on the forward's stream"
+        del buf
+    log(f"latency us: warm {lat}, cold {cold}")
 
     # per-stage GPU time over the same number of forwards (events on the forward's stream)
     C.clef_head_set_profiling(h, True)
@@ -196,34 +251,49 @@ def main():
     # emits them, chunk k of every record before chunk k + 1): the work left after the last chunk
     # (clef_head_stream_end) is the head's latency once the backbone is done
     stream = None
-    if not args.no_stream:
+    if not args.no_stream and not f32:   # streamed ingest runs in the bf16 mode only
         stream = streamed_ingest(args, C, HeadRunner, case, runner, torch, np, H)
         log(f"streamed ingest: {stream}")
     log("stage us: " + ", ".join(f"{k}={v:.1f}" for k, v in stage_us.items()))
     lg, pr, am = runner.outputs()
 
-    NR = case.head.routing_layers
-    gemm_flops = {"memory_gemm": 2.0 * T * H * D, "kv_gemm": 2.0 * T * D * (2 * D * NR)}
+    NR, NL = case.head.routing_layers, case.head.layers
+    # the K/V stage also computes the field layers' cross K/V in the decoder-layer variant
+    kv_layers = NR + (NL if args.field_cross_attention else 0)
+    gemm_flops = {"memory_gemm": 2.0 * T * H * D, "kv_gemm": 2.0 * T * D * (2 * D * kv_layers)}
     dominant = max(gemm_flops, key=lambda k: stage_us[k])
     achieved = gemm_flops[dominant] / (stage_us[dominant] * 1e-6) / 1e12
-    # counters were taken on the bf16 memory GEMM; the fp16 one is another kernel
-    traffic = load_traffic(dominant, args.config) if (args.hidden == "bf16" or dominant != "memory_gemm") else None
-    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    # counters were taken on the bf16 big-GEMM kernels; the fp16 memory GEMM and the fp32 mode's are others
+    traffic = (load_traffic(dominant, args.config)
+               if not f32 and (args.hidden == "bf16" or dominant != "memory_gemm") else None)
+    # fp32 mode: every fp32 product runs as three bf16 MFMA terms, so its ceiling is a third of the bf16 rate
+    peak = PEAK_BF16_TFLOPS / 3.0 if f32 else PEAK_BF16_TFLOPS
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+    if traffic is not None:
+        roofline["traffic_basis"] = ("FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated: L2-to-fabric bytes, "
+                                     "memory-side (MALL) cache hits included")
+    if f32:
+        roofline["peak_basis"] = (f"bf16 MFMA {PEAK_BF16_TFLOPS} TFLOP/s / 3 bf16 terms per fp32 product "
+                                  f"(fp32 MFMA peak: {PEAK_F32_MFMA_TFLOPS})")
     stages = {k: {"us": round(v, 2)} for k, v in stage_us.items()}
     for k, fl in gemm_flops.items():
         stages[k]["tflops"] = round(fl / (stage_us[k] * 1e-6) / 1e12, 1)
-    hid_bytes = 2.0 * T * H
-    stages["rowstats"]["gbs"] = round(hid_bytes / (stage_us["rowstats"] * 1e-6) / 1e9, 1)
-    kv_bytes = 2.0 * 2 * T * D * NR
-    stages["route_attn"]["gbs"] = round(kv_bytes / (stage_us["route_attn"] * 1e-6) / 1e9, 1)
-    lex_bytes = 2.0 * H * len(b.o_ids)
-    stages["lexical"]["gbs"] = round(lex_bytes / (stage_us["lexical"] * 1e-6) / 1e9, 1)
+        stages[k]["frac_mfma"] = round(fl / (stage_us[k] * 1e-6) / 1e12 / peak, 4)
+    # algorithmic bytes of the HBM-bound stages: hidden rows once (row statistics), span rows and
+    # global rows (pooling), lexical-table rows (gather), K and V of every layer (routing attention)
+    span_rows = int((b.q_span[:, 1] - b.q_span[:, 0]).sum() + (b.o_span[:, 1] - b.o_span[:, 0]).sum()) + b.B
+    kv_el = 4 if f32 else 2
+    hbm = {"rowstats": 2.0 * T * H, "pool": 2.0 * span_rows * H, "lexical": 2.0 * H * len(b.o_ids),
+           "route_attn": kv_el * 2.0 * T * D * NR}
+    for k, by in hbm.items():
+        gbs = by / (stage_us[k] * 1e-6) / 1e9
+        stages[k]["gbs"] = round(gbs, 1)
+        stages[k]["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import head as O
-        from threadpoolctl import threadpool_info
         params = O.load_params(case.weights)
         # cycle through the batch's records until the time budget is spent
         done, outs, t0 = [], [], time.perf_counter()
@@ -235,7 +305,7 @@ def main():
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        hinfo, threads = host_info()
         # the first pass over the records also checks the GPU outputs
         first = done[:b.B]
         o0 = [int(b.o_offsets[b.q_offsets[r]]) for r in first]
@@ -247,7 +317,7 @@ def main():
         cpu = {"value": round(len(done) / el, 3), "unit": "records/s", "cores": threads, "kind": "oracle",
                "sample": f"{len(done)} record forwards cycling over the batch's {b.B} records, fp64 NumPy, {el:.1f}s",
                "max_abs_dlogit_vs_gpu": float(np.abs(gl - ol).max()),
-               "max_abs_dprob_vs_gpu": float(np.abs(gp - op).max())}
+               "max_abs_dprob_vs_gpu": float(np.abs(gp - op).max()), **hinfo}
         log(f"oracle: {cpu}")
 
     for r in runners[::-1]:
@@ -265,13 +335,17 @@ def main():
         "in_flight": len(runners),
         "ms_per_batch_one_in_flight": round(ms_one, 4),
         "records_per_s_one_in_flight": round(b.B / (ms_one * 1e-3), 1),
+        "latency_us": {**lat, "timer": "HIP events around each forward on its stream, one batch at a time"},
+        "latency_cold_us": cold,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.hidden == "bf16" else "f16 hidden, bf16 weights",
+        "dtype": ("f32" + ("" if args.hidden == "bf16" else " (fp16 hidden)")) if f32 else
+                 ("bf16" if args.hidden == "bf16" else "f16 hidden, bf16 weights"),
         "data": "synthetic (seeded; random-init head weights, N(0,1) hidden states, N(0,0.02) lexical table)",
         "config": {"workload": WORKLOADS[args.config] + ("" if args.hidden == "bf16" else ", fp16 hidden states")
-                   + (", decoder-layer fields" if args.field_cross_attention else ""),
+                   + (", decoder-layer fields" if args.field_cross_attention else "")
+                   + (", fp32 head (CLEF_PRECISION_F32)" if f32 else ""),
                    "global_batch": int(b.B),
                    "seq_len": int(b.L), "valid_rows": T, "questions": int(b.NQ), "options": int(b.NO)},
         "roofline": roofline,
