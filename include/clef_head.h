@@ -332,6 +332,16 @@ CLEF_API int clef_head_weight_info(const clef_head_config *cfg, int32_t i, char 
  *   CLEF_TRACE_F       fp32 [NQ, D]           field vectors after the field layers
  *   CLEF_TRACE_JCOS    fp32 [NO]              joint cosine
  *   CLEF_TRACE_MLP     fp32 [NO]              residual MLP output
+ *   CLEF_TRACE_POOL_TABLE int32 [NQ + NO + B'][4], B' = records with questions:
+ *                      the pooling entries the kernels read (CoreML metadata page,
+ *                      decision.spans): (first row of the span in the hidden buffer's
+ *                      own layout, span length, first row in the packed row space,
+ *                      output slot) for every question span, then every option span,
+ *                      then the global row [n_b - 1, n_b) of every record with questions
+ *   CLEF_TRACE_LEX_TABLE int32 [NO][4]: (first position in the id table, id count,
+ *                      question slot, global slot) of every option
+ *   CLEF_TRACE_IDS     int32 [sum of option span lengths]: the uploaded id table
+ * The last three are read back from the device copy the kernels used.
  * bytes must equal the snapshot's size. */
 #define CLEF_TRACE_POOLED  1
 #define CLEF_TRACE_LEXICAL 2
@@ -341,6 +351,9 @@ CLEF_API int clef_head_weight_info(const clef_head_config *cfg, int32_t i, char 
 #define CLEF_TRACE_F       6
 #define CLEF_TRACE_JCOS    7
 #define CLEF_TRACE_MLP     8
+#define CLEF_TRACE_POOL_TABLE 9
+#define CLEF_TRACE_LEX_TABLE 10
+#define CLEF_TRACE_IDS     11
 #define CLEF_TRACE_U       16
 CLEF_API int clef_head_set_trace(clef_head *h, int32_t enable);
 CLEF_API int clef_head_trace(clef_head *h, int32_t which, void *host_dst, int64_t bytes);
@@ -363,6 +376,21 @@ CLEF_API int clef_head_trace(clef_head *h, int32_t which, void *host_dst, int64_
 #define CLEF_NUM_STAGES       10
 CLEF_API int clef_head_set_profiling(clef_head *h, int32_t enable);
 CLEF_API int clef_head_stage_times(clef_head *h, double *ms, int64_t *forwards);
+
+/* Test hooks, process-wide, for exercising failure paths and reads of
+ * unwritten memory (no page operation):
+ *   CLEF_DEBUG_ALLOC_LIMIT  value = bytes (0: none): every single device or
+ *                           pinned allocation the library would make above it
+ *                           fails, and the call returns CLEF_E_NOMEM
+ *   CLEF_DEBUG_POISON       value != 0: working memory allocated from then on
+ *                           (workspace, trace copies, streamed staging rows,
+ *                           and the allocation-free scratch at every call) is
+ *                           first filled with 0xFFFFFFFF (a NaN in fp32 and
+ *                           bf16) by a kernel on the call's stream
+ * Returns CLEF_E_ARG for an unknown setting or a negative limit. */
+#define CLEF_DEBUG_ALLOC_LIMIT 1
+#define CLEF_DEBUG_POISON      2
+CLEF_API int clef_head_debug_set(int32_t what, int64_t value);
 
 #ifdef __cplusplus
 }

@@ -25,13 +25,16 @@ CLEF_PRECISION_BF16, CLEF_PRECISION_F32 = 0, 1
 CLEF_NOALLOC_SCRATCH_BYTES = 256 << 20
 CLEF_TRACE_POOLED, CLEF_TRACE_LEXICAL, CLEF_TRACE_PRIOR, CLEF_TRACE_MEMORY = 1, 2, 3, 4
 CLEF_TRACE_F0, CLEF_TRACE_F, CLEF_TRACE_JCOS, CLEF_TRACE_MLP, CLEF_TRACE_U = 5, 6, 7, 8, 16
+CLEF_TRACE_POOL_TABLE, CLEF_TRACE_LEX_TABLE, CLEF_TRACE_IDS = 9, 10, 11
+CLEF_DEBUG_ALLOC_LIMIT, CLEF_DEBUG_POISON = 1, 2
 
 EXPORTS = ("clef_head_create", "clef_head_create_sharing", "clef_head_forward", "clef_head_forward_answers",
            "clef_head_forward_noalloc",
            "clef_head_stream_begin", "clef_head_stream_rows", "clef_head_stream_end", "clef_head_stream_cancel",
            "clef_head_destroy", "clef_head_last_error",
            "clef_head_check_batch", "clef_head_span_rows", "clef_head_weight_count", "clef_head_weight_info",
-           "clef_head_set_trace", "clef_head_trace", "clef_head_set_profiling", "clef_head_stage_times")
+           "clef_head_set_trace", "clef_head_trace", "clef_head_set_profiling", "clef_head_stage_times",
+           "clef_head_debug_set")
 STAGES = ("rowstats", "pool", "lexical", "memory_gemm", "kv_gemm", "query_proj", "route_dense", "route_attn",
           "field", "score")
 
@@ -106,6 +109,7 @@ def load() -> ctypes.CDLL:
     L.clef_head_set_trace.argtypes = [_P, ctypes.c_int32]
     L.clef_head_trace.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_int64]
     L.clef_head_set_profiling.argtypes = [_P, ctypes.c_int32]
+    L.clef_head_debug_set.argtypes = [ctypes.c_int32, ctypes.c_int64]
     L.clef_head_stage_times.argtypes = [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     _lib = L
     return L
@@ -269,6 +273,10 @@ def clef_head_set_trace(handle: int, enable: bool):
 def clef_head_trace(handle: int, which: int, out: np.ndarray) -> np.ndarray:
     _check(load().clef_head_trace(handle, which, out.ctypes.data, out.nbytes))
     return out
+
+
+def clef_head_debug_set(what: int, value: int):
+    _check(load().clef_head_debug_set(what, value))
 
 
 def clef_head_set_profiling(handle: int, enable: bool):

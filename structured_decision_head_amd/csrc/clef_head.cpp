@@ -16,6 +16,7 @@
 //      |f-u|]); softmax and argmax per question.
 #include "clef_head.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -43,6 +44,28 @@ int fail(int code, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return code;
+}
+
+// Test hooks (clef_head_debug_set): a cap on every single device or pinned
+// allocation, and NaN-poisoning of newly allocated working memory.
+std::atomic<int64_t> g_alloc_limit{0};
+std::atomic<int> g_poison{0};
+
+bool over_limit(size_t bytes) {
+  const int64_t lim = g_alloc_limit.load();
+  return lim > 0 && (int64_t)bytes > lim;
+}
+
+hipError_t dev_malloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (over_limit(bytes)) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+
+hipError_t pinned_malloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (over_limit(bytes)) return hipErrorOutOfMemory;
+  return hipHostMalloc(p, bytes, hipHostMallocDefault);
 }
 
 #define HIPCHK(x)                                                                              \
@@ -447,6 +470,10 @@ struct clef_head {
   std::shared_ptr<HeadGroup> group;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool staged_pending = false;
+  // end of the handle's last piece of GPU work (forward or streamed chunk): the
+  // next one waits for it, and buffers are only freed or regrown after it
+  hipEvent_t done = nullptr;
+  bool done_recorded = false;
   // trace
   bool trace = false;
   void* tr = nullptr;
@@ -458,6 +485,10 @@ struct clef_head {
   float *pooled = nullptr, *ebar = nullptr, *prior = nullptr;
   bf16_t* mem = nullptr;
   float *tr_u = nullptr, *tr_f0 = nullptr, *tr_f = nullptr, *tr_jcos = nullptr, *tr_mlp = nullptr;
+  // the index tables the last traced forward uploaded (read back from the device)
+  const int32_t* tr_tab = nullptr;
+  size_t tr_off_pool = 0, tr_off_lex = 0, tr_off_ids = 0;
+  int64_t tr_npool = 0, tr_nlex = 0, tr_nids = 0;
   // allocation-free forwards: the plan's tables, kept until the next such call
   std::vector<int32_t> noalloc_tab;
   // stage timing
@@ -724,7 +755,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
   }
 
   void* d = nullptr;
-  if (hipMalloc(&d, blob.host.size()) != hipSuccess)
+  if (dev_malloc(&d, blob.host.size()) != hipSuccess)
     return fail(CLEF_E_NOMEM, "hipMalloc of %zu bytes of weights failed", blob.host.size());
   if (hipMemcpy(d, blob.host.data(), blob.host.size(), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(d);
@@ -875,7 +906,8 @@ namespace {
 bool create_streams(clef_head* h) {
   if (hipEventCreateWithFlags(&h->staged, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess)
     return false;
   if (!h->group) {
     auto g = std::make_shared<HeadGroup>();
@@ -950,6 +982,10 @@ int clef_head_create_sharing(const clef_head* src, clef_head** out) {
 
 void clef_head_destroy(clef_head* h) {
   if (!h) return;
+  if (h->done) {
+    if (h->done_recorded) (void)hipEventSynchronize(h->done);   // the handle's last work still reads its buffers
+    (void)hipEventDestroy(h->done);
+  }
   for (auto e : h->ev) (void)hipEventDestroy(e);
   if (h->side) (void)hipStreamSynchronize(h->side.get());   // this head's side work; the stream goes with its last user
   h->side.reset();
@@ -965,6 +1001,19 @@ void clef_head_destroy(clef_head* h) {
   if (h->pinned) (void)hipHostFree(h->pinned);
   h->dweights.reset();
   delete h;
+}
+
+int clef_head_debug_set(int32_t what, int64_t value) {
+  if (what == CLEF_DEBUG_ALLOC_LIMIT) {
+    if (value < 0) return fail(CLEF_E_ARG, "allocation limit must be >= 0");
+    g_alloc_limit.store(value);
+    return CLEF_OK;
+  }
+  if (what == CLEF_DEBUG_POISON) {
+    g_poison.store(value != 0 ? 1 : 0);
+    return CLEF_OK;
+  }
+  return fail(CLEF_E_ARG, "unknown debug setting %d", what);
 }
 
 int clef_head_set_profiling(clef_head* h, int32_t enable) {
@@ -1007,6 +1056,9 @@ int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) 
   else if (which == CLEF_TRACE_F) { src = h->tr_f; n = NQ * D * 4; }
   else if (which == CLEF_TRACE_JCOS) { src = h->tr_jcos; n = NO * 4; }
   else if (which == CLEF_TRACE_MLP) { src = h->tr_mlp; n = NO * 4; }
+  else if (which == CLEF_TRACE_POOL_TABLE) { src = h->tr_tab + h->tr_off_pool; n = (size_t)h->tr_npool * 16; }
+  else if (which == CLEF_TRACE_LEX_TABLE) { src = h->tr_tab + h->tr_off_lex; n = (size_t)h->tr_nlex * 16; }
+  else if (which == CLEF_TRACE_IDS) { src = h->tr_tab + h->tr_off_ids; n = (size_t)h->tr_nids * 4; }
   else if (which >= CLEF_TRACE_U && which <= CLEF_TRACE_U + NR) {
     src = h->tr_u + (size_t)(which - CLEF_TRACE_U) * NO * D;
     n = NO * D * 4;
@@ -1023,13 +1075,14 @@ int clef_head_trace(clef_head* h, int32_t which, void* host_dst, int64_t bytes) 
 static int stage_plan(clef_head* h, const Plan& p, const WsLayout& L, hipStream_t st) {
   if (L.total > h->ws_bytes) {
     if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
-    HIPCHK(hipDeviceSynchronize());
+    if (h->done_recorded) HIPCHK(hipEventSynchronize(h->done));   // the old workspace's last reader
     if (h->ws) (void)hipFree(h->ws);
     h->ws = nullptr;
     h->ws_bytes = 0;
     const size_t want = L.total + L.total / 4;
-    if (hipMalloc(&h->ws, want) != hipSuccess) return fail(CLEF_E_NOMEM, "workspace hipMalloc of %zu bytes failed", want);
+    if (dev_malloc(&h->ws, want) != hipSuccess) return fail(CLEF_E_NOMEM, "workspace hipMalloc of %zu bytes failed", want);
     h->ws_bytes = want;
+    if (g_poison.load()) launch_fill_u32(st, h->ws, want, 0xffffffffu);
   }
   const size_t tab_bytes = p.tab.size() * 4;
   if (h->staged_pending) HIPCHK(hipEventSynchronize(h->staged));
@@ -1038,7 +1091,7 @@ static int stage_plan(clef_head* h, const Plan& p, const WsLayout& L, hipStream_
     h->pinned = nullptr;
     h->pinned_bytes = 0;
     const size_t want = tab_bytes + tab_bytes / 2 + 4096;
-    if (hipHostMalloc(&h->pinned, want, hipHostMallocDefault) != hipSuccess)
+    if (pinned_malloc(&h->pinned, want) != hipSuccess)
       return fail(CLEF_E_NOMEM, "pinned staging of %zu bytes failed", want);
     h->pinned_bytes = want;
   }
@@ -1059,6 +1112,7 @@ static int stage_plan_noalloc(clef_head* h, const Plan& p, const WsLayout& L, vo
                 "the batch needs %zu bytes of workspace; the allocation-free entry point holds at most %zu "
                 "(use clef_head_forward for larger batches)",
                 L.total, (size_t)kNoallocScratchBytes);
+  if (g_poison.load()) launch_fill_u32(st, ws, L.total, 0xffffffffu);
   h->noalloc_tab = p.tab;
   HIPCHK(hipMemcpyAsync(static_cast<uint8_t*>(ws) + L.tab, h->noalloc_tab.data(), h->noalloc_tab.size() * 4,
                         hipMemcpyHostToDevice, st));
@@ -1088,6 +1142,8 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
     ~Restore() { if (d != p) (void)hipSetDevice(p); }
   } restore{h->device, dev_prev};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  // the workspace is the handle's: its previous work, on whatever stream, comes first
+  if (h->done_recorded) HIPCHK(hipStreamWaitEvent(st, h->done, 0));
 
   const WsLayout L = ws_layout(c, p);
   if (streamed && L.total > h->ws_bytes) return fail(CLEF_E_ARG, "streamed batch does not fit the staged workspace");
@@ -1108,12 +1164,13 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   if (h->trace) {
     const size_t need = align256((size_t)(NR + 1) * NO * D * 4) + 2 * align256((size_t)NQ * D * 4) + 2 * align256((size_t)NO * 4);
     if (need > h->tr_bytes) {
-      HIPCHK(hipDeviceSynchronize());
+      if (h->done_recorded) HIPCHK(hipEventSynchronize(h->done));
       if (h->tr) (void)hipFree(h->tr);
       h->tr = nullptr;
       h->tr_bytes = 0;
-      if (hipMalloc(&h->tr, need) != hipSuccess) return fail(CLEF_E_NOMEM, "trace hipMalloc failed");
+      if (dev_malloc(&h->tr, need) != hipSuccess) return fail(CLEF_E_NOMEM, "trace hipMalloc failed");
       h->tr_bytes = need;
+      if (g_poison.load()) launch_fill_u32(st, h->tr, need, 0xffffffffu);
     }
     uint8_t* t = static_cast<uint8_t*>(h->tr);
     h->tr_u = reinterpret_cast<float*>(t);
@@ -1348,6 +1405,8 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   MARK(CLEF_STAGE_SCORE);
 #undef MARK
   HIPCHK(hipGetLastError());
+  HIPCHK(hipEventRecord(h->done, st));
+  h->done_recorded = true;
   if (h->prof) {
     HIPCHK(hipEventSynchronize(h->ev[marks.size() - 1]));
     for (size_t i = 1; i < marks.size(); ++i) {
@@ -1364,6 +1423,13 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   h->last_B = p.nact;
   h->last_Tpad = p.Tpad;
   h->pooled = noalloc ? nullptr : pooled;   // no snapshots of the shared scratch
+  h->tr_tab = dtab;
+  h->tr_off_pool = p.off_pool;
+  h->tr_off_lex = p.off_lex;
+  h->tr_off_ids = p.off_ids;
+  h->tr_npool = p.npool;
+  h->tr_nlex = NO;
+  h->tr_nids = p.nids;
   h->ebar = ebar;
   h->prior = prior;
   h->mem = (joint && NR > 0) ? mem : nullptr;
@@ -1427,12 +1493,13 @@ int clef_head_stream_begin(clef_head* h, const clef_head_batch* batch, void* hip
   const size_t H = h->cfg.hidden_size;
   const size_t need = (size_t)std::max<int64_t>(batch->cu_seqlens[B], 1) * H * 2;
   if (need > S.rows_bytes) {
-    HIPCHK(hipDeviceSynchronize());
+    if (h->done_recorded) HIPCHK(hipEventSynchronize(h->done));
     if (S.rows) (void)hipFree(S.rows);
     S.rows = nullptr;
     S.rows_bytes = 0;
-    if (hipMalloc(&S.rows, need) != hipSuccess) return fail(CLEF_E_NOMEM, "staging rows hipMalloc of %zu bytes failed", need);
+    if (dev_malloc(&S.rows, need) != hipSuccess) return fail(CLEF_E_NOMEM, "staging rows hipMalloc of %zu bytes failed", need);
     S.rows_bytes = need;
+    if (g_poison.load()) launch_fill_u32(st, S.rows, need, 0xffffffffu);
   }
   const WsLayout L = ws_layout(h->cfg, p);
   rc = stage_plan(h, p, L, st);
@@ -1489,6 +1556,7 @@ int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nr
     ~Restore() { if (d != p) (void)hipSetDevice(p); }
   } restore{h->device, dev_prev};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (h->done_recorded) HIPCHK(hipStreamWaitEvent(st, h->done, 0));
   const size_t H = h->cfg.hidden_size;
   const auto& tl = S.rec_tiles[record];
   if (!tl.empty()) {   // records without questions take no tiles: their rows are never read
@@ -1499,7 +1567,11 @@ int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nr
   const int32_t before = S.received[record];
   S.received[record] += nrows;
   // tiles of this record completed by the chunk: tile j holds rows [256 j, min(256 (j + 1), n))
-  if (tl.empty()) return CLEF_OK;
+  if (tl.empty()) {
+    HIPCHK(hipEventRecord(h->done, st));
+    h->done_recorded = true;
+    return CLEF_OK;
+  }
   const int n = S.len[record];
   uint8_t* ws = static_cast<uint8_t*>(h->ws);
   const int4* htiles = reinterpret_cast<const int4*>(S.tab.data() + S.off_tiles);
@@ -1529,6 +1601,8 @@ int clef_head_stream_rows(clef_head* h, int32_t record, int32_t row0, int32_t nr
     }
   }
   HIPCHK(hipGetLastError());
+  HIPCHK(hipEventRecord(h->done, st));
+  h->done_recorded = true;
   return CLEF_OK;
 }
 

@@ -12,6 +12,17 @@
 
 namespace clef {
 
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
+}
+
+void launch_fill_u32(hipStream_t st, void* p, size_t bytes, uint32_t v) {
+  const size_t n = bytes / 4;
+  if (n == 0) return;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), n, v);
+}
+
 // ---------------------------------------------------------------------------
 // mu / rstd of every row of a 256-row tile (one wave per row, 4 rows per
 // block; grid = (tiles, 64)).  Rows past the tile's valid count get (0, 0) so
@@ -68,98 +79,144 @@ void launch_rowstats(hipStream_t st, const bf16_t* X, int H, bool f16, const int
 }
 
 // ---------------------------------------------------------------------------
-// Span pooling.  Entry e = (first hidden row, length, first stats row, output
-// slot): out[slot] = gamma * mean_t((x_t - mu_t) * rstd_t) + beta, which is
-// the mean of the LayerNorm-ed rows.  One block per entry.
+// Span gathers (pooling and the lexical mean).  One block of 4 waves per
+// entry; wave w takes the entry's rows w, w + 4, w + 8, ..., R at a time with
+// all R rows' loads in flight (R = 4, or 2 for rows wider than 4096 elements,
+// whose loads would not fit the registers), and every lane covers the whole row width in
+// 512-element chunks (lane l holds elements 8 l .. 8 l + 7 of each chunk, so a
+// wave's load of a chunk reads 1 KB of contiguous memory).  The four waves'
+// sums are then added in wave order through LDS, one chunk at a time, so the
+// result does not depend on timing.
 // ---------------------------------------------------------------------------
-template <int NV, bool F16>
-__global__ __launch_bounds__(256) void k_pool(const bf16_t* __restrict__ X, int H,
-                                              const int4* __restrict__ ent,
-                                              const float2* __restrict__ stats,
-                                              const float* __restrict__ gamma,
+namespace {
+
+// Sum over waves in fixed order: every thread gets the block total of chunk c
+// for its two elements 2 t, 2 t + 1 (t = threadIdx.x) of the 512.  red holds
+// 4 x 512 floats; the call ends with a barrier.
+DEV float2 wave_order_sum(const float (&acc)[8], float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float4* dst = reinterpret_cast<float4*>(red + w * 512 + lane * 8);
+  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+  const int e = threadIdx.x * 2;
+  float2 r = *reinterpret_cast<const float2*>(red + e);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    const float2 v = *reinterpret_cast<const float2*>(red + i * 512 + e);
+    r.x += v.x;
+    r.y += v.y;
+  }
+  __syncthreads();
+  return r;
+}
+
+}  // namespace
+
+// Span pooling.  Entry e = (first hidden row, length, first stats row, output
+// slot): out[slot] = gamma * mean_t((x_t - mu_t) * rstd_t) + beta, the mean of
+// the LayerNorm-ed rows.
+template <int NCH, bool F16>
+__global__ __launch_bounds__(256) void k_pool(const bf16_t* __restrict__ X, const int4* __restrict__ ent,
+                                              const float2* __restrict__ stats, const float* __restrict__ gamma,
                                               const float* __restrict__ beta, float* __restrict__ out) {
+  constexpr int H = NCH * 512;
+  __shared__ __attribute__((aligned(16))) float red[4 * 512];
   const int4 e = ent[blockIdx.x];
-  const int nvec = H >> 3;
-  float acc[NV][8];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float acc[NCH][8];
 #pragma unroll
-  for (int j = 0; j < NV; ++j)
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
-  for (int t = 0; t < e.y; ++t) {
-    const float2 s = stats[e.z + t];
-    const uint4* row = reinterpret_cast<const uint4*>(X + (size_t)(e.x + t) * H);
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
+  constexpr int R = NCH <= 8 ? 4 : 2;
+  for (int t = w; t < e.y; t += 4 * R) {
+    uint4 q[R][NCH];
+    float2 sr[R];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = threadIdx.x + 256 * j;
-      if (v < nvec) {
-        float x[8];
-        unpack8_hidden<F16>(row[v], x);
+    for (int j = 0; j < R; ++j)
+      if (t + 4 * j < e.y) {
+        const uint4* row = reinterpret_cast<const uint4*>(X + (size_t)(e.x + t + 4 * j) * H) + lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] += (x[i] - s.x) * s.y;
+        for (int c = 0; c < NCH; ++c) q[j][c] = row[c * 64];
+        sr[j] = stats[e.z + t + 4 * j];
       }
-    }
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (t + 4 * j < e.y) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          float x[8];
+          unpack8_hidden<F16>(q[j][c], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[c][i] += (x[i] - sr[j].x) * sr[j].y;
+        }
+      }
   }
   const float inv = 1.0f / (float)e.y;
   float* o = out + (size_t)e.w * H;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = threadIdx.x + 256 * j;
-    if (v < nvec) {
-      float r[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] = gamma[8 * v + i] * (acc[j][i] * inv) + beta[8 * v + i];
-      reinterpret_cast<float4*>(o)[2 * v] = make_float4(r[0], r[1], r[2], r[3]);
-      reinterpret_cast<float4*>(o)[2 * v + 1] = make_float4(r[4], r[5], r[6], r[7]);
-    }
+  for (int c = 0; c < NCH; ++c) {
+    const float2 v = wave_order_sum(acc[c], red);
+    const int k = c * 512 + threadIdx.x * 2;
+    const float2 g = *reinterpret_cast<const float2*>(gamma + k), b = *reinterpret_cast<const float2*>(beta + k);
+    *reinterpret_cast<float2*>(o + k) = make_float2(g.x * (v.x * inv) + b.x, g.y * (v.y * inv) + b.y);
   }
 }
 
 void launch_pool(hipStream_t st, const bf16_t* X, int H, bool f16, const int4* ent, int nent, const float2* stats,
                  const float* gamma, const float* beta, float* out) {
   if (nent == 0) return;
-  const int nv = (H / 8 + 255) / 256;
-  switch (nv) {
-#define CASE(n)                                                                                            \
-  case n:                                                                                                  \
-    if (f16) hipLaunchKernelGGL((k_pool<n, true>), dim3(nent), dim3(256), 0, st, X, H, ent, stats, gamma, beta, out); \
-    else hipLaunchKernelGGL((k_pool<n, false>), dim3(nent), dim3(256), 0, st, X, H, ent, stats, gamma, beta, out);    \
+  switch (H / 512) {
+#define CASE(n)                                                                                              \
+  case n:                                                                                                    \
+    if (f16) hipLaunchKernelGGL((k_pool<n, true>), dim3(nent), dim3(256), 0, st, X, ent, stats, gamma, beta, out); \
+    else hipLaunchKernelGGL((k_pool<n, false>), dim3(nent), dim3(256), 0, st, X, ent, stats, gamma, beta, out);    \
     break;
-    CASE(1) CASE(2) CASE(3) CASE(4)
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
   }
 }
 
-// ---------------------------------------------------------------------------
 // Lexical gather-mean and prior.  Entry k = (first id, count, question slot,
 // global slot) in the pooled buffer: e_k = mean of table rows; prior_k =
 // cos(e_k, pooled[q] + pooled[g]) with norms clamped at 1e-8.
-// ---------------------------------------------------------------------------
-template <int NV>
-__global__ __launch_bounds__(256) void k_lex_prior(const bf16_t* __restrict__ E, int H,
-                                                   const int4* __restrict__ ent,
-                                                   const int* __restrict__ ids,
-                                                   const float* __restrict__ pooled,
+template <int NCH>
+__global__ __launch_bounds__(256) void k_lex_prior(const bf16_t* __restrict__ E, const int4* __restrict__ ent,
+                                                   const int* __restrict__ ids, const float* __restrict__ pooled,
                                                    float* __restrict__ ebar, float* __restrict__ prior) {
+  constexpr int H = NCH * 512;
+  __shared__ __attribute__((aligned(16))) float red[4 * 512];
   __shared__ float sm[4];
   const int4 e = ent[blockIdx.x];
-  const int nvec = H >> 3;
-  float acc[NV][8];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float acc[NCH][8];
 #pragma unroll
-  for (int j = 0; j < NV; ++j)
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
-  for (int t = 0; t < e.y; ++t) {
-    const uint4* row = reinterpret_cast<const uint4*>(E + (size_t)ids[e.x + t] * H);
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
+  constexpr int R = NCH <= 8 ? 4 : 2;
+  for (int t = w; t < e.y; t += 4 * R) {
+    uint4 q[R][NCH];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int v = threadIdx.x + 256 * j;
-      if (v < nvec) {
-        float x[8];
-        unpack8(row[v], x);
+    for (int j = 0; j < R; ++j)
+      if (t + 4 * j < e.y) {
+        const uint4* row = reinterpret_cast<const uint4*>(E + (size_t)ids[e.x + t + 4 * j] * H) + lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[j][i] += x[i];
+        for (int c = 0; c < NCH; ++c) q[j][c] = row[c * 64];
       }
-    }
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (t + 4 * j < e.y) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          float x[8];
+          unpack8(q[j][c], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[c][i] += x[i];
+        }
+      }
   }
   const float inv = 1.0f / (float)e.y;
   const float* qv = pooled + (size_t)e.z * H;
@@ -167,21 +224,16 @@ __global__ __launch_bounds__(256) void k_lex_prior(const bf16_t* __restrict__ E,
   float* eo = ebar + (size_t)blockIdx.x * H;
   float ea = 0.f, ee = 0.f, aa = 0.f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int v = threadIdx.x + 256 * j;
-    if (v < nvec) {
-      float r[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        r[i] = acc[j][i] * inv;
-        const float a = qv[8 * v + i] + gv[8 * v + i];
-        ea += r[i] * a;
-        ee += r[i] * r[i];
-        aa += a * a;
-      }
-      reinterpret_cast<float4*>(eo)[2 * v] = make_float4(r[0], r[1], r[2], r[3]);
-      reinterpret_cast<float4*>(eo)[2 * v + 1] = make_float4(r[4], r[5], r[6], r[7]);
-    }
+  for (int c = 0; c < NCH; ++c) {
+    const float2 v = wave_order_sum(acc[c], red);
+    const int k = c * 512 + threadIdx.x * 2;
+    const float2 r = make_float2(v.x * inv, v.y * inv);
+    const float2 q = *reinterpret_cast<const float2*>(qv + k), g = *reinterpret_cast<const float2*>(gv + k);
+    const float a0 = q.x + g.x, a1 = q.y + g.y;
+    ea += r.x * a0 + r.y * a1;
+    ee += r.x * r.x + r.y * r.y;
+    aa += a0 * a0 + a1 * a1;
+    *reinterpret_cast<float2*>(eo + k) = r;
   }
   ea = block_sum<4>(ea, sm);
   ee = block_sum<4>(ee, sm);
@@ -193,10 +245,10 @@ __global__ __launch_bounds__(256) void k_lex_prior(const bf16_t* __restrict__ E,
 void launch_lex_prior(hipStream_t st, const bf16_t* E, int H, const int4* ent, int nent, const int* ids,
                       const float* pooled, float* ebar, float* prior) {
   if (nent == 0) return;
-  const int nv = (H / 8 + 255) / 256;
-  switch (nv) {
-#define CASE(n) case n: hipLaunchKernelGGL(k_lex_prior<n>, dim3(nent), dim3(256), 0, st, E, H, ent, ids, pooled, ebar, prior); break;
-    CASE(1) CASE(2) CASE(3) CASE(4)
+  switch (H / 512) {
+#define CASE(n) case n: hipLaunchKernelGGL(k_lex_prior<n>, dim3(nent), dim3(256), 0, st, E, ent, ids, pooled, ebar, prior); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
   }
 }

@@ -16,6 +16,10 @@ hipError_t noalloc_scratch(int device, void** out);
 // feeds to a V^T P^T MFMA step sit in 16 contiguous bytes.
 DEV int vblock_pos(int k) { return (k & 16) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
+// Fill `bytes` (a multiple of 4) at p with the 32-bit pattern v (a kernel, so
+// that it can sit in a captured graph; used to poison fresh working memory).
+void launch_fill_u32(hipStream_t, void* p, size_t bytes, uint32_t v);
+
 // ---------------------------------------------------------------------------
 // row kernels
 // ---------------------------------------------------------------------------
