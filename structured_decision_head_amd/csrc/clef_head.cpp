@@ -1290,17 +1290,17 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         const int Tp = (int)p.Tpad;
         if (p.f16)
           launch_sgemm(st, LdHid<true>{X, (int)H, tiles, stats, W.lnin_g, W.lnin_b}, EpStore{mem32, D, W.bmem},
-                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 1);
+                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 0);
         else
           launch_sgemm(st, LdHid<false>{X, (int)H, tiles, stats, W.lnin_g, W.lnin_b}, EpStore{mem32, D, W.bmem},
-                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 1);
+                       W.Wmem_fr, Tp, D, (int)H, bigpart, nullptr, 0.f, 3, 0);
         MARK(CLEF_STAGE_MEMORY_GEMM);
         if (NR > 0)
           launch_sgemm(st, LdRows{mem32, D, nullptr}, EpHeads{kv32, p.Tpad, W.bkv}, W.Wkv_fr, Tp, NR * 2 * D, D,
-                       bigpart, nullptr, 0.f, 3, 1);
+                       bigpart, nullptr, 0.f, 3, 0);
         if (cross)
           launch_sgemm(st, LdRows{mem32, D, nullptr}, EpHeads{fkv32, p.Tpad, W.bfkv}, W.Wfkv_fr, Tp, NL * 2 * D,
-                       D, bigpart, nullptr, 0.f, 3, 1);
+                       D, bigpart, nullptr, 0.f, 3, 0);
         MARK(CLEF_STAGE_KV_GEMM);
       } else {
         launch_gemm_mem(st, X, (int)H, p.f16, tiles, p.ntiles, p.f16 ? W.Wmem16 : W.Wmem, stats,
