@@ -25,7 +25,7 @@ void launch_fill_u32(hipStream_t st, void* p, size_t bytes, uint32_t v) {
 
 // ---------------------------------------------------------------------------
 // mu / rstd of every row of a 256-row tile (one wave per row, 4 rows per
-// block; grid = (tiles, 64)).  Rows past the tile's valid count get (0, 0) so
+// block; grid = (64, tiles), so consecutive workgroups read consecutive rows).  Rows past the tile's valid count get (0, 0) so
 // that padded rows of the packed row space stay finite downstream.  Hidden
 // elements are bf16, or fp16 when F16 (the CoreML packaging feeds fp16 hidden
 // states to the head, CoreML conversion metadata page "decision.head").
@@ -35,9 +35,9 @@ __global__ __launch_bounds__(256) void k_rowstats(const bf16_t* __restrict__ X,
                                                        const int4* __restrict__ tiles,
                                                        float2* __restrict__ stats, float eps) {
   constexpr int H = NCH * 512;
-  const int4 t = tiles[blockIdx.x];
+  const int4 t = tiles[blockIdx.y];
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= t.z) {
     if (lane == 0) stats[t.y + r] = make_float2(0.f, 0.f);
     return;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_rowstats(const bf16_t* __restrict__ X,
 
 void launch_rowstats(hipStream_t st, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles,
                      float2* stats, float eps) {
-  const dim3 grid(ntiles, 64), block(256);
+  const dim3 grid(64, ntiles), block(256);
   switch (H / 512) {
 #define CASE(n)                                                                              \
   case n:                                                                                    \
