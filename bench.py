@@ -148,6 +148,36 @@ def streamed_ingest(args, C, HeadRunner, case, runner, torch, np, H):
             "total_us": round(float(np.median(totals)) * 1e3, 1)}
 
 
+def library_gemm(args, torch, synth):
+    """torch.matmul (hipBLASLt) on the two big products of the workload, over the
+    same 256-row tile space the head's GEMMs cover; W given as the transposed
+    view of [out, in] rows (the faster of the two operand forms measured)."""
+    case = synth.config_case(args.config, with_table=False)
+    b = case.batch
+    rows = 256 * sum(-(-int(n) // 256) for n in b.lengths)
+    H, D = case.head.hidden_size, case.head.width
+    out = {"library_gemm": "torch.matmul bf16 (hipBLASLt), median of 20", "config": args.config, "rows": rows}
+    torch.manual_seed(0)
+    for name, M, N, K in (("memory", rows, D, H), ("kv", rows, 2 * D * case.head.routing_layers, D)):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(5):
+            c = torch.matmul(a, w.t())
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(20):
+            s.record()
+            c = torch.matmul(a, w.t())
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1e3)
+        us = sorted(ts)[len(ts) // 2]
+        out[name] = {"M": M, "N": N, "K": K, "us": round(us, 1), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+        del a, w, c
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +197,9 @@ def main():
     ap.add_argument("--no-stream", action="store_true", help="skip the streamed-ingest measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul, hipBLASLt) on the shapes of the workload's "
+                         "memory and K/V products, plain bf16 with no epilogue: a comparison point")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (the head shards by record with no exchange between GPUs: "
@@ -190,6 +223,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+        return
+    if args.library_gemm:
+        library_gemm(args, torch, synth)
         return
     t = time.time()
     f32 = args.precision == "f32"

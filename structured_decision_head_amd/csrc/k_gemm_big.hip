@@ -29,12 +29,15 @@ constexpr int BM = 256, BN = 256;
 // of lane l sits at block row 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4 and block
 // column 32 ni + (l % 32).
 //
-// The finished tile is converted to bf16 and written with 8- or 16-byte LDS
+// A finished memory tile is converted to bf16 and written with 8-byte LDS
 // stores into an image of its final memory layout (the operand ring is free
 // by then); all 256 threads then copy the image out with 16-byte global
-// stores, each wave instruction covering 1 KB of contiguous memory.  Per-tile
-// constants are loaded by thread tid when the kernel starts, so their latency
-// hides under the main loop, and parked in a small LDS area behind the ring.
+// stores, each wave instruction covering 1 KB of contiguous memory.  K/V
+// tiles need no image: their fragment-order layouts let every lane store
+// whole 16-byte chunks straight from the accumulators, again 1 KB per wave
+// instruction.  Per-tile constants are loaded by thread tid when the kernel
+// starts, so their latency hides under the main loop, and parked in a small
+// LDS area behind the ring.
 constexpr int kConstFloats = 1024;
 
 struct EpiMem {          // transposed tiles; rows of out are the packed row space
@@ -44,7 +47,8 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   bf16_t* out;           // [rows][1024]
   static constexpr bool kF16 = false;                  // operands bf16
   static constexpr bool kDirect = false;               // output staged through LDS
-  static constexpr bool kHasPlain = false;
+  static constexpr bool kRegs = false;
+  static constexpr bool kPlain = false;                // every tile transposed
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
   static constexpr int kImageBytes = 256 * kLd * 2;
   DEV bool transposed(int) const { return true; }
@@ -80,8 +84,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
         }
       }
   }
-  DEV void stage(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
-  DEV void store(const bf16_t* img, int orow0, int ocol0, bool, int tid) const {
+  DEV void store(const bf16_t* img, int orow0, int ocol0, int tid) const {
 #pragma unroll 8
     for (int i = tid; i < 256 * 32; i += 256) {
       const int r = i >> 5, ch = i & 31;
@@ -116,8 +119,9 @@ struct EpiKV {
   long long Tpad;
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
-  static constexpr bool kHasPlain = true;
-  static constexpr int kImageBytes = 4 * 256 * 64 * 2;
+  static constexpr bool kRegs = true;                  // stored from the accumulators
+  static constexpr bool kPlain = true;                 // V tiles are plain
+  static constexpr int kImageBytes = 0;
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV bf16_t* head_base(int col) const {
     const int r = col >> 11, isv = (col >> 10) & 1, h = (col >> 6) & 15;
@@ -125,77 +129,71 @@ struct EpiKV {
   }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
   DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
-  // K (transposed): image [head][row][64] in 128-byte rows, 16-byte chunk c of
-  // row r at position c ^ (r & 7): the 8-byte writes of 32 consecutive rows and
-  // the 16-byte reads of 8 consecutive rows both spread evenly over the banks
-  DEV static int kpos(int row, int col) { return row * 64 + ((((col >> 3) ^ row) & 7) << 3) + (col & 7); }
-  DEV void stage_t(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
-    const int h4 = 4 * (lane >> 5);
+  // Every store instruction of a wave writes one contiguous 1 KB run (64
+  // consecutive 16-byte chunks of a 32-row block).  orow0 / ocol0: the tile's
+  // first output row / column; ra0 / rb0: tile-local first row of the wave's
+  // MFMA A / B operand block (accumulator rows / columns).
+  //  * K (transposed tile): accumulator (mi, ni, e) of lane l is dim
+  //    ra0 + 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4 of key rb0 + 32 ni + l % 32,
+  //    so lanes l and l + 32 hold the two 8-byte halves of one chunk.  One
+  //    v_permlane32_swap per 32-bit word gives lane l (< 32) the whole chunk of
+  //    dim group 2p and lane l + 32 that of group 2p + 1: chunk indices
+  //    64 (2 (mi & 1) + p) + l, i.e. kchunk() of the key and the 8-dim group.
+  //  * V (plain tile): accumulator (mi, ni, e) of lane l is key
+  //    ra0 + 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4 of feature rb0 + 32 ni + l % 32;
+  //    e = 8 q .. 8 q + 7 are key positions 8 (2 q + l / 32) .. + 7 of
+  //    vblock_pos(), the 16-byte chunk vchunk(f, 2 q + l / 32) = 64 (2 q + f / 32) + l.
+  template <bool TR>
+  DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
+                      int lane) const {
+    const int hh = lane >> 5;
+    if constexpr (TR) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi) {
+        const int lcb = ra0 + mi * 32;
+        bf16_t* hb = head_base(ocol0 + lcb) + (size_t)(64 * 2 * (mi & 1) + lane) * 8;
+        float4 b[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int lc = lc0 + mi * 32 + 8 * g + h4;
-        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
-        bf16_t* base = img + (lc >> 6) * (256 * 64);
+        for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const float4*>(cst + lcb + 8 * g + 4 * hh);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const f32x16& a = acc[mi][ni];
-          uint2 v;
-          v.x = pack_bf16x2(a[4 * g] + b.x, a[4 * g + 1] + b.y);
-          v.y = pack_bf16x2(a[4 * g + 2] + b.z, a[4 * g + 3] + b.w);
-          *reinterpret_cast<uint2*>(base + kpos(lr0 + ni * 32 + (lane & 31), lc & 63)) = v;
+          bf16_t* blk = hb + (size_t)((orow0 + rb0 + ni * 32) >> 5) * 2048;
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int g0 = 2 * p, g1 = 2 * p + 1;
+            const uint32_t p0 = pack_bf16x2(a[4 * g0] + b[g0].x, a[4 * g0 + 1] + b[g0].y);
+            const uint32_t p1 = pack_bf16x2(a[4 * g0 + 2] + b[g0].z, a[4 * g0 + 3] + b[g0].w);
+            const uint32_t q0 = pack_bf16x2(a[4 * g1] + b[g1].x, a[4 * g1 + 1] + b[g1].y);
+            const uint32_t q1 = pack_bf16x2(a[4 * g1 + 2] + b[g1].z, a[4 * g1 + 3] + b[g1].w);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+            *reinterpret_cast<uint4*>(blk + p * 512) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          }
         }
       }
-  }
-  // V (plain): image [head][row block][64][32] (V^T blocks; store() puts them
-  // in fragment order); 16-byte chunk c of a 64-byte feature row f sits at
-  // c ^ ((f >> 2) & 3), so 16 consecutive feature rows cover all 16 bank groups
-  DEV void stage(const f32x16 (&acc)[4][4], const float* cst, bf16_t* img, int lr0, int lc0, int lane) const {
-    const int hh = lane >> 5;
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int lc = lc0 + ni * 32 + (lane & 31);
-      const float b = cst[lc];
-      const int f = lc & 63;
-      bf16_t* base = img + (lc >> 6) * 16384 + f * 32;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        bf16_t* blk = base + ((lr0 >> 5) + mi) * 2048;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const f32x16& a = acc[mi][ni];
-          const int e = 8 * q;
-          uint4 v;
-          v.x = pack_bf16x2(a[e] + b, a[e + 1] + b);
-          v.y = pack_bf16x2(a[e + 2] + b, a[e + 3] + b);
-          v.z = pack_bf16x2(a[e + 4] + b, a[e + 5] + b);
-          v.w = pack_bf16x2(a[e + 6] + b, a[e + 7] + b);
-          *reinterpret_cast<uint4*>(blk + 8 * ((2 * q + hh) ^ ((f >> 2) & 3))) = v;
-        }
-      }
-    }
-  }
-  // Both write 4 heads x 32 KB in memory order (consecutive threads, consecutive
-  // 16-byte chunks): thread t writes chunk t of each 32-row block, i.e. row /
-  // feature t % 32 of fragment part t / 32 of the layout above, so its source
-  // position in the image differs from block to block by a constant stride.
-  DEV void store(const bf16_t* img, int orow0, int ocol0, bool tr, int tid) const {
-    int src;
-    if (tr) {
-      const int rr = tid & 31, ch = 2 * (tid >> 6) + ((tid >> 5) & 1);   // inverse of kchunk()
-      src = kpos(rr, ch * 8);                // + 2048 per block: the swizzle depends on rr only
     } else {
-      const int f = 32 * ((tid >> 6) & 1) + (tid & 31), c = 2 * (tid >> 7) + ((tid >> 5) & 1);   // inverse of vchunk()
-      src = f * 32 + 8 * (c ^ ((f >> 2) & 3));
-    }
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      bf16_t* dst = head_base(ocol0 + hh * 64) + (size_t)orow0 * 64 + tid * 8;
-      const bf16_t* im = img + hh * 16384 + src;
+      for (int ni = 0; ni < 4; ++ni) {
+        const int lc = rb0 + ni * 32 + (lane & 31);
+        const float b = cst[lc];
+        bf16_t* hb = head_base(ocol0 + rb0 + ni * 32) + (size_t)(64 * ((lc >> 5) & 1) + lane) * 8;
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        *reinterpret_cast<uint4*>(dst + b * 2048) = *reinterpret_cast<const uint4*>(im + b * 2048);
+        for (int mi = 0; mi < 4; ++mi) {
+          const f32x16& a = acc[mi][ni];
+          bf16_t* blk = hb + (size_t)((orow0 + ra0 + mi * 32) >> 5) * 2048;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int e = 8 * q;
+            uint4 v;
+            v.x = pack_bf16x2(a[e] + b, a[e + 1] + b);
+            v.y = pack_bf16x2(a[e + 2] + b, a[e + 3] + b);
+            v.z = pack_bf16x2(a[e + 4] + b, a[e + 5] + b);
+            v.w = pack_bf16x2(a[e + 6] + b, a[e + 7] + b);
+            *reinterpret_cast<uint4*>(blk + q * 1024) = v;
+          }
+        }
+      }
     }
   }
 };
@@ -211,7 +209,8 @@ struct EpiPart {
   int N;
   static constexpr bool kF16 = F16;
   static constexpr bool kDirect = true;
-  static constexpr bool kHasPlain = false;
+  static constexpr bool kRegs = false;
+  static constexpr bool kPlain = false;
   static constexpr int kImageBytes = 0;
   DEV bool transposed(int) const { return true; }
   DEV void load_consts(int, int, int, float (&)[4]) const {}
@@ -230,9 +229,6 @@ struct EpiPart {
               make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
   }
-  DEV void stage_t(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
-  DEV void stage(const f32x16 (&)[4][4], const float*, bf16_t*, int, int, int) const {}
-  DEV void store(const bf16_t*, int, int, bool, int) const {}
 };
 
 // Output tile of workgroup b.  Workgroups are dealt to the 8 XCDs round-robin
@@ -288,33 +284,28 @@ DEV f32x16 mfma32(const u32x4 a, const u32x4 b, const f32x16 c) {
 // matrix core's whole queue (memory GEMM 234 -> 217 us, K/V GEMM 247 -> 236
 // us on the online-serving batch).
 template <class Epi>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
-               const bf16_t* __restrict__ W, int K, int nsplit, Epi epi) {
-  constexpr int KS = 64, NST = 2;
-  constexpr int kRingBytes = NST * 2 * BM * 8 * 16;
-  constexpr int kSpan = Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
-  // operand ring [stage][A|B][row * 8 + swizzled chunk] (after the main loop the
-  // same bytes hold the output image), then the tile constants
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kSpan + kConstFloats * 4];
-  u32x4 (*smem)[2][BM * 8] = reinterpret_cast<u32x4 (*)[2][BM * 8]>(lds);
-  float* cst = reinterpret_cast<float*>(lds + kSpan);
+constexpr int lds_span() {
+  constexpr int kRingBytes = 2 * 2 * BM * 8 * 16;   // 2 stages x (A | B) x 256 rows x 128 B
+  return Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
+}
 
-  // nsplit > 1: workgroup b multiplies K slice b / (tiles) of length K / nsplit
-  const int ntiles_mn = gridDim.x / nsplit;
-  const int ks = blockIdx.x / ntiles_mn;
+// One output tile (or one K slice of it) in orientation TR (true: transposed,
+// the W rows are the MFMA A operand).  lds: the workgroup's operand ring, then
+// the tile constants.
+template <class Epi, bool TR>
+DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int K, int nsplit, int ks,
+                   int tn, const int4 T, const Epi& epi, unsigned char* lds) {
+  constexpr int KS = 64;
+  u32x4 (*smem)[2][BM * 8] = reinterpret_cast<u32x4 (*)[2][BM * 8]>(lds);
+  float* cst = reinterpret_cast<float*>(lds + lds_span<Epi>());
   const int kbase = ks * (K / nsplit);
-  int tm, tn;
-  tile_order(blockIdx.x - ks * ntiles_mn, ntiles_mn / ntile_n, ntile_n, tm, tn);
-  const int4 T = tiles[tm];              // (first A row, first output row, valid rows, record)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;     // 2 x 2 waves, each 128 x 128
   // transposed tiles feed the W rows as the MFMA A operand: acc rows are then
   // output columns and acc columns are A rows
-  const bool tr = epi.transposed(tn);
-  const int ra_src = tr ? 1 : 0, rb_src = tr ? 0 : 1;
-  const int wa = tr ? wn : wm, wb = tr ? wm : wn;
+  constexpr int ra_src = TR ? 1 : 0, rb_src = TR ? 0 : 1;
+  const int wa = TR ? wn : wm, wb = TR ? wm : wn;
 
   // copy sources: instruction i of wave w fills rows 8 (8 w + i) .. +8 of a stage.
   // Buffer copies: a uniform resource per operand (its record count bounds every
@@ -501,18 +492,38 @@ void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ t
   // (finite) inputs and keep the padded part of the row space finite.
   if constexpr (Epi::kDirect) {
     epi.store_acc(acc, T.y + wb * 128, tn * BN + wa * 128, ks, lane);
-    return;
-  }
-  bf16_t* img = reinterpret_cast<bf16_t*>(lds);
-  __syncthreads();                       // every wave is done with the operand ring
-  if constexpr (Epi::kHasPlain) {
-    if (!tr) epi.stage(acc, cst, img, wa * 128, wb * 128, lane);
-    else epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
+  } else if constexpr (Epi::kRegs) {
+    epi.template store_regs<TR>(acc, cst, T.y, tn * BN, wa * 128, wb * 128, lane);
   } else {
+    bf16_t* img = reinterpret_cast<bf16_t*>(lds);
+    __syncthreads();                     // every wave is done with the operand ring
     epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
+    __syncthreads();
+    epi.store(img, T.y, tn * BN, tid);
   }
-  __syncthreads();
-  epi.store(img, T.y, tn * BN, tr, tid);
+}
+
+template <class Epi>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
+               const bf16_t* __restrict__ W, int K, int nsplit, Epi epi) {
+  // operand ring [stage][A|B][row * 8 + swizzled chunk] (after the main loop the
+  // same bytes may hold the output image), then the tile constants
+  __shared__ __attribute__((aligned(16))) unsigned char lds[lds_span<Epi>() + kConstFloats * 4];
+  // nsplit > 1: workgroup b multiplies K slice b / (tiles) of length K / nsplit
+  const int ntiles_mn = gridDim.x / nsplit;
+  const int ks = blockIdx.x / ntiles_mn;
+  int tm, tn;
+  tile_order(blockIdx.x - ks * ntiles_mn, ntiles_mn / ntile_n, ntile_n, tm, tn);
+  const int4 T = tiles[tm];              // (first A row, first output row, valid rows, record)
+  // the orientation is uniform over the workgroup; each is compiled on its own
+  if constexpr (Epi::kPlain) {
+    if (!epi.transposed(tn)) {
+      gemm_tile<Epi, false>(A, lda, W, K, nsplit, ks, tn, T, epi, lds);
+      return;
+    }
+  }
+  gemm_tile<Epi, true>(A, lda, W, K, nsplit, ks, tn, T, epi, lds);
 }
 
 
