@@ -23,13 +23,9 @@ DEV uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 16-byte load with the non-temporal hint: the line is not kept in L2 or the
-// memory-side cache, so a stream read once does not evict (and first write
-// back) the dirty lines other kernels left there.
-DEV uint4 ld_stream(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+// 16-byte store with the non-temporal hint (16-byte aligned): the line is
+// written through rather than kept dirty in L2 and the memory-side cache.
+DEV void store_stream(void* p, const u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
 
 // Unpack 8 bf16 held in a uint4 into floats.
 DEV void unpack8(const uint4 v, float* f) {

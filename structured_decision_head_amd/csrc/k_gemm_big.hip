@@ -130,7 +130,10 @@ struct EpiKV {
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
   DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
   // Every store instruction of a wave writes one contiguous 1 KB run (64
-  // consecutive 16-byte chunks of a 32-row block).  orow0 / ocol0: the tile's
+  // consecutive 16-byte chunks of a 32-row block), with the non-temporal hint:
+  // K and V are read once per routing layer, so they need not sit dirty in
+  // the caches, where reads of the next batch's hidden rows would first have to
+  // write them back.  orow0 / ocol0: the tile's
   // first output row / column; ra0 / rb0: tile-local first row of the wave's
   // MFMA A / B operand block (accumulator rows / columns).
   //  * K (transposed tile): accumulator (mi, ni, e) of lane l is dim
@@ -168,7 +171,7 @@ struct EpiKV {
             const uint32_t q1 = pack_bf16x2(a[4 * g1 + 2] + b[g1].z, a[4 * g1 + 3] + b[g1].w);
             const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
-            *reinterpret_cast<uint4*>(blk + p * 512) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            store_stream(blk + p * 512, u32x4{s0[0], s1[0], s0[1], s1[1]});
           }
         }
       }
@@ -185,12 +188,9 @@ struct EpiKV {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int e = 8 * q;
-            uint4 v;
-            v.x = pack_bf16x2(a[e] + b, a[e + 1] + b);
-            v.y = pack_bf16x2(a[e + 2] + b, a[e + 3] + b);
-            v.z = pack_bf16x2(a[e + 4] + b, a[e + 5] + b);
-            v.w = pack_bf16x2(a[e + 6] + b, a[e + 7] + b);
-            *reinterpret_cast<uint4*>(blk + q * 1024) = v;
+            store_stream(blk + q * 1024,
+                         u32x4{pack_bf16x2(a[e] + b, a[e + 1] + b), pack_bf16x2(a[e + 2] + b, a[e + 3] + b),
+                               pack_bf16x2(a[e + 4] + b, a[e + 5] + b), pack_bf16x2(a[e + 6] + b, a[e + 7] + b)});
           }
         }
       }

@@ -29,9 +29,6 @@ void launch_fill_u32(hipStream_t st, void* p, size_t bytes, uint32_t v) {
 // that padded rows of the packed row space stay finite downstream.  Hidden
 // elements are bf16, or fp16 when F16 (the CoreML packaging feeds fp16 hidden
 // states to the head, CoreML conversion metadata page "decision.head").
-// The rows are read with the non-temporal hint: this is the one full pass over
-// the hidden states, and allocating them in the caches would first write back
-// the dirty lines (K/V, memory rows) other forwards left there.
 // ---------------------------------------------------------------------------
 template <int NCH, bool F16>
 __global__ __launch_bounds__(256) void k_rowstats(const bf16_t* __restrict__ X,
@@ -48,7 +45,7 @@ __global__ __launch_bounds__(256) void k_rowstats(const bf16_t* __restrict__ X,
   const uint4* row = reinterpret_cast<const uint4*>(X + (size_t)(t.x + r) * H);
   uint4 q[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) q[c] = ld_stream(row + c * 64 + lane);
+  for (int c = 0; c < NCH; ++c) q[c] = row[c * 64 + lane];
   float v[NCH * 8];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) unpack8_hidden<F16>(q[c], v + 8 * c);
