@@ -427,9 +427,11 @@ struct Weights {
   const bf16_t* Wfkv = nullptr;   // decoder-layer field variant: cross K/V of every field layer, stacked
   const float* bfkv = nullptr;
   // precision mode fp32: the memory projection unfolded (LayerNorm applied to the rows) with its own bias,
-  // and the stacked K/V projections, all in the small GEMMs' fragment order
+  // and the stacked K/V projections, in the small GEMMs' fragment order (batches of few row tiles) and as
+  // rows repeated three times, [W | W | W] (the big GEMM over the three bf16 terms of each activation)
   const float* bmem = nullptr;
   const bf16_t *Wmem_fr = nullptr, *Wkv_fr = nullptr, *Wfkv_fr = nullptr;
+  const bf16_t *Wmem3 = nullptr, *Wkv3 = nullptr, *Wfkv3 = nullptr;
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -590,6 +592,13 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     const std::vector<uint16_t> v = fragment_order(src, N, K);
     put_bf(v.data(), v.size(), dst);
   };
+  // [N][K] rows repeated three times along K: [N][3 K] = [W | W | W]
+  auto put_rep3 = [&](const uint16_t* src, int N, int K, const bf16_t** dst) {
+    std::vector<uint16_t> v((size_t)N * 3 * K);
+    for (int n = 0; n < N; ++n)
+      for (int p = 0; p < 3; ++p) memcpy(&v[((size_t)n * 3 + p) * K], src + (size_t)n * K, (size_t)K * 2);
+    put_bf(v.data(), v.size(), dst);
+  };
 
   Weights& W = h->w;
   // input LayerNorm (pooling) and the memory projection with the LayerNorm folded in
@@ -622,6 +631,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     put_f(cm, &W.cmem);
     if (c.precision == CLEF_PRECISION_F32) {
       put_frag(Wm, D, H, &W.Wmem_fr);
+      put_rep3(Wm, D, H, &W.Wmem3);
       put_f(bm, &W.bmem);
     }
     put_bf(Wp16.data(), Wp16.size(), &W.Wmem16);
@@ -675,7 +685,10 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     if (NR > 0) {
       put_bf(Wkv.data(), Wkv.size(), &W.Wkv);
       put_f(bkv, &W.bkv);
-      if (c.precision == CLEF_PRECISION_F32) put_frag(Wkv.data(), NR * 2 * D, D, &W.Wkv_fr);
+      if (c.precision == CLEF_PRECISION_F32) {
+        put_frag(Wkv.data(), NR * 2 * D, D, &W.Wkv_fr);
+        put_rep3(Wkv.data(), NR * 2 * D, D, &W.Wkv3);
+      }
     } else {
       W.Wkv = nullptr;
       W.bkv = nullptr;
@@ -739,7 +752,10 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     }
     put_bf(Wf.data(), Wf.size(), &W.Wfkv);
     put_f(bfv, &W.bfkv);
-    if (c.precision == CLEF_PRECISION_F32) put_frag(Wf.data(), NL * 2 * D, D, &W.Wfkv_fr);
+    if (c.precision == CLEF_PRECISION_F32) {
+      put_frag(Wf.data(), NL * 2 * D, D, &W.Wfkv_fr);
+      put_rep3(Wf.data(), NL * 2 * D, D, &W.Wfkv3);
+    }
   }
   put_frag(bf("score.w1"), D, 4 * D, &W.Ws1);
   put_f(tof("score.b1"), &W.bs1);
@@ -775,9 +791,15 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 
 // workspace layout for one plan
 struct WsLayout {
-  size_t tab, stats, pooled, ebar, prior, mem, kv, fkv, bigpart, u, ustats, qbuf, attn, hbuf, qv, qo, gp, f, fstats,
-      fattn, pm, pl, po, part, total;
+  size_t tab, stats, pooled, ebar, prior, mem, kv, fkv, bigpart, xplanes, mplanes, u, ustats, qbuf, attn, hbuf, qv,
+      qo, gp, f, fstats, fattn, pm, pl, po, part, total;
 };
+
+// fp32 head: whole-K big GEMMs over the activations' three bf16 terms once the
+// batch has enough row tiles to fill the chip without splitting K (the memory
+// product's 4 column tiles then give more than 64 workgroups); fewer tiles run
+// on the split-K small GEMMs.
+bool f32_big_gemms(int ntiles) { return ntiles > 16; }
 
 WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   const size_t H = c.hidden_size, NQ = p.NQ, NO = p.NO, Tp = p.Tpad, NR = c.routing_layers;
@@ -806,6 +828,10 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
       if (NLx > 0) fl = std::max(fl, sgemm_shape((int)Tp, (int)NLx * 2 * D, D).part_floats);
     }
     L.bigpart = take(fl * 4);
+    if (f32_big_gemms(p.ntiles)) {
+      L.xplanes = take(Tp * 3 * H * 2);   // LayerNorm-ed rows, three bf16 terms
+      L.mplanes = take(Tp * 3 * D * 2);   // memory rows, three bf16 terms
+    }
   } else {
     const size_t sm = big_gemm_split(p.ntiles, D / 256, (int)H), skv = big_gemm_split(p.ntiles, (int)NR * 8, D);
     const size_t sf = big_gemm_split(p.ntiles, (int)NLx * 8, D);
@@ -1285,7 +1311,17 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         std::lock_guard<std::mutex> lk(g.mu);
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
-      if (f32) {
+      if (f32 && f32_big_gemms(p.ntiles)) {
+        // normalised rows as three bf16 terms times [W | W | W], then K/V the same way into head-major fp32 planes
+        bf16_t* xplanes = reinterpret_cast<bf16_t*>(ws + L.xplanes);
+        bf16_t* mplanes = reinterpret_cast<bf16_t*>(ws + L.mplanes);
+        launch_ln_split3(st, X, (int)H, p.f16, tiles, p.ntiles, stats, W.lnin_g, W.lnin_b, xplanes);
+        launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mem32, mplanes);
+        MARK(CLEF_STAGE_MEMORY_GEMM);
+        if (NR > 0) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wkv3, W.bkv, NR, kv32, p.Tpad);
+        if (cross) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wfkv3, W.bfkv, NL, fkv32, p.Tpad);
+        MARK(CLEF_STAGE_KV_GEMM);
+      } else if (f32) {
         // normalised rows times the unfolded memory weight, then K/V into head-major fp32 planes
         const int Tp = (int)p.Tpad;
         if (p.f16)

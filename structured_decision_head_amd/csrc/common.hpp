@@ -57,6 +57,26 @@ DEV void split8(const float* f, uint4& hi, uint4& lo) {
   lo = pack8(r);
 }
 
+// Split 8 floats into NT bf16 terms whose sum approximates (NT = 2) or equals
+// (NT = 3) each float: t0 = bf16(x), t1 = bf16(x - t0), t2 = bf16(x - t0 - t1).
+// Every difference is exact in fp32 (x - bf16(x) needs at most 16 significant
+// bits, and the next remainder at most 8).
+template <int NT>
+DEV void split_terms(const float* f, uint4 (&t)[NT]) {
+  float r[8], h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = f[i];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    t[j] = pack8(r);
+    if (j + 1 < NT) {
+      unpack8(t[j], h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] -= h[i];
+    }
+  }
+}
+
 DEV bf16x8 as_bf16x8(const uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 DEV bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -71,6 +91,12 @@ DEV void unpack8_f16(const uint4 v, float* f) {
   const h2 c = __builtin_bit_cast(h2, v.z), d = __builtin_bit_cast(h2, v.w);
   f[0] = (float)a.x; f[1] = (float)a.y; f[2] = (float)b.x; f[3] = (float)b.y;
   f[4] = (float)c.x; f[5] = (float)c.y; f[6] = (float)d.x; f[7] = (float)d.y;
+}
+
+// Unpack 4 bf16 held in two 32-bit words into floats.
+DEV void unpack4(uint32_t a, uint32_t b, float* f) {
+  f[0] = __uint_as_float(a << 16); f[1] = __uint_as_float(a & 0xffff0000u);
+  f[2] = __uint_as_float(b << 16); f[3] = __uint_as_float(b & 0xffff0000u);
 }
 
 // Unpack 8 16-bit values of the hidden element type (fp16 if F16, else bf16).

@@ -198,6 +198,98 @@ struct EpiKV {
   }
 };
 
+// fp32 head.  Its products run on this kernel as bf16 GEMMs of three times
+// the depth: the A rows hold the three exact bf16 terms of each fp32 value
+// side by side ([t0 | t1 | t2], each K0 wide) and the weight rows repeat
+// three times ([W | W | W]), so every product is exact and the MFMAs'
+// fp32 accumulation is the only rounding.  All tiles are transposed:
+// accumulator (mi, ni, e) of lane l is column ra0 + 32 mi + 8 (e / 4) +
+// 4 (l / 32) + e % 4 of row rb0 + 32 ni + l % 32, four consecutive columns
+// per (mi, ni, e / 4), stored straight from the accumulators.
+//
+// Memory rows: m = acc + b, written as fp32 rows [rows][1024] and as the
+// three bf16 terms of each value in [rows][3 x 1024] (the A operand of the
+// K/V product).
+struct EpiMem32 {
+  const float* bias;
+  float* mem;            // [rows][1024] fp32
+  bf16_t* planes;        // [rows][3 * 1024] bf16
+  static constexpr bool kF16 = false;
+  static constexpr bool kDirect = false;
+  static constexpr bool kRegs = true;
+  static constexpr bool kPlain = false;
+  static constexpr int kImageBytes = 0;
+  DEV bool transposed(int) const { return true; }
+  DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
+  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
+  template <bool TR>
+  DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
+                      int lane) const {
+    const int h4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int lc = ra0 + mi * 32 + 8 * g + h4;
+        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const f32x16& a = acc[mi][ni];
+          const size_t row = (size_t)(orow0 + rb0 + ni * 32 + (lane & 31));
+          const float v[4] = {a[4 * g] + b.x, a[4 * g + 1] + b.y, a[4 * g + 2] + b.z, a[4 * g + 3] + b.w};
+          *reinterpret_cast<float4*>(mem + row * 1024 + ocol0 + lc) = make_float4(v[0], v[1], v[2], v[3]);
+          float r[4] = {v[0], v[1], v[2], v[3]}, h[4];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const uint2 t = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+            *reinterpret_cast<uint2*>(planes + row * 3072 + p * 1024 + ocol0 + lc) = t;
+            if (p < 2) {
+              unpack4(t.x, t.y, h);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) r[i] -= h[i];
+            }
+          }
+        }
+      }
+  }
+};
+
+// K / V of the fp32 head: C = acc + b into head-major fp32 planes, columns
+// [64 p, 64 p + 64) -> plane p of Tpad rows of 64 (the fp32 attention's layout).
+struct EpiKV32 {
+  const float* bias;
+  float* kv;
+  long long Tpad;
+  static constexpr bool kF16 = false;
+  static constexpr bool kDirect = false;
+  static constexpr bool kRegs = true;
+  static constexpr bool kPlain = false;
+  static constexpr int kImageBytes = 0;
+  DEV bool transposed(int) const { return true; }
+  DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
+  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
+  template <bool TR>
+  DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
+                      int lane) const {
+    const int h4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int lc = ra0 + mi * 32 + 8 * g + h4, n = ocol0 + lc;
+        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
+        float* plane = kv + (size_t)(n >> 6) * Tpad * 64 + (n & 63);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const f32x16& a = acc[mi][ni];
+          const size_t row = (size_t)(orow0 + rb0 + ni * 32 + (lane & 31));
+          *reinterpret_cast<float4*>(plane + row * 64) =
+              make_float4(a[4 * g] + b.x, a[4 * g + 1] + b.y, a[4 * g + 2] + b.z, a[4 * g + 3] + b.w);
+        }
+      }
+  }
+};
+
 // Split-K partial sums: K slice s of a tile writes its raw fp32 accumulators to
 // part[s][row][col] (row in the packed row space, N columns); a reduction
 // kernel sums the slices in order and applies the memory or K/V epilogue.
@@ -644,6 +736,21 @@ void launch_gemm_mem(hipStream_t st, const bf16_t* hidden, int H, bool f16, cons
   } else {
     hipLaunchKernelGGL(k_gemm256<EpiMem>, grid, dim3(256), 0, st, hidden, H, tiles, ntn, Wm, H, 1, epi);
   }
+}
+
+void launch_gemm_mem32(hipStream_t st, const bf16_t* xplanes, int H, const int4* tiles, int ntiles,
+                       const bf16_t* Wm3, const float* bias, float* mem, bf16_t* mplanes) {
+  if (ntiles == 0) return;
+  hipLaunchKernelGGL(k_gemm256<EpiMem32>, dim3(ntiles * (1024 / BN)), dim3(256), 0, st, xplanes, 3 * H, tiles,
+                     1024 / BN, Wm3, 3 * H, 1, EpiMem32{bias, mem, mplanes});
+}
+
+void launch_gemm_kv32(hipStream_t st, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv3,
+                      const float* bias, int n_layers, float* kv, long long Tpad) {
+  if (ntiles == 0 || n_layers == 0) return;
+  const int ntn = n_layers * 2048 / BN;
+  hipLaunchKernelGGL(k_gemm256<EpiKV32>, dim3(ntiles * ntn), dim3(256), 0, st, mplanes, 3 * 1024, tiles, ntn, Wkv3,
+                     3 * 1024, 1, EpiKV32{bias, kv, Tpad});
 }
 
 void launch_gemm_kv(hipStream_t st, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,

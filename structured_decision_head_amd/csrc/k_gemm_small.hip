@@ -23,26 +23,6 @@ namespace {
 
 constexpr int SBM = kSgemmRows, SKC = 128;
 
-// Split 8 floats into NT bf16 terms whose sum approximates (NT = 2) or equals
-// (NT = 3) each float: t0 = bf16(x), t1 = bf16(x - t0), t2 = bf16(x - t0 - t1).
-// Every difference is exact in fp32 (x - bf16(x) needs at most 16 significant
-// bits, and the next remainder at most 8).
-template <int NT>
-DEV void split_terms(const float* f, uint4 (&t)[NT]) {
-  float r[8], h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = f[i];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    t[j] = pack8(r);
-    if (j + 1 < NT) {
-      unpack8(t[j], h);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r[i] -= h[i];
-    }
-  }
-}
-
 // Tile: 64 rows x (32 * 4 / WR) columns.  The 4 waves form a WR x (4 / WR)
 // grid; each wave owns 64 / WR rows and 32 columns.  Narrow tiles (WR = 2, 4)
 // give more workgroups for narrow outputs, so that the whole chip streams

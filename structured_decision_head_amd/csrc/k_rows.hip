@@ -79,6 +79,65 @@ void launch_rowstats(hipStream_t st, const bf16_t* X, int H, bool f16, const int
 }
 
 // ---------------------------------------------------------------------------
+// fp32 head: the LayerNorm-ed rows x_hat = (x - mu) rstd gamma + beta of every
+// valid row of a 256-row tile (one wave per row, grid as k_rowstats), each fp32
+// element written as its three bf16 terms (t0 + t1 + t2 = x_hat exactly) into
+// planes[row][p * H + k], p = 0, 1, 2: the A operand of the memory product run
+// as a bf16 GEMM of depth 3 H against the weight repeated three times.  The
+// arithmetic is the fp32 row loader's (LdHid).  Rows past the valid count are
+// written as zeros (the GEMM multiplies whole tiles, and those rows must stay
+// finite).
+// ---------------------------------------------------------------------------
+template <int NCH, bool F16>
+__global__ __launch_bounds__(256) void k_ln_split3(const bf16_t* __restrict__ X, const int4* __restrict__ tiles,
+                                                   const float2* __restrict__ stats, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, bf16_t* __restrict__ planes) {
+  constexpr int H = NCH * 512;
+  const int4 t = tiles[blockIdx.y];
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  bf16_t* out = planes + (size_t)(t.y + r) * 3 * H;
+  if (r >= t.z) {
+    for (int i = lane; i < 3 * H / 8; i += 64) reinterpret_cast<uint4*>(out)[i] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const float2 st = stats[t.y + r];
+  const uint4* row = reinterpret_cast<const uint4*>(X + (size_t)(t.x + r) * H);
+#pragma unroll 2
+  for (int c = 0; c < NCH; ++c) {
+    const int k = (c * 64 + lane) * 8;
+    float v[8], x[8];
+    unpack8_hidden<F16>(row[c * 64 + lane], v);
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + k), g1 = *reinterpret_cast<const float4*>(gamma + k + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(beta + k), b1 = *reinterpret_cast<const float4*>(beta + k + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (v[i] - st.x) * st.y * gg[i] + bb[i];
+    uint4 tt[3];
+    split_terms<3>(x, tt);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(out + (size_t)p * H + k) = tt[p];
+  }
+}
+
+void launch_ln_split3(hipStream_t st, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles,
+                      const float2* stats, const float* gamma, const float* beta, bf16_t* planes) {
+  if (ntiles == 0) return;
+  const dim3 grid(64, ntiles), block(256);
+  switch (H / 512) {
+#define CASE(n)                                                                                                  \
+  case n:                                                                                                        \
+    if (f16) hipLaunchKernelGGL((k_ln_split3<n, true>), grid, block, 0, st, X, tiles, stats, gamma, beta, planes); \
+    else hipLaunchKernelGGL((k_ln_split3<n, false>), grid, block, 0, st, X, tiles, stats, gamma, beta, planes);    \
+    break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Span gathers (pooling and the lexical mean).  One block of 4 waves per
 // entry; wave w takes the entry's rows w, w + 4, w + 8, ..., R at a time with
 // all R rows' loads in flight (R = 4, or 2 for rows wider than 4096 elements,

@@ -27,6 +27,10 @@ void launch_fill_u32(hipStream_t, void* p, size_t bytes, uint32_t v);
 // tiles: int4 (first hidden row, first packed row, valid rows <= 256, record)
 void launch_rowstats(hipStream_t, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles, float2* stats,
                      float eps);
+// fp32 head: LayerNorm-ed rows of every tile's valid rows as three bf16 terms,
+// planes[t.y + r][p * H + k]
+void launch_ln_split3(hipStream_t, const bf16_t* X, int H, bool f16, const int4* tiles, int ntiles,
+                      const float2* stats, const float* gamma, const float* beta, bf16_t* planes);
 // entries: int4 (first hidden row, length, first stats row, output slot)
 void launch_pool(hipStream_t, const bf16_t* X, int H, bool f16, const int4* ent, int nent, const float2* stats,
                  const float* gamma, const float* beta, float* out);
@@ -52,6 +56,16 @@ int big_gemm_split(int ntiles, int ntn, int K);
 void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const int4* tiles, int ntiles,
                      const bf16_t* Wm, const float2* stats, const float* c, const float* d, bf16_t* mem,
                      float* part, long long Tpad, int split = 0, long long row0 = 0);
+// fp32 head: the memory product over the LayerNorm-ed rows' three bf16 terms
+// (xplanes [rows][3 H], rows in the packed row space, tiles with first A row =
+// first packed row) against Wm3 = [W | W | W] ([1024][3 H]); writes fp32 rows
+// mem [rows][1024] and their three bf16 terms mplanes [rows][3 x 1024].  The
+// K/V product over mplanes against Wkv3 = [Wkv | Wkv | Wkv] writes fp32
+// head-major planes ([layer][K|V][head][Tpad][64]).  Whole-K launches.
+void launch_gemm_mem32(hipStream_t, const bf16_t* xplanes, int H, const int4* tiles, int ntiles, const bf16_t* Wm3,
+                       const float* bias, float* mem, bf16_t* mplanes);
+void launch_gemm_kv32(hipStream_t, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv3,
+                      const float* bias, int n_layers, float* kv, long long Tpad);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
                     const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part, int split = 0,
                     long long row0 = 0);

@@ -144,6 +144,33 @@ def test_f32_decoder_fields_and_gate_closed(torch_gpu):
     _check(case, out, "gate closed fp32")
 
 
+def test_f32_big_gemm_path_memory_rows_and_decoder(torch_gpu):
+    """A batch of more than 16 row tiles, where the memory and K/V products run
+    as whole-K bf16 GEMMs over the three bf16 terms of each fp32 activation
+    (the single-record and small-batch tests above take the split-K path):
+    one record's memory rows against the oracle's, then every output, with
+    the decoder-layer field variant so that the field K/V product runs too."""
+    from structured_decision_head_amd import clefhead as C
+    spec = f32(synth.config_spec(1, B=6, L=3000, lengths=("uniform", 2500, 3000),
+                                 head=synth.HeadConfig(vocab_size=4096, field_cross_attention=1)))
+    case = synth.make_case(spec)
+    b = case.batch
+    tiles = sum(-(-int(n) // 256) for n in b.lengths)
+    say(f"case fp32 mode, {tiles} row tiles, decoder-layer fields: lengths={b.lengths.tolist()}")
+    assert tiles > 16
+    r, out = _run(case, trace=True)
+    n0 = int(b.lengths[0])
+    mem = r.trace(C.CLEF_TRACE_MEMORY, (tiles * 256, case.head.width))[:n0]
+    r.close()
+    p = O.load_params(case.weights)
+    xh = O.layer_norm(O.hidden_rows(b, 0, n0), p["ln_in.w"], p["ln_in.b"], case.head.ln_eps)
+    ref = O.linear(xh, p["mem.w"], p["mem.b"])
+    rel = float(np.abs(mem - ref).max() / np.abs(ref).max())
+    say(f"  memory rows of record 0: max relative error {rel:.2e}")
+    assert rel < 2e-5
+    _check(case, out, "fp32 big-GEMM path, decoder fields")
+
+
 def test_f32_refuses_streamed_ingest(torch_gpu):
     from structured_decision_head_amd import clefhead as C
     from structured_decision_head_amd.runner import HeadRunner
