@@ -121,6 +121,10 @@ def test_poisoned_working_memory_changes_nothing(torch_gpu):
             mini, head=dataclasses.replace(mini.head, field_cross_attention=1))), C.CLEF_PADDED, {}),
         "fp32 mode": (synth.make_case(dataclasses.replace(
             mini, head=dataclasses.replace(mini.head, precision=1))), C.CLEF_PADDED, {}),
+        # 25 row tiles: the fp32 products run as whole-K GEMMs over three-term rows
+        "fp32 mode, whole-K GEMMs": (synth.make_case(dataclasses.replace(
+            mini, B=5, lengths=("uniform", 1030, 1100), head=dataclasses.replace(mini.head, precision=1))),
+            C.CLEF_PADDED, {}),
         "single record": (synth.config_case(0), C.CLEF_PADDED, {}),
         "H=5120 NaN padding": (synth.make_case(mini4()), C.CLEF_PADDED, {}),
     }
@@ -170,8 +174,10 @@ def test_allocation_failure_gives_nomem(torch_gpu):
 
 def _offset_outlier_case(precision):
     """Hidden rows x = offset_row + scale_row * z with offsets up to +-8, scales
-    0.5..4 and four channels carrying values near +-200 (bf16-rounded)."""
-    spec = synth.config_spec(1, B=3, L=1100, lengths=("uniform", 600, 1100), seed=4242,
+    0.5..4 and four channels carrying values near +-200 (bf16-rounded).  25 row
+    tiles, so that the memory projection runs whole-K (the folded LayerNorm in
+    its epilogue; in the fp32 mode the three-term rows)."""
+    spec = synth.config_spec(1, B=5, L=1100, lengths=("uniform", 1030, 1100), seed=4242,
                              head=synth.HeadConfig(vocab_size=4096, precision=precision))
     case = synth.make_case(spec)
     b = case.batch
