@@ -14,8 +14,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define DEV __device__ __forceinline__
 
-DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-
 // Two floats to two bf16 (round to nearest even, hardware conversion), a in the low half.
 DEV uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -44,17 +42,6 @@ DEV uint4 pack8(const float* f) {
   v.z = pack_bf16x2(f[4], f[5]);
   v.w = pack_bf16x2(f[6], f[7]);
   return v;
-}
-
-// Split 8 floats into hi = bf16(x) and lo = bf16(x - hi); hi + lo carries
-// about 16 significant bits of x.
-DEV void split8(const float* f, uint4& hi, uint4& lo) {
-  hi = pack8(f);
-  float h[8], r[8];
-  unpack8(hi, h);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = f[i] - h[i];
-  lo = pack8(r);
 }
 
 // Split 8 floats into NT bf16 terms whose sum approximates (NT = 2) or equals
