@@ -427,11 +427,12 @@ struct Weights {
   const bf16_t* Wfkv = nullptr;   // decoder-layer field variant: cross K/V of every field layer, stacked
   const float* bfkv = nullptr;
   // precision mode fp32: the memory projection unfolded (LayerNorm applied to the rows) with its own bias,
-  // and the stacked K/V projections, in the small GEMMs' fragment order (batches of few row tiles) and as
-  // rows repeated three times, [W | W | W] (the big GEMM over the three bf16 terms of each activation)
+  // and the stacked K/V projections, in the small GEMMs' fragment order (batches of few row tiles); the
+  // memory weight also as rows repeated three times, [W | W | W] (the big GEMM over the three bf16 terms
+  // of each activation; the K/V product reads Wkv / Wfkv three times instead)
   const float* bmem = nullptr;
   const bf16_t *Wmem_fr = nullptr, *Wkv_fr = nullptr, *Wfkv_fr = nullptr;
-  const bf16_t *Wmem3 = nullptr, *Wkv3 = nullptr, *Wfkv3 = nullptr;
+  const bf16_t* Wmem3 = nullptr;
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -685,10 +686,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     if (NR > 0) {
       put_bf(Wkv.data(), Wkv.size(), &W.Wkv);
       put_f(bkv, &W.bkv);
-      if (c.precision == CLEF_PRECISION_F32) {
-        put_frag(Wkv.data(), NR * 2 * D, D, &W.Wkv_fr);
-        put_rep3(Wkv.data(), NR * 2 * D, D, &W.Wkv3);
-      }
+      if (c.precision == CLEF_PRECISION_F32) put_frag(Wkv.data(), NR * 2 * D, D, &W.Wkv_fr);
     } else {
       W.Wkv = nullptr;
       W.bkv = nullptr;
@@ -752,10 +750,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
     }
     put_bf(Wf.data(), Wf.size(), &W.Wfkv);
     put_f(bfv, &W.bfkv);
-    if (c.precision == CLEF_PRECISION_F32) {
-      put_frag(Wf.data(), NL * 2 * D, D, &W.Wfkv_fr);
-      put_rep3(Wf.data(), NL * 2 * D, D, &W.Wfkv3);
-    }
+    if (c.precision == CLEF_PRECISION_F32) put_frag(Wf.data(), NL * 2 * D, D, &W.Wfkv_fr);
   }
   put_frag(bf("score.w1"), D, 4 * D, &W.Ws1);
   put_f(tof("score.b1"), &W.bs1);
@@ -1312,14 +1307,15 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
       if (f32 && f32_big_gemms(p.ntiles)) {
-        // normalised rows as three bf16 terms times [W | W | W], then K/V the same way into head-major fp32 planes
+        // normalised rows as three bf16 terms times [W | W | W], then their three-term memory rows times Wkv
+        // read three times, into head-major fp32 planes
         bf16_t* xplanes = reinterpret_cast<bf16_t*>(ws + L.xplanes);
         bf16_t* mplanes = reinterpret_cast<bf16_t*>(ws + L.mplanes);
         launch_ln_split3(st, X, (int)H, p.f16, tiles, p.ntiles, stats, W.lnin_g, W.lnin_b, xplanes);
         launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mem32, mplanes);
         MARK(CLEF_STAGE_MEMORY_GEMM);
-        if (NR > 0) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wkv3, W.bkv, NR, kv32, p.Tpad);
-        if (cross) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wfkv3, W.bfkv, NL, fkv32, p.Tpad);
+        if (NR > 0) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv32, p.Tpad);
+        if (cross) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wfkv, W.bfkv, NL, fkv32, p.Tpad);
         MARK(CLEF_STAGE_KV_GEMM);
       } else if (f32) {
         // normalised rows times the unfolded memory weight, then K/V into head-major fp32 planes

@@ -49,6 +49,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   static constexpr bool kDirect = false;               // output staged through LDS
   static constexpr bool kRegs = false;
   static constexpr bool kPlain = false;                // every tile transposed
+  static constexpr int kWrapW = 0;
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
   static constexpr int kImageBytes = 256 * kLd * 2;
   DEV bool transposed(int) const { return true; }
@@ -121,6 +122,7 @@ struct EpiKV {
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;                  // stored from the accumulators
   static constexpr bool kPlain = true;                 // V tiles are plain
+  static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV bf16_t* head_base(int col) const {
@@ -200,8 +202,10 @@ struct EpiKV {
 
 // fp32 head.  Its products run on this kernel as bf16 GEMMs of three times
 // the depth: the A rows hold the three exact bf16 terms of each fp32 value
-// side by side ([t0 | t1 | t2], each K0 wide) and the weight rows repeat
-// three times ([W | W | W]), so every product is exact and the MFMAs'
+// side by side ([t0 | t1 | t2], each K0 wide) and every term meets the same
+// weight row (stored repeated, [W | W | W], for the memory product; read
+// three times through the K-position wrap for the K/V product, whose 2 MB
+// column group then stays in L2), so every product is exact and the MFMAs'
 // fp32 accumulation is the only rounding.  All tiles are transposed:
 // accumulator (mi, ni, e) of lane l is column ra0 + 32 mi + 8 (e / 4) +
 // 4 (l / 32) + e % 4 of row rb0 + 32 ni + l % 32, four consecutive columns
@@ -218,6 +222,7 @@ struct EpiMem32 {
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
   static constexpr bool kPlain = false;
+  static constexpr int kWrapW = 0;       // the weight stored repeated, [W | W | W]
   static constexpr int kImageBytes = 0;
   DEV bool transposed(int) const { return true; }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
@@ -264,6 +269,7 @@ struct EpiKV32 {
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
   static constexpr bool kPlain = false;
+  static constexpr int kWrapW = 1024;    // one [N][1024] weight read three times: its 2 MB column group stays in L2
   static constexpr int kImageBytes = 0;
   DEV bool transposed(int) const { return true; }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
@@ -303,6 +309,7 @@ struct EpiPart {
   static constexpr bool kDirect = true;
   static constexpr bool kRegs = false;
   static constexpr bool kPlain = false;
+  static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
   DEV bool transposed(int) const { return true; }
   DEV void load_consts(int, int, int, float (&)[4]) const {}
@@ -405,16 +412,21 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   // as the scalar offset.
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)(A + (size_t)T.x * lda), 0, T.z * lda * 2, 0x00020000);   // valid rows only
+  // W rows are K long, or Epi::kWrapW long when the product's depth repeats
+  // the weight (K position k reads W column k mod kWrapW, a power of two)
+  constexpr int kWrap = Epi::kWrapW;
+  const int ldw = kWrap ? kWrap : K;
   const __amdgpu_buffer_rsrc_t rsw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)(tn * BN) * K), 0, BN * K * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)(tn * BN) * ldw), 0, BN * ldw * 2, 0x00020000);
   // rows of copy i are 8 i after those of copy 0, so their swizzle term
   // ((row >> 1) & 7) differs by 4 i mod 8: even and odd copies use two bases.
   // Rows past the tile's valid count read zeros (outside the A resource).
   const int crow = 64 * w + (lane >> 3);
   const int cch = (lane & 7) ^ ((crow >> 1) & 7);
   const uint32_t aoffE = (uint32_t)(crow * lda + cch * 8) * 2, aoffO = (uint32_t)(crow * lda + (cch ^ 4) * 8) * 2;
-  const uint32_t woffE = (uint32_t)(crow * K + cch * 8) * 2, woffO = (uint32_t)(crow * K + (cch ^ 4) * 8) * 2;
-  const uint32_t astep = (uint32_t)(8 * lda) * 2, wstep = (uint32_t)(8 * K) * 2;
+  const uint32_t woffE = (uint32_t)(crow * ldw + cch * 8) * 2, woffO = (uint32_t)(crow * ldw + (cch ^ 4) * 8) * 2;
+  const uint32_t astep = (uint32_t)(8 * lda) * 2, wstep = (uint32_t)(8 * ldw) * 2;
+#define WCOL(k) (kWrap ? ((k) & (kWrap - 1)) : (k))
   // fragment positions: 32x32x16 operands, lane -> row (lane & 31), chunk 2 kk + (lane >> 5).
   // Block bases are multiples of 32 rows, so the swizzle depends on the lane only
   // and block i of a substep sits 256 chunks after block 0.
@@ -428,7 +440,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
 #define COPY_B(stage, k0)                                                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? woffO : woffE) + i * wstep, (kbase + (k0)) * 2, 0, 0);
+                                             ((i & 1) ? woffO : woffE) + i * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
 #define COPY_STAGE(stage, k0) COPY_A(stage, k0) COPY_B(stage, k0)
 #define LOAD_FRAGS(F, stage, kk)                                                 \
   {                                                                              \
@@ -488,7 +500,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
                                            (((i) & 1) ? aoffO : aoffE) + (i) * astep, (kbase + (k0)) * 2, 0, 0);
 #define CPB1(stage, k0, i)                                                                      \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + (i))], 16, \
-                                           (((i) & 1) ? woffO : woffE) + (i) * wstep, (kbase + (k0)) * 2, 0, 0);
+                                           (((i) & 1) ? woffO : woffE) + (i) * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
 #define HALF_CP(F, G, gst, gkk, CP, cst, ck0)                                                   \
   _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                               \
     MFMA2(F, t)                                                                                 \
@@ -568,6 +580,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
     MULTIPLY(Y)
     __builtin_amdgcn_sched_barrier(0);
   }
+#undef WCOL
 #undef MFMA2
 #undef FRAG1
 #undef CPA1
@@ -745,11 +758,11 @@ void launch_gemm_mem32(hipStream_t st, const bf16_t* xplanes, int H, const int4*
                      1024 / BN, Wm3, 3 * H, 1, EpiMem32{bias, mem, mplanes});
 }
 
-void launch_gemm_kv32(hipStream_t st, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv3,
+void launch_gemm_kv32(hipStream_t st, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv,
                       const float* bias, int n_layers, float* kv, long long Tpad) {
   if (ntiles == 0 || n_layers == 0) return;
   const int ntn = n_layers * 2048 / BN;
-  hipLaunchKernelGGL(k_gemm256<EpiKV32>, dim3(ntiles * ntn), dim3(256), 0, st, mplanes, 3 * 1024, tiles, ntn, Wkv3,
+  hipLaunchKernelGGL(k_gemm256<EpiKV32>, dim3(ntiles * ntn), dim3(256), 0, st, mplanes, 3 * 1024, tiles, ntn, Wkv,
                      3 * 1024, 1, EpiKV32{bias, kv, Tpad});
 }
 

@@ -60,11 +60,12 @@ void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const i
 // (xplanes [rows][3 H], rows in the packed row space, tiles with first A row =
 // first packed row) against Wm3 = [W | W | W] ([1024][3 H]); writes fp32 rows
 // mem [rows][1024] and their three bf16 terms mplanes [rows][3 x 1024].  The
-// K/V product over mplanes against Wkv3 = [Wkv | Wkv | Wkv] writes fp32
-// head-major planes ([layer][K|V][head][Tpad][64]).  Whole-K launches.
+// K/V product over mplanes against the stacked Wkv ([N][1024], read once per
+// term) writes fp32 head-major planes ([layer][K|V][head][Tpad][64]).
+// Whole-K launches.
 void launch_gemm_mem32(hipStream_t, const bf16_t* xplanes, int H, const int4* tiles, int ntiles, const bf16_t* Wm3,
                        const float* bias, float* mem, bf16_t* mplanes);
-void launch_gemm_kv32(hipStream_t, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv3,
+void launch_gemm_kv32(hipStream_t, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv,
                       const float* bias, int n_layers, float* kv, long long Tpad);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
                     const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part, int split = 0,
