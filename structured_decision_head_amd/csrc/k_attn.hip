@@ -187,111 +187,139 @@ void launch_route_attn(hipStream_t st, const float* Q, const bf16_t* Kl, const b
                      rec, pm, pl, po, Ptot, chunk, scale_log2);
 }
 
-// fp32 routing attention (precision mode fp32): one 256-thread block per
-// (work item, head).  Thread t owns query t / 8 of the item's 32-query block
-// and 8 of its 64 dims (t % 8); a score is the sum of the 8 parts' dot
-// products (three lane exchanges).  Keys and values are staged in LDS 64 rows
-// at a time; the online softmax takes 8 keys per step (one rescale per step).
-// The queries carry log2(e) / sqrt(64) and the partials are written exactly as
-// k_route_attn writes them, so k_route_combine merges either.
-__global__ __launch_bounds__(256) void k_route_attn32(const float* __restrict__ Q, const float* __restrict__ Kl,
-                                                      const float* __restrict__ Vl, long long Tpad,
-                                                      const int4* __restrict__ items, const int* __restrict__ rec,
-                                                      float* __restrict__ pm, float* __restrict__ pl,
-                                                      float* __restrict__ po, long long Ptot, int chunk,
-                                                      float scale_log2) {
-  __shared__ float4 sK[64][16], sV[64][16];
-  const int j = blockIdx.y;
-  const int4 bc = items[blockIdx.x];     // (record, chunk, first query of the block, -)
+namespace {
+
+// fp32 K or V of one 32-key step: 8 fragments, fragment q at float4 index
+// 64 q + lane of the 2048-float block (k32_off / v32_off order).
+DEV void frag_load32(f32x4 (&r)[8], const float* P, int row0, int lane) {
+  const float* p = P + (size_t)(row0 >> 5) * 2048 + lane * 4;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r[q] = *reinterpret_cast<const f32x4*>(p + q * 256);
+}
+
+// One 32-key step in fp32 on v_mfma_f32_32x32x2_f32 (A: lane l gives row
+// l % 32 at depth l / 32; B: column l % 32 at depth l / 32).  S^T = K Q^T as
+// 32 depth-2 products (product i: dims 2 i, 2 i + 1; lane l holds query l % 32
+// at dims 2 i + l / 32); the lane then owns query l % 32 and keys
+// kb + 8 (e / 4) + 4 g + (e % 4) as in the bf16 kernel, and product i of
+// O^T = V^T P^T takes exactly those keys for e = i.
+DEV void kv_step32(const f32x4 (&k)[8], const f32x4 (&v)[8], const float (&q)[32], int kb, int n, int g, float& m,
+                   float& l, f32x16 (&o)[2]) {
+  f32x16 s;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[i >> 2][i & 3], q[i], s, 0, 0, 0);
+  float mx = -INFINITY;
+  if (kb + 32 <= n) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kb + 8 * (e >> 2) + 4 * g + (e & 3);
+      s[e] = (key < n) ? s[e] : -INFINITY;
+      mx = fmaxf(mx, s[e]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mn = fmaxf(m, mx);          // finite: key kb < n is always valid
+  // v_exp_f32 as in the bf16 kernel (its only difference from the library's
+  // exp2f: results below 2^-126 may come out as zero)
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);   // m = -inf gives 0
+  float ls = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s[e] = __builtin_amdgcn_exp2f(s[e] - mn);
+    ls += s[e];
+  }
+  ls += __shfl_xor(ls, 32, 64);
+  l = l * alpha + ls;
+  m = mn;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    o[0][e] *= alpha;
+    o[1][e] *= alpha;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[4 * dt + (i >> 2)][i & 3], s[i], o[dt], 0, 0, 0);
+}
+
+}  // namespace
+
+// fp32 routing attention (precision mode fp32): the bf16 kernel's work split
+// (one wave per (record, chunk, 32-query block, head)) with fp32 operands on
+// the matrix cores; the next 32-key step's keys and values are loaded while
+// the current one is multiplied.  The queries carry log2(e) / sqrt(64) and the
+// partials are written exactly as k_route_attn writes them, so
+// k_route_combine merges either.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_route_attn32(
+    const float* __restrict__ Q, const float* __restrict__ Kl, const float* __restrict__ Vl, long long Tpad,
+    const int4* __restrict__ items, int nitems, const int* __restrict__ rec, float* __restrict__ pm,
+    float* __restrict__ pl, float* __restrict__ po, long long Ptot, int chunk, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int gx = gridDim.x;
+  const int rl = xcd_remap(blockIdx.x + blockIdx.y * gx, gx * gridDim.y);
+  const int it = (rl % gx) * 4 + (threadIdx.x >> 6);
+  if (it >= nitems) return;
+  const int j = rl / gx;
+  const int4 bc = items[it];             // (record, chunk, first query of the block, -)
   const int* R = rec + 8 * bc.x;
   const int kv0 = R[0], n = R[1], o0 = R[2], no = R[3], pbase = R[4], nc = R[5];
   const int c = bc.y;
   const int k_lo = c * chunk, k_hi = min(n, k_lo + chunk);   // every chunk holds at least one key
   const float* Kj = Kl + (size_t)j * Tpad * 64;
   const float* Vj = Vl + (size_t)j * Tpad * 64;
-  const int t = threadIdx.x, part = t & 7;
-  const int qi = bc.z + (t >> 3);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int qi = bc.z + l32;
   const bool qvalid = qi < no;
-  float q[8], o[8];
+  float q[32];
   {
-    const float* qp = Q + (size_t)(o0 + (qvalid ? qi : 0)) * 1024 + j * 64 + part * 8;
-    const float4 a = *reinterpret_cast<const float4*>(qp), b = *reinterpret_cast<const float4*>(qp + 4);
-    f4x2(a, b, q);
+    const float* qp = Q + (size_t)(o0 + (qvalid ? qi : 0)) * 1024 + j * 64;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      q[d] = qvalid ? q[d] * scale_log2 : 0.f;
-      o[d] = 0.f;
+    for (int t = 0; t < 16; ++t) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(qp + 4 * t);   // dims 4 t .. 4 t + 3
+      q[2 * t] = qvalid ? a[g] * scale_log2 : 0.f;
+      q[2 * t + 1] = qvalid ? a[2 + g] * scale_log2 : 0.f;
     }
   }
   float m = -INFINITY, l = 0.f;
+  f32x16 o[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
+
+  // K is double-buffered (two 32-key steps per iteration, so that both
+  // buffers have static registers); V has one buffer, refilled for the next
+  // step as soon as the current step's value products have been issued, and
+  // needed only after that step's scores and softmax
+  f32x4 ka[8], kb2[8], v[8];
+  frag_load32(ka, Kj, kv0 + k_lo, lane);
+  frag_load32(v, Vj, kv0 + k_lo, lane);
   for (int kb = k_lo; kb < k_hi; kb += 64) {
-    const int nk = min(64, k_hi - kb);
-    __syncthreads();   // the previous tile has been read
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int idx = t + 256 * r4, row = idx >> 4, c4 = idx & 15;
-      if (row < nk) {
-        const size_t off = (size_t)(kv0 + kb + row) * 64 + 4 * c4;
-        sK[row][c4] = *reinterpret_cast<const float4*>(Kj + off);
-        sV[row][c4] = *reinterpret_cast<const float4*>(Vj + off);
-      }
-    }
-    __syncthreads();
-    for (int k8 = 0; k8 < nk; k8 += 8) {
-      const int kn = min(8, nk - k8);   // uniform over the block
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s[i] = 0.f;
-        if (i < kn) {
-          float kk[8];
-          f4x2(sK[k8 + i][2 * part], sK[k8 + i][2 * part + 1], kk);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) s[i] += q[d] * kk[d];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s[i] += __shfl_xor(s[i], 1, 64);
-        s[i] += __shfl_xor(s[i], 2, 64);
-        s[i] += __shfl_xor(s[i], 4, 64);
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i)
-        if (i < kn) mx = fmaxf(mx, s[i]);
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2f(m - mn);   // m = -inf gives 0
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = i < kn ? exp2f(s[i] - mn) : 0.f;
-        ps += p[i];
-      }
-      l = l * alpha + ps;
-      m = mn;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < kn) {
-          float vv[8];
-          f4x2(sV[k8 + i][2 * part], sV[k8 + i][2 * part + 1], vv);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) o[d] += p[i] * vv[d];
-        }
-      }
-    }
+    if (kb + 32 < k_hi) frag_load32(kb2, Kj, kv0 + kb + 32, lane);
+    kv_step32(ka, v, q, kb, n, g, m, l, o);
+    if (kb + 32 >= k_hi) break;
+    frag_load32(v, Vj, kv0 + kb + 32, lane);
+    if (kb + 64 < k_hi) frag_load32(ka, Kj, kv0 + kb + 64, lane);
+    kv_step32(kb2, v, q, kb + 32, n, g, m, l, o);
+    if (kb + 64 < k_hi) frag_load32(v, Vj, kv0 + kb + 64, lane);
   }
   if (qvalid) {
     const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
-    if (part == 0) {
+    if (g == 0) {
       pm[slot] = m;
       pl[slot] = l;
     }
-    float* op = po + slot * 64 + part * 8;
-    *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    float* op = po + slot * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(op + dt * 32 + 8 * i + 4 * g) =
+            make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
   }
 }
 
@@ -300,8 +328,8 @@ void launch_route_attn32(hipStream_t st, const float* Q, const float* Kl, const 
                          long long Ptot, int chunk) {
   if (nitems == 0) return;
   const float scale_log2 = 0.125f * 1.4426950408889634f;   // 1/sqrt(64) * log2(e)
-  hipLaunchKernelGGL(k_route_attn32, dim3(nitems, 16), dim3(256), 0, st, Q, Kl, Vl, Tpad, items, rec, pm, pl, po,
-                     Ptot, chunk, scale_log2);
+  hipLaunchKernelGGL(k_route_attn32, dim3((nitems + 3) / 4, 16), dim3(256), 0, st, Q, Kl, Vl, Tpad, items, nitems,
+                     rec, pm, pl, po, Ptot, chunk, scale_log2);
 }
 
 // Merge the chunk partials of (option, head): one wave.  Lanes split the

@@ -260,7 +260,17 @@ struct EpiMem32 {
 };
 
 // K / V of the fp32 head: C = acc + b into head-major fp32 planes, columns
-// [64 p, 64 p + 64) -> plane p of Tpad rows of 64 (the fp32 attention's layout).
+// [64 p, 64 p + 64) -> plane p of Tpad rows, in 32-row blocks of the fp32
+// routing attention's fragment order (k32_off / v32_off).  K tiles are
+// transposed, V tiles plain, so that each store instruction of a wave covers
+// whole 16-byte runs of one block:
+//  * K: accumulator (mi, ni, 4 g' + c) of lane l is dim d0 + c, d0 =
+//    ra0 + 32 mi + 8 g' + 4 (l / 32), of key rb0 + 32 ni + l % 32; dims d0 and
+//    d0 + 2 (d0 + 1 and d0 + 3) are consecutive floats of one parity run, the
+//    two lanes l and l + 32 fill a 16-byte slot together (512 bytes a store);
+//  * V: accumulator (mi, ni, 4 g' + c) of lane l is key ra0 + 32 mi + 8 g' +
+//    4 (l / 32) + c of dim rb0 + 32 ni + l % 32: one 16-byte slot per lane,
+//    64 (4 (d / 32) + g') + l in the block (1 KB a store).
 struct EpiKV32 {
   const float* bias;
   float* kv;
@@ -268,31 +278,49 @@ struct EpiKV32 {
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
-  static constexpr bool kPlain = false;
+  static constexpr bool kPlain = true;   // V tiles are plain
   static constexpr int kWrapW = 1024;    // one [N][1024] weight read three times: its 2 MB column group stays in L2
   static constexpr int kImageBytes = 0;
-  DEV bool transposed(int) const { return true; }
+  DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
   DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
   template <bool TR>
   DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
                       int lane) const {
-    const int h4 = 4 * (lane >> 5);
+    const int hh = lane >> 5;
+    if constexpr (TR) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int lc = ra0 + mi * 32 + 8 * g + h4, n = ocol0 + lc;
-        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
-        float* plane = kv + (size_t)(n >> 6) * Tpad * 64 + (n & 63);
+        for (int g = 0; g < 4; ++g) {
+          const int lc = ra0 + mi * 32 + 8 * g + 4 * hh, n = ocol0 + lc, d0 = n & 63;
+          const float4 b = *reinterpret_cast<const float4*>(cst + lc);
+          float* base = kv + (size_t)(n >> 6) * Tpad * 64 + (size_t)((d0 >> 3) * 64 + (lane & 31)) * 4 + ((d0 >> 1) & 3);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+          for (int ni = 0; ni < 4; ++ni) {
+            const f32x16& a = acc[mi][ni];
+            float* blk = base + (size_t)((orow0 + rb0 + ni * 32) >> 5) * 2048;
+            *reinterpret_cast<float2*>(blk) = make_float2(a[4 * g] + b.x, a[4 * g + 2] + b.z);
+            *reinterpret_cast<float2*>(blk + 128) = make_float2(a[4 * g + 1] + b.y, a[4 * g + 3] + b.w);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int lc = rb0 + ni * 32 + (lane & 31), n = ocol0 + lc;
+        const float b = cst[lc];
+        float* base = kv + (size_t)(n >> 6) * Tpad * 64 + (size_t)(((n & 63) >> 5) * 256 + lane) * 4;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
           const f32x16& a = acc[mi][ni];
-          const size_t row = (size_t)(orow0 + rb0 + ni * 32 + (lane & 31));
-          *reinterpret_cast<float4*>(plane + row * 64) =
-              make_float4(a[4 * g] + b.x, a[4 * g + 1] + b.y, a[4 * g + 2] + b.z, a[4 * g + 3] + b.w);
+          float* blk = base + (size_t)((orow0 + ra0 + mi * 32) >> 5) * 2048;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(blk + g * 256) =
+                make_float4(a[4 * g] + b, a[4 * g + 1] + b, a[4 * g + 2] + b, a[4 * g + 3] + b);
         }
       }
+    }
   }
 };
 

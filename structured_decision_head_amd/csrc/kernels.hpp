@@ -16,6 +16,23 @@ hipError_t noalloc_scratch(int device, void** out);
 // feeds to a V^T P^T MFMA step sit in 16 contiguous bytes.
 DEV int vblock_pos(int k) { return (k & 16) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3); }
 
+// fp32 head: K and V of one head are planes of Tpad keys x 64 dims, stored in
+// blocks of 32 keys (2048 floats) in the order of the fp32 routing attention's
+// v_mfma_f32_32x32x2_f32 fragments, so that each fragment load of a wave reads
+// 1 KB of contiguous memory.  K (A operand of S^T = K Q^T, call i covers dims
+// 2 i and 2 i + 1): lane l reads dims d with d % 2 = l / 32 of key l % 32, in
+// float4 groups of consecutive d / 2.  V (A operand of O^T = V^T P^T, call i
+// covers keys 8 (i / 4) + (i % 4) and that + 4, the order of the score
+// accumulators): lane l reads dim 32 dt + l % 32 at keys with (k / 4) % 2 = l / 32.
+DEV size_t k32_off(int key, int d) {
+  const int idx = d >> 1;
+  return (size_t)(key >> 5) * 2048 + ((((idx >> 2) * 2 + (d & 1)) * 32 + (key & 31)) << 2) + (idx & 3);
+}
+DEV size_t v32_off(int key, int d) {
+  const int k = key & 31;
+  return (size_t)(key >> 5) * 2048 + (((((d >> 5) * 4 + (k >> 3)) * 2 + ((k >> 2) & 1)) * 32 + (d & 31)) << 2) + (k & 3);
+}
+
 // Fill `bytes` (a multiple of 4) at p with the 32-bit pattern v (a kernel, so
 // that it can sit in a captured graph; used to poison fresh working memory).
 void launch_fill_u32(hipStream_t, void* p, size_t bytes, uint32_t v);
@@ -61,8 +78,8 @@ void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const i
 // first packed row) against Wm3 = [W | W | W] ([1024][3 H]); writes fp32 rows
 // mem [rows][1024] and their three bf16 terms mplanes [rows][3 x 1024].  The
 // K/V product over mplanes against the stacked Wkv ([N][1024], read once per
-// term) writes fp32 head-major planes ([layer][K|V][head][Tpad][64]).
-// Whole-K launches.
+// term) writes fp32 head-major planes ([layer][K|V][head][Tpad][64], 32-row
+// blocks in k32_off / v32_off order).  Whole-K launches.
 void launch_gemm_mem32(hipStream_t, const bf16_t* xplanes, int H, const int4* tiles, int ntiles, const bf16_t* Wm3,
                        const float* bias, float* mem, bf16_t* mplanes);
 void launch_gemm_kv32(hipStream_t, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv,
@@ -304,10 +321,13 @@ struct EpResid {         // C += acc + bias (residual stream)
 };
 
 struct EpHeads {         // C = acc + bias into head-major planes: columns [64 p, 64 p + 64) -> plane p of Tpad rows
-  float* C;
+  float* C;              // columns stacked [K_0 | V_0 | K_1 | V_1 | ...], 1024 each; planes in k32_off / v32_off order
   long long Tpad;
   const float* bias;
-  DEV float* at(int m, int n) const { return C + ((size_t)(n >> 6) * Tpad + m) * 64 + (n & 63); }
+  DEV float* at(int m, int n) const {
+    const int d = n & 63;
+    return C + (size_t)(n >> 6) * Tpad * 64 + (((n >> 10) & 1) ? v32_off(m, d) : k32_off(m, d));
+  }
   DEV float operator()(int m, int n, float v) const {
     const float r = v + bias[n];
     *at(m, n) = r;
@@ -317,7 +337,10 @@ struct EpHeads {         // C = acc + bias into head-major planes: columns [64 p
   DEV Pre pre4(int, int n) const { return Pre{ld_f4(bias + n)}; }
   DEV float4 apply4(int m, int n, float4 v, const Pre& p) const {   // the 4 columns never straddle a plane
     const float4 r = add_f4(v, p.b);
-    st_f4(at(m, n), r);
+    *at(m, n) = r.x;
+    *at(m, n + 1) = r.y;
+    *at(m, n + 2) = r.z;
+    *at(m, n + 3) = r.w;
     return r;
   }
 };
@@ -384,7 +407,8 @@ void launch_route_attn(hipStream_t, const float* Q, const bf16_t* Kl, const bf16
                        long long Ptot, int chunk);
 // fp32 form (precision mode fp32): the same items, partials and scaling, over
 // fp32 K and V held in head-major planes of Tpad rows x 64 floats (head j of
-// the layer at Kl + j * Tpad * 64), fp32 arithmetic throughout.
+// the layer at Kl + j * Tpad * 64, elements at k32_off / v32_off), fp32
+// operands and accumulation throughout (v_mfma_f32_32x32x2_f32).
 void launch_route_attn32(hipStream_t, const float* Q, const float* Kl, const float* Vl, long long Tpad,
                          const int4* items, int nitems, const int* rec, float* pm, float* pl, float* po,
                          long long Ptot, int chunk);
