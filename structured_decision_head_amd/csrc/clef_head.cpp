@@ -787,7 +787,7 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
 // workspace layout for one plan
 struct WsLayout {
   size_t tab, stats, pooled, ebar, prior, mem, kv, fkv, bigpart, xplanes, mplanes, u, ustats, qbuf, attn, hbuf, qv,
-      qo, gp, f, fstats, fattn, pm, pl, po, part, total;
+      qo, gp, f, fstats, fattn, opart, pm, pl, po, part, total;
 };
 
 // fp32 head: whole-K big GEMMs over the activations' three bf16 terms once the
@@ -845,6 +845,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
   L.f = take(NQ * D * 4);
   L.fstats = take(NQ * 8);
   L.fattn = take(NQ * D * 4);
+  L.opart = take((size_t)NH * ceil_div(NQ, kSgemmRows) * kSgemmRows * D * 4);   // per-head slices of attn W_o^T
   const size_t Pmax = (size_t)std::max(p.Ptot, p.Ptot_f);   // routing and field cross-attention partials
   L.pm = take(NH * Pmax * 4);
   L.pl = take(NH * Pmax * 4);
@@ -1245,6 +1246,7 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
   float* f = reinterpret_cast<float*>(ws + L.f);
   float2* fstats = reinterpret_cast<float2*>(ws + L.fstats);
   float* fattn = reinterpret_cast<float*>(ws + L.fattn);
+  float* opart = reinterpret_cast<float*>(ws + L.opart);
   float* pm = reinterpret_cast<float*>(ws + L.pm);
   float* pl = reinterpret_cast<float*>(ws + L.pl);
   float* po = reinterpret_cast<float*>(ws + L.po);
@@ -1404,8 +1406,10 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
       const Layer& Ly = W.field[l];
       const SgemmShape gq =
           launch_sgemm_partial(st, LdLN{f, D, fstats, Ly.ln1g, Ly.ln1b}, Ly.Wqkv, NQ, 3 * D, D, part, NT);
-      launch_field_attn(st, part, gq.nsplit, (size_t)gq.mtiles * kSgemmRows * 3 * D, Ly.bqkv, rec, p.nact, fattn);
-      launch_sgemm(st, LdRows{fattn, D, nullptr}, EpResid{f, D, Ly.bo}, Ly.Wo, NQ, D, D, part, fstats, eps, NT);
+      const size_t Mq = (size_t)ceil_div(NQ, kSgemmRows) * kSgemmRows;
+      launch_field_attn(st, part, gq.nsplit, (size_t)gq.mtiles * kSgemmRows * 3 * D, Ly.bqkv, rec, p.nact, Ly.Wo,
+                        opart, Mq * D, NT);
+      launch_splitk_reduce(st, opart, NH, Mq, NQ, D, EpResid{f, D, Ly.bo}, fstats, eps);
       if (cross) {
         // cross-attention of the fields over the record's memory rows (the routing attention kernels with
         // the fields as queries), pre-LN, residual

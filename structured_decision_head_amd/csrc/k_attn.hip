@@ -378,19 +378,32 @@ void launch_route_combine(hipStream_t st, const float* pm, const float* pl, cons
                      out);
 }
 
-// Field self-attention: one 256-thread block per (record, head).  Thread t
-// owns query row t / 4 of a 64-row block and 16 of its 64 dims (t % 4); a score
-// is the sum of the four partial dot products (two lane exchanges).  Keys and
-// values are staged in LDS 64 rows at a time with an online softmax, so any
-// number of fields works.  QKV rows are [q | k | v] of width 3 x 1024.
+// Field self-attention with its output projection: one 256-thread block per
+// (record, head).  Thread t owns query row t / 4 of a 64-row block and 16 of
+// its 64 dims (t % 4); a score is the sum of the four partial dot products
+// (two lane exchanges).  Keys and values are staged in LDS 64 rows at a time
+// with an online softmax, so any number of fields works.  QKV rows are
+// [q | k | v] of width 3 x 1024.
+//
+// The head's 64 output dims then meet the matching 64 columns of W_o (the
+// K range [64 j, 64 j + 64) of the [1024][1024] product): the block's rows
+// go to LDS as NT exact-or-near bf16 terms (as in the small GEMMs) and the
+// four waves multiply them with v_mfma_f32_16x16x32_bf16 against W_o's
+// fragment-order blocks, 256 output columns each.  The result is split-K
+// slice j of attn W_o^T, left at P + j * pstride + row * 1024 for the
+// reduction that adds the 16 slices in order with the bias and the residual.
+template <int NT>
 __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QKV, int nsplit, size_t stride,
                                                     const float* __restrict__ bqkv, const int* __restrict__ rec,
-                                                    float* __restrict__ out) {
+                                                    const bf16_t* __restrict__ Wo, float* __restrict__ P,
+                                                    size_t pstride) {
   __shared__ float4 sK[64][16], sV[64][16];
+  __shared__ uint4 sO[NT][64][9];   // [term][row][8-dim chunk], one chunk of padding per row
   const int* R = rec + 8 * blockIdx.x;
   const int q0 = R[6], nq = R[7];
   const int j = blockIdx.y;
   const int t = threadIdx.x, qi_l = t >> 2, part = t & 3;
+  const int w = t >> 6, lane = t & 63;
   for (int qb = 0; qb < nq; qb += 64) {
     const int qi = qb + qi_l;
     const bool valid = qi < nq;
@@ -405,7 +418,8 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
     float m = -INFINITY, l = 0.f;
     for (int kb = 0; kb < nq; kb += 64) {
       const int nk = min(64, nq - kb);
-      if (qb > 0 || kb > 0) __syncthreads();   // the previous block's keys are still being read
+      // the previous block's keys, or the previous query block's output terms, are still being read
+      if (qb > 0 || kb > 0) __syncthreads();
       // 64 rows x 16 float4 each for K and V: 4 float4 per thread
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -440,20 +454,80 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
         }
       }
     }
-    if (valid) {
-      const float inv = 1.0f / l;
-      float* op = out + (size_t)(q0 + qi) * 1024 + j * 64 + part * 16;
+    {
+      // normalised output of this head (rows past the record: zeros) as NT bf16 terms
+      const float inv = valid ? 1.0f / l : 0.f;
+      float x[16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<float4*>(op + 4 * c) = make_float4(o[c].x * inv, o[c].y * inv, o[c].z * inv, o[c].w * inv);
+      for (int c = 0; c < 4; ++c) {
+        x[4 * c] = o[c].x * inv;
+        x[4 * c + 1] = o[c].y * inv;
+        x[4 * c + 2] = o[c].z * inv;
+        x[4 * c + 3] = o[c].w * inv;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 tt[NT];
+        split_terms<NT>(x + 8 * h, tt);
+#pragma unroll
+        for (int e = 0; e < NT; ++e) sO[e][qi_l][2 * part + h] = tt[e];
+      }
+    }
+    __syncthreads();
+    // 16x16x32 fragments: A lane l = row l % 16, dims 8 (l / 16) .. of a 32-dim step;
+    // W_o block (16-column strip n16, K step k32) at (n16 * 32 + k32) * 512, lane l's 8 values at 8 l;
+    // accumulator e of lane l = row 4 (l / 16) + e, column l % 16
+    const int nrb = min(4, (nq - qb + 15) >> 4);
+#pragma unroll 1
+    for (int gq = 0; gq < 4; ++gq) {
+      const int s0 = 16 * w + 4 * gq;   // first 16-column strip of this pass
+      uint4 b[4][2];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          b[cb][kk] = *reinterpret_cast<const uint4*>(Wo + ((size_t)(s0 + cb) * 32 + 2 * j + kk) * 512 + lane * 8);
+#pragma unroll 1
+      for (int rb = 0; rb < nrb; ++rb) {
+        uint4 a[2][NT];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int e = 0; e < NT; ++e) a[kk][e] = sO[e][rb * 16 + (lane & 15)][4 * kk + (lane >> 4)];
+        f32x4 acc[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < NT; ++e)
+              acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[kk][e]), as_bf16x8(b[cb][kk]), acc[cb], 0,
+                                                                0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = qb + rb * 16 + 4 * (lane >> 4) + e;
+          if (row < nq) {
+            float* pr = P + (size_t)j * pstride + (size_t)(q0 + row) * 1024 + (lane & 15);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) pr[(s0 + cb) * 16] = acc[cb][e];
+          }
+        }
+      }
     }
   }
 }
 
 void launch_field_attn(hipStream_t st, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
-                       const int* rec, int nrec, float* out) {
+                       const int* rec, int nrec, const bf16_t* Wo, float* P, size_t pstride, int nt) {
   if (nrec == 0) return;
-  hipLaunchKernelGGL(k_field_attn, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, out);
+  if (nt == 3)
+    hipLaunchKernelGGL(k_field_attn<3>, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo, P,
+                       pstride);
+  else
+    hipLaunchKernelGGL(k_field_attn<2>, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo, P,
+                       pstride);
 }
 
 }  // namespace clef

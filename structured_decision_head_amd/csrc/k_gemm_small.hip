@@ -278,6 +278,17 @@ SgemmShape launch_sgemm_partial(hipStream_t st, const Ld& ld, const bf16_t* W, i
   launch_tile(s, st, ld, EpPart{part, N}, W, M, N, K, part, nt, 0);
   return s;
 }
+template <class Epi>
+void launch_splitk_reduce(hipStream_t st, const float* part, int nsplit, size_t Mp, int M, int N, const Epi& epi,
+                          float2* stats, float eps) {
+  if (M == 0) return;
+  const size_t n4 = (size_t)M * N / 4;
+  hipLaunchKernelGGL((k_splitk_reduce<Epi>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, nsplit, Mp,
+                     M, N, epi, stats, eps);
+}
+template void launch_splitk_reduce<EpResid>(hipStream_t, const float*, int, size_t, int, int, const EpResid&, float2*,
+                                            float);
+
 template SgemmShape launch_sgemm_partial<LdLN>(hipStream_t, const LdLN&, const bf16_t*, int, int, int, float*, int);
 template SgemmShape launch_sgemm_partial<LdZ>(hipStream_t, const LdZ&, const bf16_t*, int, int, int, float*, int);
 

@@ -396,6 +396,13 @@ template <class Ld>
 SgemmShape launch_sgemm_partial(hipStream_t, const Ld&, const bf16_t* W, int M, int N, int K, float* part,
                                 int nt = 2);
 
+// The reduction pass alone, over nsplit slices part + (q * Mp + m) * N + n
+// that another kernel wrote (summed in slice order, then the epilogue; stats
+// as in launch_sgemm, N = 1024).
+template <class Epi>
+void launch_splitk_reduce(hipStream_t, const float* part, int nsplit, size_t Mp, int M, int N, const Epi&,
+                          float2* stats, float eps);
+
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
@@ -414,9 +421,12 @@ void launch_route_attn32(hipStream_t, const float* Q, const float* Kl, const flo
                          long long Ptot, int chunk);
 void launch_route_combine(hipStream_t, const float* pm, const float* pl, const float* po, long long Ptot,
                           const int* opt_rec, const int* rec, int NO, float* out);
-// QKV: split-K slices (nsplit, slice stride in floats, row width 3072) + bias
+// QKV: split-K slices (nsplit, slice stride in floats, row width 3072) + bias.
+// Writes, per head j, split-K slice j of attn W_o^T at P + j * pstride +
+// row * 1024 (rows of every record's fields; Wo in the small GEMMs' fragment
+// order, K = 1024; nt bf16 terms per activation as in launch_sgemm).
 void launch_field_attn(hipStream_t, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
-                       const int* rec, int nrec, float* out);
+                       const int* rec, int nrec, const bf16_t* Wo, float* P, size_t pstride, int nt = 2);
 
 // ---------------------------------------------------------------------------
 // aggregation and scoring
