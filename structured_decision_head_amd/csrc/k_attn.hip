@@ -404,6 +404,17 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
   const int j = blockIdx.y;
   const int t = threadIdx.x, qi_l = t >> 2, part = t & 3;
   const int w = t >> 6, lane = t & 63;
+  // W_o block (16-column strip n16, K step k32) at (n16 * 32 + k32) * 512, lane
+  // l's 8 values at 8 l.  The fragments of the wave's first pass are loaded
+  // before the attention (they depend on the head only), each later pass's
+  // while the previous pass multiplies.
+  const bf16_t* wo = Wo + ((size_t)(16 * w) * 32 + 2 * j) * 512 + lane * 8;
+  uint4 b[4][2], bn[4][2];
+#define FA_LOAD_WO(dst, GQ)                                                                           \
+  _Pragma("unroll") for (int cb = 0; cb < 4; ++cb)                                                    \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                                  \
+      dst[cb][kk] = *reinterpret_cast<const uint4*>(wo + ((size_t)(4 * (GQ) + cb) * 32 + kk) * 512);
+  FA_LOAD_WO(b, 0)
   for (int qb = 0; qb < nq; qb += 64) {
     const int qi = qb + qi_l;
     const bool valid = qi < nq;
@@ -481,12 +492,8 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
 #pragma unroll 1
     for (int gq = 0; gq < 4; ++gq) {
       const int s0 = 16 * w + 4 * gq;   // first 16-column strip of this pass
-      uint4 b[4][2];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          b[cb][kk] = *reinterpret_cast<const uint4*>(Wo + ((size_t)(s0 + cb) * 32 + 2 * j + kk) * 512 + lane * 8);
+      // the next pass's fragments (after the last pass: the first pass's, for the next query block)
+      FA_LOAD_WO(bn, (gq + 1) & 3)
 #pragma unroll 1
       for (int rb = 0; rb < nrb; ++rb) {
         uint4 a[2][NT];
@@ -515,8 +522,13 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
           }
         }
       }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) b[cb][kk] = bn[cb][kk];
     }
   }
+#undef FA_LOAD_WO
 }
 
 void launch_field_attn(hipStream_t st, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
