@@ -162,6 +162,17 @@ def test_smallest_and_largest_hidden_size(torch_gpu, H):
     _check_all(case, _run(case), f"H={H}")
 
 
+def test_records_with_more_than_64_fields(torch_gpu):
+    """Records of 70 fields: the field attention takes each record's fields in
+    two 64-row query blocks, and its W_o share runs once per block."""
+    spec = _spec("many-fields", 7601, B=2, lengths=("fixed", 1600, 1600), fields="counts", counts=(40, 20, 10),
+                 choice_opts=(2, 3), opt_len=(1, 2), instr_len=(2, 4))
+    say("case 2 records of 70 fields")
+    case = synth.make_case(spec)
+    assert int(np.diff(case.batch.q_offsets).min()) == 70
+    _check_all(case, _run(case), "70 fields")
+
+
 def test_question_with_the_most_options(torch_gpu):
     """A question with 1024 options, the most the per-question kernels hold."""
     spec = _spec("max-options", 7501, B=1, lengths=("fixed", 3400, 3400), fields="ordered",

@@ -3,8 +3,8 @@ fp32 arithmetic, as the CoreML packaging of clef-flash runs it on fp16 hidden
 states (CoreML conversion metadata page, decision.head, dtype_of_record).
 
 Tolerance (derived from the arithmetic).  Every product of the mode is exact
-(bf16 weights times activations split into three bf16 terms, or fp32 VALU
-products in attention) and only fp32 accumulation rounds, unit roundoff
+(bf16 weights times activations split into three bf16 terms) or fp32 (the
+attention's products) and only fp32 accumulation rounds, unit roundoff
 u = 2^-24.  A length-K accumulation of O(1) terms then errs by about
 sqrt(K) u relative (K <= 8192: <= 5.4e-6); a logit passes through about 26
 dependent accumulations (option query, 2 routing layers of 4 products, 4
@@ -181,3 +181,16 @@ def test_f32_refuses_streamed_ingest(torch_gpu):
         C.clef_head_stream_begin(r.handle, r.args)
     assert e.value.code == C.CLEF_E_UNSUPPORTED
     r.close()
+
+
+def test_f32_records_with_more_than_64_fields(torch_gpu):
+    """Records of 70 fields in the fp32 mode: two 64-row query blocks per record
+    in the field attention, whose W_o share takes three bf16 terms per value."""
+    spec = f32(synth.CaseSpec(name="many-fields", seed=7602, head=synth.HeadConfig(hidden_size=4096, vocab_size=4096),
+                              B=2, L=None, lengths=("fixed", 1600, 1600), fields="counts", counts=(40, 20, 10),
+                              choice_opts=(2, 3), opt_len=(1, 2), instr_len=(2, 4)))
+    say("case 2 records of 70 fields, fp32 mode")
+    case = synth.make_case(spec)
+    assert int(np.diff(case.batch.q_offsets).min()) == 70
+    _r, out = _run(case)
+    _check(case, out, "70 fields, fp32")
