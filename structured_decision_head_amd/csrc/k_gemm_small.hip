@@ -67,14 +67,20 @@ __global__ __launch_bounds__(256) void k_sgemm(Ld ld, Epi epi, const bf16_t* __r
   // conversion (LayerNorm, hi/lo split) and the MFMAs are independent, so they
   // overlap; one barrier per chunk hands the converted buffer over.
   typename Ld::Raw ra[4];
+  typename Ld::Row rw[4];                // the thread's 4 rows, resolved once
   typename Ld::Cst cq;                   // per-column constants of this thread's 8 columns
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid + 256 * i) >> 4;
+    if (m0 + r < M) rw[i] = ld.row(m0 + r);
+  }
   uint4 bq[2][4];
 #define SG_FETCH_A(K0)                                                                   \
   {                                                                                      \
     cq = ld.cst((K0) + (tid & 15) * 8);                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
       const int v = tid + 256 * i, r = v >> 4, c = v & 15;                               \
-      if (m0 + r < M) ra[i] = ld.fetch(m0 + r, (K0) + c * 8);                            \
+      if (m0 + r < M) ra[i] = ld.fetch(rw[i], (K0) + c * 8);                             \
     }                                                                                    \
   }
 #define SG_FETCH_W(K0)                                                                   \

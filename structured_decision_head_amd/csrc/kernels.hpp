@@ -91,12 +91,14 @@ void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntile
 // ---------------------------------------------------------------------------
 // small GEMMs: C[M, N] = A[M, K] W[N, K]^T, A formed by a loader, C by an epilogue
 // ---------------------------------------------------------------------------
-// A loaders: fetch() issues the global loads of 8 consecutive A elements
-// (row m, columns k..k+7) into a Raw value; cst() issues the loads of any
-// per-column constants of those 8 columns (the same for every row a thread
-// handles); finish() turns them into floats.  Splitting the steps lets the
-// GEMM keep the next chunk's loads in flight while it multiplies the current
-// one, with no load left to wait for in finish().
+// A loaders: row() resolves, once per row before the K loop, whatever a row
+// needs that does not depend on k (its address, gathered index, statistics);
+// fetch() issues the global loads of 8 consecutive A elements (that row,
+// columns k..k+7) into a Raw value; cst() issues the loads of any per-column
+// constants of those 8 columns (the same for every row a thread handles);
+// finish() turns them into floats.  Splitting the steps lets the GEMM keep
+// the next chunk's loads in flight while it multiplies the current one, with
+// no load left to wait for in finish() and no dependent load in fetch().
 DEV void f4x2(float4 a, float4 b, float* x) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -107,8 +109,10 @@ struct LdRows {          // A[m] = src[rows ? rows[m] : m]
   const int* rows;
   struct Raw { float4 a, b; };
   struct Cst {};
-  DEV Raw fetch(int m, int k) const {
-    const float* p = src + (size_t)(rows ? rows[m] : m) * ld + k;
+  struct Row { const float* p; };
+  DEV Row row(int m) const { return Row{src + (size_t)(rows ? rows[m] : m) * ld}; }
+  DEV Raw fetch(const Row& w, int k) const {
+    const float* p = w.p + k;
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
   DEV Cst cst(int) const { return {}; }
@@ -123,9 +127,11 @@ struct LdLN {            // A[m] = LayerNorm(src[m]) with precomputed (mu, rstd)
   const float* b;
   struct Raw { float4 a, c; float2 s; };
   struct Cst { float4 g0, g1, b0, b1; };   // gamma and beta of the 8 columns
-  DEV Raw fetch(int m, int k) const {
-    const float* p = src + (size_t)m * ld + k;
-    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4), stats[m]};
+  struct Row { const float* p; float2 s; };
+  DEV Row row(int m) const { return Row{src + (size_t)m * ld, stats[m]}; }
+  DEV Raw fetch(const Row& w, int k) const {
+    const float* p = w.p + k;
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4), w.s};
   }
   DEV Cst cst(int k) const {
     return Cst{*reinterpret_cast<const float4*>(g + k), *reinterpret_cast<const float4*>(g + k + 4),
@@ -156,12 +162,16 @@ struct LdHid {
   const float* b;
   struct Raw { uint4 v; float2 s; };
   struct Cst { float4 g0, g1, b0, b1; };
-  DEV Raw fetch(int m, int k) const {
+  struct Row { const bf16_t* p; float2 s; };   // p null: a padding row (zeros)
+  DEV Row row(int m) const {
     const int4 t = tiles[m >> 8];
     const int r = m & 255;
+    return Row{r < t.z ? X + (size_t)(t.x + r) * H : nullptr, stats[m]};
+  }
+  DEV Raw fetch(const Row& w, int k) const {
     Raw raw;
-    raw.s = stats[m];
-    raw.v = r < t.z ? *reinterpret_cast<const uint4*>(X + (size_t)(t.x + r) * H + k) : make_uint4(0u, 0u, 0u, 0u);
+    raw.s = w.s;
+    raw.v = w.p ? *reinterpret_cast<const uint4*>(w.p + k) : make_uint4(0u, 0u, 0u, 0u);
     return raw;
   }
   DEV Cst cst(int k) const {
@@ -184,8 +194,10 @@ struct LdSeg2 {          // A[m] = [p0[m] | p1[m]], each H wide
   int H;
   struct Raw { float4 a, b; };
   struct Cst {};
-  DEV Raw fetch(int m, int k) const {
-    const float* p = k < H ? p0 + (size_t)m * H + k : p1 + (size_t)m * H + (k - H);
+  struct Row { size_t off; };
+  DEV Row row(int m) const { return Row{(size_t)m * H}; }
+  DEV Raw fetch(const Row& w, int k) const {
+    const float* p = k < H ? p0 + w.off + k : p1 + w.off + (k - H);
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
   DEV Cst cst(int) const { return {}; }
@@ -198,13 +210,23 @@ struct LdZ {             // A[m] = [f | u | f*u | |f-u|], f = F[fq[m]], u = U[m]
   const int* fq;
   struct Raw { float4 f0, f1, u0, u1; };
   struct Cst {};
+  struct Row { const float* f; const float* u; };
   DEV Cst cst(int) const { return {}; }
-  DEV Raw fetch(int m, int k) const {
-    const int c = k & 1023;
-    const float* fp = F + (size_t)fq[m] * 1024 + c;
-    const float* up = U + (size_t)m * 1024 + c;
-    return Raw{*reinterpret_cast<const float4*>(fp), *reinterpret_cast<const float4*>(fp + 4),
-               *reinterpret_cast<const float4*>(up), *reinterpret_cast<const float4*>(up + 4)};
+  DEV Row row(int m) const { return Row{F + (size_t)fq[m] * 1024, U + (size_t)m * 1024}; }
+  // only the operands of k's segment (the same for a whole 128-deep chunk)
+  DEV Raw fetch(const Row& w, int k) const {
+    const int seg = k >> 10, c = k & 1023;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    Raw r{z, z, z, z};
+    if (seg != 1) {
+      r.f0 = *reinterpret_cast<const float4*>(w.f + c);
+      r.f1 = *reinterpret_cast<const float4*>(w.f + c + 4);
+    }
+    if (seg != 0) {
+      r.u0 = *reinterpret_cast<const float4*>(w.u + c);
+      r.u1 = *reinterpret_cast<const float4*>(w.u + c + 4);
+    }
+    return r;
   }
   DEV void finish(const Raw& r, const Cst&, int, int k, float* x) const {
     const int seg = k >> 10;
