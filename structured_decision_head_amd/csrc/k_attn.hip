@@ -3,17 +3,19 @@
 // Evidence routing (clef-4bit page §三 step 2; Clef-Flash overview §三): all
 // option queries of a record attend, per head, over every valid memory row of
 // that record.  The keys are split into chunks (a multiple of 64 rows, chosen
-// per batch); one wave owns
-// (record, head, chunk), loops over its record's queries 32 at a time and
-// writes flash-decode partials (running max, running sum, unnormalised
-// output) that k_route_combine merges.  Scores and the value mix use
-// v_mfma_f32_32x32x16_bf16 in a transposed form (S^T = K Q^T, O^T = V^T P^T) so
-// that each lane owns one query: the softmax statistics stay lane-local and the
-// probabilities are already in the B-operand layout of the second product.
+// per batch); one wave owns (record, key chunk, block of 32 queries, head) and
+// writes flash-decode partials (running max, running sum, unnormalised output)
+// that k_route_combine merges.  Scores and the value mix run on the matrix
+// cores in a transposed form (S^T = K Q^T, O^T = V^T P^T) so that each lane
+// owns one query: the softmax statistics stay lane-local and the
+// probabilities are already in the B-operand layout of the second product
+// (v_mfma_f32_32x32x16_bf16 in the bf16 kernel, v_mfma_f32_32x32x2_f32 in
+// the fp32 one).
 //
 // Field self-attention (clef-4bit page §三 step 3): every field of a record
 // attends to every field of the same record; tiny (a few dozen fields), so
-// plain fp32 with an online softmax.
+// fp32 vector arithmetic with an online softmax, followed on the matrix cores
+// by the head's share of the output projection.
 #include "kernels.hpp"
 
 namespace clef {
