@@ -432,7 +432,9 @@ struct Weights {
   // of each activation; the K/V product reads Wkv / Wfkv three times instead)
   const float* bmem = nullptr;
   const bf16_t *Wmem_fr = nullptr, *Wkv_fr = nullptr, *Wfkv_fr = nullptr;
-  const bf16_t* Wmem3 = nullptr;
+  const bf16_t* Wmem3 = nullptr;    // [W | W | W] (fp32 head, fp16 hidden rows)
+  const bf16_t* Wmem3f = nullptr;   // three bf16 terms of fp32(W diag(gamma)) (fp32 head, bf16 hidden rows)
+  const float* cmem32 = nullptr;    // row sums of fp32(W diag(gamma))
   std::vector<Layer> route, field;
   float sb, bs2, gate_logit, gate, lam;
 };
@@ -634,6 +636,25 @@ int build_weights(clef_head* h, const clef_head_weight* w, int32_t nw) {
       put_frag(Wm, D, H, &W.Wmem_fr);
       put_rep3(Wm, D, H, &W.Wmem3);
       put_f(bm, &W.bmem);
+      // the folded weight in fp32, as three exact bf16 terms side by side, and its row sums
+      std::vector<uint16_t> Wt((size_t)D * 3 * H);
+      std::vector<float> cm32(D);
+      for (int j = 0; j < D; ++j) {
+        double cs = 0;
+        for (int k = 0; k < H; ++k) {
+          const float wv = bf16_to_f(Wm[(size_t)j * H + k]) * g[k];
+          cs += wv;
+          float r = wv;
+          for (int t = 0; t < 3; ++t) {
+            const uint16_t b = f_to_bf16(r);
+            Wt[((size_t)j * 3 + t) * H + k] = b;
+            r -= bf16_to_f(b);
+          }
+        }
+        cm32[j] = (float)cs;
+      }
+      put_bf(Wt.data(), Wt.size(), &W.Wmem3f);
+      put_f(cm32, &W.cmem32);
     }
     put_bf(Wp16.data(), Wp16.size(), &W.Wmem16);
     put_f(cm16, &W.cmem16);
@@ -824,7 +845,7 @@ WsLayout ws_layout(const clef_head_config& c, const Plan& p) {
     }
     L.bigpart = take(fl * 4);
     if (f32_big_gemms(p.ntiles)) {
-      L.xplanes = take(Tp * 3 * H * 2);   // LayerNorm-ed rows, three bf16 terms
+      if (p.f16) L.xplanes = take(Tp * 3 * H * 2);   // LayerNorm-ed fp16 rows, three bf16 terms
       L.mplanes = take(Tp * 3 * D * 2);   // memory rows, three bf16 terms
     }
   } else {
@@ -1309,12 +1330,19 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         if (g.recorded) HIPCHK(hipStreamWaitEvent(st, g.gemm_done, 0));
       }
       if (f32 && f32_big_gemms(p.ntiles)) {
-        // normalised rows as three bf16 terms times [W | W | W], then their three-term memory rows times Wkv
-        // read three times, into head-major fp32 planes
+        // memory rows: bf16 hidden rows (exact) read three times against the three bf16 terms of the folded
+        // weight, LayerNorm in the epilogue; fp16 hidden rows normalised into three bf16 terms times
+        // [W | W | W].  Then their three-term memory rows times Wkv read three times, into head-major fp32
+        // planes
         bf16_t* xplanes = reinterpret_cast<bf16_t*>(ws + L.xplanes);
         bf16_t* mplanes = reinterpret_cast<bf16_t*>(ws + L.mplanes);
-        launch_ln_split3(st, X, (int)H, p.f16, tiles, p.ntiles, stats, W.lnin_g, W.lnin_b, xplanes);
-        launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mem32, mplanes);
+        if (p.f16) {
+          launch_ln_split3(st, X, (int)H, p.f16, tiles, p.ntiles, stats, W.lnin_g, W.lnin_b, xplanes);
+          launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mem32, mplanes);
+        } else {
+          launch_gemm_mem32_folded(st, X, (int)H, tiles, p.ntiles, W.Wmem3f, stats, W.cmem32, W.dmem, mem32,
+                                   mplanes);
+        }
         MARK(CLEF_STAGE_MEMORY_GEMM);
         if (NR > 0) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wkv, W.bkv, NR, kv32, p.Tpad);
         if (cross) launch_gemm_kv32(st, mplanes, kvtiles, p.ntiles, W.Wfkv, W.bfkv, NL, fkv32, p.Tpad);

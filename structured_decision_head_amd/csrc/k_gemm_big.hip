@@ -52,6 +52,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   static constexpr int kWrapW = 0;
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
   static constexpr int kImageBytes = 256 * kLd * 2;
+  DEV int a_wrap() const { return 0; }
   DEV bool transposed(int) const { return true; }
   // constants: [0, 256) c and [256, 512) d of the tile's columns, then (mean, rstd) of its rows
   DEV void load_consts(int orow0, int ocol0, int tid, float (&r)[4]) const {
@@ -124,6 +125,7 @@ struct EpiKV {
   static constexpr bool kPlain = true;                 // V tiles are plain
   static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
+  DEV int a_wrap() const { return 0; }
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV bf16_t* head_base(int col) const {
     const int r = col >> 11, isv = (col >> 10) & 1, h = (col >> 6) & 15;
@@ -201,47 +203,74 @@ struct EpiKV {
 };
 
 // fp32 head.  Its products run on this kernel as bf16 GEMMs of three times
-// the depth: the A rows hold the three exact bf16 terms of each fp32 value
-// side by side ([t0 | t1 | t2], each K0 wide) and every term meets the same
-// weight row (stored repeated, [W | W | W], for the memory product; read
-// three times through the K-position wrap for the K/V product, whose 2 MB
-// column group then stays in L2), so every product is exact and the MFMAs'
-// fp32 accumulation is the only rounding.  All tiles are transposed:
-// accumulator (mi, ni, e) of lane l is column ra0 + 32 mi + 8 (e / 4) +
-// 4 (l / 32) + e % 4 of row rb0 + 32 ni + l % 32, four consecutive columns
-// per (mi, ni, e / 4), stored straight from the accumulators.
+// the depth in which every product is exact, so the MFMAs' fp32 accumulation
+// is the only rounding: either the A rows hold the three exact bf16 terms of
+// each fp32 value side by side ([t0 | t1 | t2], each K0 wide) and every term
+// meets the same weight row (stored repeated, [W | W | W], for the memory
+// product over fp16 hidden rows; read three times through the K-position
+// wrap for the K/V product, whose 2 MB column group then stays in L2), or the
+// A row is exact in bf16 already (bf16 hidden rows) and is read three times
+// through its own K-position wrap against the weight's three terms.  All
+// tiles are transposed: accumulator (mi, ni, e) of lane l is column ra0 +
+// 32 mi + 8 (e / 4) + 4 (l / 32) + e % 4 of row rb0 + 32 ni + l % 32, four
+// consecutive columns per (mi, ni, e / 4), stored straight from the
+// accumulators.
 //
-// Memory rows: m = acc + b, written as fp32 rows [rows][1024] and as the
-// three bf16 terms of each value in [rows][3 x 1024] (the A operand of the
-// K/V product).
+// Memory rows, written as fp32 rows [rows][1024] and as the three bf16 terms
+// of each value in [rows][3 x 1024] (the A operand of the K/V product):
+//  * over LayerNorm-ed rows' terms against [W | W | W]: m = acc + b (c, stats
+//    null; d = b);
+//  * over the raw bf16 hidden rows, read three times (A's K position wraps at
+//    awrap = H), against the three bf16 terms of fp32(W diag(gamma)): the
+//    LayerNorm folded as in the bf16 mode, m = rstd (acc - mu c) + d, with
+//    c_j the sum of the fp32 weights of row j and d = W beta + b.  The hidden
+//    values are exact in bf16, so every product is exact here too.
+// Both take the same arithmetic form: with c = 0 and (mu, rstd) = (0, 1)
+// it gives acc + d exactly.
 struct EpiMem32 {
-  const float* bias;
+  const float2* stats;   // (mean, rstd) per packed row, or null
+  const float* c;        // or null
+  const float* d;
   float* mem;            // [rows][1024] fp32
   bf16_t* planes;        // [rows][3 * 1024] bf16
+  int awrap;             // A's K-position wrap (0: none)
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
   static constexpr bool kPlain = false;
-  static constexpr int kWrapW = 0;       // the weight stored repeated, [W | W | W]
+  static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
+  DEV int a_wrap() const { return awrap; }
   DEV bool transposed(int) const { return true; }
-  DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
-  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
+  // constants: [0, 256) d and [256, 512) c of the tile's columns, then (mean, rstd) of its rows
+  DEV void load_consts(int orow0, int ocol0, int tid, float (&r)[4]) const {
+    const float2 st = stats ? stats[orow0 + tid] : make_float2(0.f, 1.f);
+    r[0] = d[ocol0 + tid]; r[1] = c ? c[ocol0 + tid] : 0.f; r[2] = st.x; r[3] = st.y;
+  }
+  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const {
+    cst[tid] = r[0]; cst[256 + tid] = r[1]; cst[512 + 2 * tid] = r[2]; cst[513 + 2 * tid] = r[3];
+  }
   template <bool TR>
   DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
                       int lane) const {
     const int h4 = 4 * (lane >> 5);
+    float2 st[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) st[ni] = *reinterpret_cast<const float2*>(cst + 512 + 2 * (rb0 + ni * 32 + (lane & 31)));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int lc = ra0 + mi * 32 + 8 * g + h4;
-        const float4 b = *reinterpret_cast<const float4*>(cst + lc);
+        const float4 dd = *reinterpret_cast<const float4*>(cst + lc);
+        const float4 cc = *reinterpret_cast<const float4*>(cst + 256 + lc);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const f32x16& a = acc[mi][ni];
+          const float mu = st[ni].x, rs = st[ni].y;
           const size_t row = (size_t)(orow0 + rb0 + ni * 32 + (lane & 31));
-          const float v[4] = {a[4 * g] + b.x, a[4 * g + 1] + b.y, a[4 * g + 2] + b.z, a[4 * g + 3] + b.w};
+          const float v[4] = {rs * (a[4 * g] - mu * cc.x) + dd.x, rs * (a[4 * g + 1] - mu * cc.y) + dd.y,
+                              rs * (a[4 * g + 2] - mu * cc.z) + dd.z, rs * (a[4 * g + 3] - mu * cc.w) + dd.w};
           *reinterpret_cast<float4*>(mem + row * 1024 + ocol0 + lc) = make_float4(v[0], v[1], v[2], v[3]);
           float r[4] = {v[0], v[1], v[2], v[3]}, h[4];
 #pragma unroll
@@ -281,6 +310,7 @@ struct EpiKV32 {
   static constexpr bool kPlain = true;   // V tiles are plain
   static constexpr int kWrapW = 1024;    // one [N][1024] weight read three times: its 2 MB column group stays in L2
   static constexpr int kImageBytes = 0;
+  DEV int a_wrap() const { return 0; }
   DEV bool transposed(int tn) const { return !(((tn * BN) >> 10) & 1); }
   DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
   DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
@@ -339,6 +369,7 @@ struct EpiPart {
   static constexpr bool kPlain = false;
   static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
+  DEV int a_wrap() const { return 0; }
   DEV bool transposed(int) const { return true; }
   DEV void load_consts(int, int, int, float (&)[4]) const {}
   DEV void put_consts(float*, int, const float (&)[4]) const {}
@@ -455,6 +486,10 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   const uint32_t woffE = (uint32_t)(crow * ldw + cch * 8) * 2, woffO = (uint32_t)(crow * ldw + (cch ^ 4) * 8) * 2;
   const uint32_t astep = (uint32_t)(8 * lda) * 2, wstep = (uint32_t)(8 * ldw) * 2;
 #define WCOL(k) (kWrap ? ((k) & (kWrap - 1)) : (k))
+  // A rows are K long, or awrap long when the product's depth repeats them
+  // (K = 3 awrap; K position k reads A column k mod awrap)
+  const int awrap = epi.a_wrap();
+#define ACOL(k) (awrap ? ((k) >= 2 * awrap ? (k) - 2 * awrap : (k) >= awrap ? (k) - awrap : (k)) : (k))
   // fragment positions: 32x32x16 operands, lane -> row (lane & 31), chunk 2 kk + (lane >> 5).
   // Block bases are multiples of 32 rows, so the swizzle depends on the lane only
   // and block i of a substep sits 256 chunks after block 0.
@@ -464,7 +499,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
 #define COPY_A(stage, k0)                                                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? aoffO : aoffE) + i * astep, (kbase + (k0)) * 2, 0, 0);
+                                             ((i & 1) ? aoffO : aoffE) + i * astep, ACOL(kbase + (k0)) * 2, 0, 0);
 #define COPY_B(stage, k0)                                                                                      \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + i)], 16,            \
@@ -525,7 +560,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   }
 #define CPA1(stage, k0, i)                                                                      \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + (i))], 16, \
-                                           (((i) & 1) ? aoffO : aoffE) + (i) * astep, (kbase + (k0)) * 2, 0, 0);
+                                           (((i) & 1) ? aoffO : aoffE) + (i) * astep, ACOL(kbase + (k0)) * 2, 0, 0);
 #define CPB1(stage, k0, i)                                                                      \
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + (i))], 16, \
                                            (((i) & 1) ? woffO : woffE) + (i) * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
@@ -609,6 +644,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
     __builtin_amdgcn_sched_barrier(0);
   }
 #undef WCOL
+#undef ACOL
 #undef MFMA2
 #undef FRAG1
 #undef CPA1
@@ -783,7 +819,15 @@ void launch_gemm_mem32(hipStream_t st, const bf16_t* xplanes, int H, const int4*
                        const bf16_t* Wm3, const float* bias, float* mem, bf16_t* mplanes) {
   if (ntiles == 0) return;
   hipLaunchKernelGGL(k_gemm256<EpiMem32>, dim3(ntiles * (1024 / BN)), dim3(256), 0, st, xplanes, 3 * H, tiles,
-                     1024 / BN, Wm3, 3 * H, 1, EpiMem32{bias, mem, mplanes});
+                     1024 / BN, Wm3, 3 * H, 1, EpiMem32{nullptr, nullptr, bias, mem, mplanes, 0});
+}
+
+void launch_gemm_mem32_folded(hipStream_t st, const bf16_t* hidden, int H, const int4* tiles, int ntiles,
+                              const bf16_t* Wt3, const float2* stats, const float* c, const float* d, float* mem,
+                              bf16_t* mplanes) {
+  if (ntiles == 0) return;
+  hipLaunchKernelGGL(k_gemm256<EpiMem32>, dim3(ntiles * (1024 / BN)), dim3(256), 0, st, hidden, H, tiles,
+                     1024 / BN, Wt3, 3 * H, 1, EpiMem32{stats, c, d, mem, mplanes, H});
 }
 
 void launch_gemm_kv32(hipStream_t st, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv,

@@ -84,6 +84,14 @@ void launch_gemm_mem32(hipStream_t, const bf16_t* xplanes, int H, const int4* ti
                        const float* bias, float* mem, bf16_t* mplanes);
 void launch_gemm_kv32(hipStream_t, const bf16_t* mplanes, const int4* tiles, int ntiles, const bf16_t* Wkv,
                       const float* bias, int n_layers, float* kv, long long Tpad);
+// fp32 head over bf16 hidden rows (exact in bf16): the raw rows (tiles as in
+// launch_gemm_mem) read three times against Wt3 = the three bf16 terms of
+// fp32(W diag(gamma)) ([1024][3 H]), LayerNorm folded in the epilogue
+// (m = rstd (acc - mu c) + d, c_j the sum of row j's fp32 weights); writes mem
+// and mplanes as launch_gemm_mem32 does.
+void launch_gemm_mem32_folded(hipStream_t, const bf16_t* hidden, int H, const int4* tiles, int ntiles,
+                              const bf16_t* Wt3, const float2* stats, const float* c, const float* d, float* mem,
+                              bf16_t* mplanes);
 void launch_gemm_kv(hipStream_t, const bf16_t* mem, const int4* tiles, int ntiles, const bf16_t* Wkv,
                     const float* bkv, int n_layers, bf16_t* kv, long long Tpad, float* part, int split = 0,
                     long long row0 = 0);
