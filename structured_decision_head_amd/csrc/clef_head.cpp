@@ -1336,11 +1336,12 @@ static int forward_impl(clef_head* h, const clef_head_batch* batch, float* logit
         // planes
         bf16_t* xplanes = reinterpret_cast<bf16_t*>(ws + L.xplanes);
         bf16_t* mplanes = reinterpret_cast<bf16_t*>(ws + L.mplanes);
+        float* mrows = h->trace ? mem32 : nullptr;   // the fp32 rows are read by the memory trace only
         if (p.f16) {
           launch_ln_split3(st, X, (int)H, p.f16, tiles, p.ntiles, stats, W.lnin_g, W.lnin_b, xplanes);
-          launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mem32, mplanes);
+          launch_gemm_mem32(st, xplanes, (int)H, kvtiles, p.ntiles, W.Wmem3, W.bmem, mrows, mplanes);
         } else {
-          launch_gemm_mem32_folded(st, X, (int)H, tiles, p.ntiles, W.Wmem3f, stats, W.cmem32, W.dmem, mem32,
+          launch_gemm_mem32_folded(st, X, (int)H, tiles, p.ntiles, W.Wmem3f, stats, W.cmem32, W.dmem, mrows,
                                    mplanes);
         }
         MARK(CLEF_STAGE_MEMORY_GEMM);

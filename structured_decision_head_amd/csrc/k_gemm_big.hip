@@ -231,7 +231,7 @@ struct EpiMem32 {
   const float2* stats;   // (mean, rstd) per packed row, or null
   const float* c;        // or null
   const float* d;
-  float* mem;            // [rows][1024] fp32
+  float* mem;            // [rows][1024] fp32, or null (only the terms are needed)
   bf16_t* planes;        // [rows][3 * 1024] bf16
   int awrap;             // A's K-position wrap (0: none)
   static constexpr bool kF16 = false;
@@ -271,7 +271,7 @@ struct EpiMem32 {
           const size_t row = (size_t)(orow0 + rb0 + ni * 32 + (lane & 31));
           const float v[4] = {rs * (a[4 * g] - mu * cc.x) + dd.x, rs * (a[4 * g + 1] - mu * cc.y) + dd.y,
                               rs * (a[4 * g + 2] - mu * cc.z) + dd.z, rs * (a[4 * g + 3] - mu * cc.w) + dd.w};
-          *reinterpret_cast<float4*>(mem + row * 1024 + ocol0 + lc) = make_float4(v[0], v[1], v[2], v[3]);
+          if (mem) *reinterpret_cast<float4*>(mem + row * 1024 + ocol0 + lc) = make_float4(v[0], v[1], v[2], v[3]);
           float r[4] = {v[0], v[1], v[2], v[3]}, h[4];
 #pragma unroll
           for (int p = 0; p < 3; ++p) {

@@ -76,7 +76,8 @@ void launch_gemm_mem(hipStream_t, const bf16_t* hidden, int H, bool f16, const i
 // fp32 head: the memory product over the LayerNorm-ed rows' three bf16 terms
 // (xplanes [rows][3 H], rows in the packed row space, tiles with first A row =
 // first packed row) against Wm3 = [W | W | W] ([1024][3 H]); writes fp32 rows
-// mem [rows][1024] and their three bf16 terms mplanes [rows][3 x 1024].  The
+// mem [rows][1024] (skipped when mem is null) and their three bf16 terms
+// mplanes [rows][3 x 1024].  The
 // K/V product over mplanes against the stacked Wkv ([N][1024], read once per
 // term) writes fp32 head-major planes ([layer][K|V][head][Tpad][64], 32-row
 // blocks in k32_off / v32_off order).  Whole-K launches.
