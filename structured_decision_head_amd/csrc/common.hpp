@@ -9,6 +9,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));                // MFM
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));           // 16-byte register vector
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -24,6 +25,7 @@ DEV uint32_t pack_bf16x2(float a, float b) {
 // 16-byte store with the non-temporal hint (16-byte aligned): the line is
 // written through rather than kept dirty in L2 and the memory-side cache.
 DEV void store_stream(void* p, const u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
+DEV void store_stream(void* p, const u32x2 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p)); }
 
 // Unpack 8 bf16 held in a uint4 into floats.
 DEV void unpack8(const uint4 v, float* f) {

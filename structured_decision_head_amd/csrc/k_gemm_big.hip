@@ -300,6 +300,9 @@ struct EpiMem32 {
 //  * V: accumulator (mi, ni, 4 g' + c) of lane l is key ra0 + 32 mi + 8 g' +
 //    4 (l / 32) + c of dim rb0 + 32 ni + l % 32: one 16-byte slot per lane,
 //    64 (4 (d / 32) + g') + l in the block (1 KB a store).
+// Stores carry the non-temporal hint, as in the bf16 K/V epilogue (K and V
+// are read once per routing layer; left dirty in the caches they cost the
+// next kernels' reads a write-back).
 struct EpiKV32 {
   const float* bias;
   float* kv;
@@ -330,8 +333,8 @@ struct EpiKV32 {
           for (int ni = 0; ni < 4; ++ni) {
             const f32x16& a = acc[mi][ni];
             float* blk = base + (size_t)((orow0 + rb0 + ni * 32) >> 5) * 2048;
-            *reinterpret_cast<float2*>(blk) = make_float2(a[4 * g] + b.x, a[4 * g + 2] + b.z);
-            *reinterpret_cast<float2*>(blk + 128) = make_float2(a[4 * g + 1] + b.y, a[4 * g + 3] + b.w);
+            store_stream(blk, u32x2{__float_as_uint(a[4 * g] + b.x), __float_as_uint(a[4 * g + 2] + b.z)});
+            store_stream(blk + 128, u32x2{__float_as_uint(a[4 * g + 1] + b.y), __float_as_uint(a[4 * g + 3] + b.w)});
           }
         }
     } else {
@@ -346,8 +349,8 @@ struct EpiKV32 {
           float* blk = base + (size_t)((orow0 + ra0 + mi * 32) >> 5) * 2048;
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(blk + g * 256) =
-                make_float4(a[4 * g] + b, a[4 * g + 1] + b, a[4 * g + 2] + b, a[4 * g + 3] + b);
+            store_stream(blk + g * 256, u32x4{__float_as_uint(a[4 * g] + b), __float_as_uint(a[4 * g + 1] + b),
+                                              __float_as_uint(a[4 * g + 2] + b), __float_as_uint(a[4 * g + 3] + b)});
         }
       }
     }
