@@ -175,8 +175,9 @@ def test_allocation_failure_gives_nomem(torch_gpu):
 def _offset_outlier_case(precision):
     """Hidden rows x = offset_row + scale_row * z with offsets up to +-8, scales
     0.5..4 and four channels carrying values near +-200 (bf16-rounded).  25 row
-    tiles, so that the memory projection runs whole-K (the folded LayerNorm in
-    its epilogue; in the fp32 mode the three-term rows)."""
+    tiles, so that the memory projection runs whole-K with the LayerNorm folded
+    into its epilogue (in the fp32 mode over the raw bf16 rows against the
+    three-term fp32 weight), where the offsets cancel."""
     spec = synth.config_spec(1, B=5, L=1100, lengths=("uniform", 1030, 1100), seed=4242,
                              head=synth.HeadConfig(vocab_size=4096, precision=precision))
     case = synth.make_case(spec)
