@@ -149,18 +149,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int e = 0; e < 16; ++e) o[0][e] = o[1][e] = 0.f;
 
     // three 32-key steps per iteration so that the triple buffer has static
-    // registers: two steps' K and V are in flight while one is multiplied
+    // registers: two steps' K and V are in flight while one is multiplied.
+    // The loads are unconditional, their block clamped to the chunk's last
+    // one (a step past the end re-reads it, from cache): a load under a
+    // branch would make the compiler's wait before each step conservative,
+    // waiting for the loads just issued instead of those two steps old.
+    const int klast = kv0 + ((k_hi - 1) & ~31);
     KV32 a, b, c3;
     kv_load(a, Kj, Vj, kv0 + k_lo, lane);
-    if (k_lo + 32 < k_hi) kv_load(b, Kj, Vj, kv0 + k_lo + 32, lane);
+    kv_load(b, Kj, Vj, min(kv0 + k_lo + 32, klast), lane);
     for (int kb = k_lo; kb < k_hi; kb += 96) {
-      if (kb + 64 < k_hi) kv_load(c3, Kj, Vj, kv0 + kb + 64, lane);
+      kv_load(c3, Kj, Vj, min(kv0 + kb + 64, klast), lane);
       kv_step(a, qf, kb, n, g, m, l, o);
       if (kb + 32 >= k_hi) break;
-      if (kb + 96 < k_hi) kv_load(a, Kj, Vj, kv0 + kb + 96, lane);
+      kv_load(a, Kj, Vj, min(kv0 + kb + 96, klast), lane);
       kv_step(b, qf, kb + 32, n, g, m, l, o);
       if (kb + 64 >= k_hi) break;
-      if (kb + 128 < k_hi) kv_load(b, Kj, Vj, kv0 + kb + 128, lane);
+      kv_load(b, Kj, Vj, min(kv0 + kb + 128, klast), lane);
       kv_step(c3, qf, kb + 64, n, g, m, l, o);
     }
     if (qvalid) {
