@@ -194,3 +194,16 @@ def test_f32_records_with_more_than_64_fields(torch_gpu):
     assert int(np.diff(case.batch.q_offsets).min()) == 70
     _r, out = _run(case)
     _check(case, out, "70 fields, fp32")
+
+
+@pytest.mark.parametrize("H", [512, 8192])
+def test_f32_smallest_and_largest_hidden_size_big_gemm_path(torch_gpu, H):
+    """hidden_size 512 and 8192 in the fp32 mode with 25 row tiles, so that the
+    memory product runs whole-K over the raw bf16 rows read three times
+    (depth 3 x 512 and 3 x 8192, the row read wrapping at H)."""
+    spec = synth.config_spec(1, B=5, L=1100, lengths=("uniform", 1030, 1100), seed=4300 + H // 512,
+                             head=synth.HeadConfig(hidden_size=H, vocab_size=4096, precision=1))
+    say(f"case fp32 mode, hidden size {H}, 25 row tiles")
+    case = synth.make_case(spec)
+    _r, out = _run(case)
+    _check(case, out, f"fp32 H={H}")
