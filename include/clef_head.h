@@ -112,13 +112,16 @@ typedef struct {
  *   page §三: its weights are bf16 and never quantised).
  * CLEF_PRECISION_F32: fp32 arithmetic throughout, as the CoreML packaging
  *   runs the head on fp16 hidden states (CoreML conversion metadata page,
- *   decision.head, dtype_of_record): memory rows and K/V in fp32 with the
- *   input LayerNorm applied to the rows (not folded into the weights), fp32
- *   attention, and every fp32 activation entering a product as three bf16
- *   terms whose sum is exact, against the exact bf16 weights, so that only
- *   the fp32 accumulation rounds.  Works with bf16 or fp16 (CLEF_HIDDEN_F16)
- *   hidden rows; streamed ingest (clef_head_stream_*) is CLEF_E_UNSUPPORTED
- *   in this mode. */
+ *   decision.head, dtype_of_record): memory rows and K/V in fp32, fp32
+ *   attention, and every fp32 value entering a product as three bf16 terms
+ *   whose sum is exact, so that each product is exact and only the fp32
+ *   accumulation rounds.  The input LayerNorm is applied to fp16 hidden rows
+ *   before their product; over bf16 hidden rows (exact as they are) it is
+ *   folded into the product's epilogue against the fp32 weight W diag(gamma)
+ *   held as three bf16 terms, whose cancellation of the row mean adds about
+ *   u |mean| / std relative error (u = 2^-24).  Works with bf16 or fp16
+ *   (CLEF_HIDDEN_F16) hidden rows; streamed ingest (clef_head_stream_*) is
+ *   CLEF_E_UNSUPPORTED in this mode. */
 #define CLEF_PRECISION_BF16 0
 #define CLEF_PRECISION_F32  1
 
