@@ -302,17 +302,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // buffers have static registers); V has one buffer, refilled for the next
   // step as soon as the current step's value products have been issued, and
   // needed only after that step's scores and softmax
+  // (loads unconditional, their block clamped to the chunk's last one, as in
+  // the bf16 kernel, so that each wait covers only the loads it needs)
+  const int klast = kv0 + ((k_hi - 1) & ~31);
   f32x4 ka[8], kb2[8], v[8];
   frag_load32(ka, Kj, kv0 + k_lo, lane);
   frag_load32(v, Vj, kv0 + k_lo, lane);
   for (int kb = k_lo; kb < k_hi; kb += 64) {
-    if (kb + 32 < k_hi) frag_load32(kb2, Kj, kv0 + kb + 32, lane);
+    frag_load32(kb2, Kj, min(kv0 + kb + 32, klast), lane);
     kv_step32(ka, v, q, kb, n, g, m, l, o);
     if (kb + 32 >= k_hi) break;
     frag_load32(v, Vj, kv0 + kb + 32, lane);
-    if (kb + 64 < k_hi) frag_load32(ka, Kj, kv0 + kb + 64, lane);
+    frag_load32(ka, Kj, min(kv0 + kb + 64, klast), lane);
     kv_step32(kb2, v, q, kb + 32, n, g, m, l, o);
-    if (kb + 64 < k_hi) frag_load32(v, Vj, kv0 + kb + 64, lane);
+    frag_load32(v, Vj, min(kv0 + kb + 64, klast), lane);
   }
   if (qvalid) {
     const size_t slot = (size_t)j * Ptot + pbase + (size_t)qi * nc + c;
