@@ -427,9 +427,10 @@ struct Weights {
   const bf16_t* Wfkv = nullptr;   // decoder-layer field variant: cross K/V of every field layer, stacked
   const float* bfkv = nullptr;
   // precision mode fp32: the memory projection unfolded (LayerNorm applied to the rows) with its own bias,
-  // and the stacked K/V projections, in the small GEMMs' fragment order (batches of few row tiles); the
-  // memory weight also as rows repeated three times, [W | W | W] (the big GEMM over the three bf16 terms
-  // of each activation; the K/V product reads Wkv / Wfkv three times instead)
+  // and the stacked K/V projections, in the small GEMMs' fragment order (batches of few row tiles); for the
+  // big GEMMs the memory weight also as rows repeated three times, [W | W | W] (against the three bf16
+  // terms of each normalised fp16 row), and folded, as the three bf16 terms of fp32(W diag(gamma)) with
+  // its row sums (against bf16 rows read three times); the K/V product reads Wkv / Wfkv three times
   const float* bmem = nullptr;
   const bf16_t *Wmem_fr = nullptr, *Wkv_fr = nullptr, *Wfkv_fr = nullptr;
   const bf16_t* Wmem3 = nullptr;    // [W | W | W] (fp32 head, fp16 hidden rows)
