@@ -58,6 +58,36 @@ def test_noalloc_two_calls_match_forward(torch_gpu):
     r2.close()
 
 
+def test_noalloc_fp32_mode_two_calls_match_forward(torch_gpu):
+    """The same in the fp32 precision mode: a batch of 25 row tiles (whole-K
+    memory and K/V products, the fp32 K/V planes in the static scratch), then
+    the single record (split-K products)."""
+    import dataclasses
+    from structured_decision_head_amd.runner import HeadRunner
+    tol = {"tol_logit": 1e-4, "tol_prob": 5e-5}
+    head = synth.HeadConfig(vocab_size=4096, precision=1)
+    big = synth.make_case(synth.config_spec(1, B=5, L=1100, lengths=("uniform", 1030, 1100), head=head))
+    say(f"case noalloc fp32 call 1: B={big.batch.B} T={int(big.batch.lengths.sum())} NO={big.batch.NO}")
+    r = HeadRunner(big)
+    r.set_batch()
+    ref, got = _both(torch_gpu, big, r)
+    for a, b in zip(ref, got):
+        assert np.array_equal(a, b)
+    compare("noalloc fp32 call 1", got, oracle_outputs(big), big.batch.o_offsets, **tol)
+    r.close()
+
+    spec0 = synth.config_spec(0)
+    small = synth.make_case(dataclasses.replace(spec0, head=dataclasses.replace(spec0.head, precision=1)))
+    say(f"case noalloc fp32 call 2 (smaller): B=1 T={int(small.batch.lengths.sum())} NO={small.batch.NO}")
+    r2 = HeadRunner(small)
+    r2.set_batch()
+    ref2, got2 = _both(torch_gpu, small, r2)
+    for a, b in zip(ref2, got2):
+        assert np.array_equal(a, b)
+    compare("noalloc fp32 call 2", got2, oracle_outputs(small), small.batch.o_offsets, **tol)
+    r2.close()
+
+
 def test_noalloc_refuses_a_batch_beyond_the_scratch(torch_gpu):
     from structured_decision_head_amd import clefhead as C
     from structured_decision_head_amd.runner import HeadRunner
