@@ -2,9 +2,10 @@
 // width -> 1024) and the routing layers' K/V projections (1024 -> 2 x 1024 per
 // layer).  These are the FLOP-dominant contractions of the head at long L.
 //
-// Operation (CoreML conversion metadata of clef-flash, "decision.head":
-// LayerNorm(hidden) -> memory; clef-4bit page §三 step 2: every option attends
-// over that memory).  LayerNorm is folded into the memory GEMM: with
+// Operation (CoreML conversion metadata page of clef-flash, decision.head: the
+// memory is a projection of the LayerNorm-ed hidden rows; clef-4bit page §三
+// step 2: every option attends over that memory).  LayerNorm is folded into
+// the memory GEMM: with
 // W' = W * diag(gamma), c_j = sum_k W'_jk and d_j = sum_k W_jk beta_k + b_j,
 //     m_tj = rstd_t * ((W' x_t)_j - mu_t * c_j) + d_j,
 // so the GEMM reads the raw bf16 hidden rows and the statistics enter only in
@@ -13,7 +14,9 @@
 // Tile: 256 x 256 outputs per workgroup, 4 waves in a 2 x 2 grid each owning
 // 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16 blocks, accumulators in AGPRs).
 // With fp16 hidden rows the memory GEMM multiplies fp16 operands (an fp16 copy
-// of W') with v_mfma_f32_32x32x16_f16 instead.
+// of W') with v_mfma_f32_32x32x16_f16 instead.  The fp32 head runs its
+// memory and K/V products on the same tile as bf16 GEMMs of three times the
+// depth with exact products (EpiMem32, EpiKV32 below).
 #include "kernels.hpp"
 
 namespace clef {
