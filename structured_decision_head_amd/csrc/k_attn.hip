@@ -402,6 +402,9 @@ void launch_route_combine(hipStream_t st, const float* pm, const float* pl, cons
 // fragment-order blocks, 256 output columns each.  The result is split-K
 // slice j of attn W_o^T, left at P + j * pstride + row * 1024 for the
 // reduction that adds the 16 slices in order with the bias and the residual.
+// With gridDim.z = cs > 1 (a small batch, fewer blocks than compute units)
+// each block repeats the small attention and keeps only the output columns of
+// part blockIdx.z, 1024 / cs of them, in 4 / cs passes instead of 4.
 template <int NT>
 __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QKV, int nsplit, size_t stride,
                                                     const float* __restrict__ bqkv, const int* __restrict__ rec,
@@ -418,7 +421,9 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
   // l's 8 values at 8 l.  The fragments of the wave's first pass are loaded
   // before the attention (they depend on the head only), each later pass's
   // while the previous pass multiplies.
-  const bf16_t* wo = Wo + ((size_t)(16 * w) * 32 + 2 * j) * 512 + lane * 8;
+  const int npass = 4 / gridDim.z;
+  const int sw = (int)blockIdx.z * 16 * npass + 4 * npass * w;   // the wave's first 16-column strip
+  const bf16_t* wo = Wo + ((size_t)sw * 32 + 2 * j) * 512 + lane * 8;
   uint4 b[4][2], bn[4][2];
 #define FA_LOAD_WO(dst, GQ)                                                                           \
   _Pragma("unroll") for (int cb = 0; cb < 4; ++cb)                                                    \
@@ -500,10 +505,12 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
     // accumulator e of lane l = row 4 (l / 16) + e, column l % 16
     const int nrb = min(4, (nq - qb + 15) >> 4);
 #pragma unroll 1
-    for (int gq = 0; gq < 4; ++gq) {
-      const int s0 = 16 * w + 4 * gq;   // first 16-column strip of this pass
+    for (int gq = 0; gq < npass; ++gq) {
+      const int s0 = sw + 4 * gq;   // first 16-column strip of this pass
       // the next pass's fragments (after the last pass: the first pass's, for the next query block)
-      FA_LOAD_WO(bn, (gq + 1) & 3)
+      if (npass > 1) {
+        FA_LOAD_WO(bn, (gq + 1) & (npass - 1))
+      }
 #pragma unroll 1
       for (int rb = 0; rb < nrb; ++rb) {
         uint4 a[2][NT];
@@ -532,10 +539,12 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
           }
         }
       }
+      if (npass > 1) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) b[cb][kk] = bn[cb][kk];
+          for (int kk = 0; kk < 2; ++kk) b[cb][kk] = bn[cb][kk];
+      }
     }
   }
 #undef FA_LOAD_WO
@@ -544,12 +553,14 @@ __global__ __launch_bounds__(256) void k_field_attn(const float* __restrict__ QK
 void launch_field_attn(hipStream_t st, const float* qkv_part, int nsplit, size_t stride, const float* bqkv,
                        const int* rec, int nrec, const bf16_t* Wo, float* P, size_t pstride, int nt) {
   if (nrec == 0) return;
+  // column parts: enough blocks to reach about one per compute unit
+  const int cs = nrec <= 4 ? 4 : nrec <= 8 ? 2 : 1;
   if (nt == 3)
-    hipLaunchKernelGGL(k_field_attn<3>, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo, P,
-                       pstride);
+    hipLaunchKernelGGL(k_field_attn<3>, dim3(nrec, 16, cs), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo,
+                       P, pstride);
   else
-    hipLaunchKernelGGL(k_field_attn<2>, dim3(nrec, 16), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo, P,
-                       pstride);
+    hipLaunchKernelGGL(k_field_attn<2>, dim3(nrec, 16, cs), dim3(256), 0, st, qkv_part, nsplit, stride, bqkv, rec, Wo,
+                       P, pstride);
 }
 
 }  // namespace clef
