@@ -39,8 +39,8 @@ constexpr int BM = 256, BN = 256;
 // tiles need no image: their fragment-order layouts let every lane store
 // whole 16-byte chunks straight from the accumulators, again 1 KB per wave
 // instruction.  Per-tile constants are loaded by thread tid when the kernel
-// starts, so their latency hides under the main loop, and parked in a small
-// LDS area behind the ring.
+// starts, so their latency hides under the main loop, held in registers, and
+// parked in a small LDS area at the ring's end once the main loop is over.
 constexpr int kConstFloats = 1024;
 
 struct EpiMem {          // transposed tiles; rows of out are the packed row space
@@ -430,48 +430,51 @@ DEV f32x16 mfma32(const u32x4 a, const u32x4 b, const f32x16 c) {
 // s_waitcnt lgkmcnt(0) only
 #define WAIT_LDS() __builtin_amdgcn_s_waitcnt((7 << 4) | 15 | (3 << 14))
 
-// Operand tiles live in a 2-stage LDS ring of 64-deep K steps; rows are 128 B
-// (eight 16-byte chunks) and chunk c of row r sits at position c ^ ((r >> 1) & 7),
+// Operand tiles are 64-deep K steps of 256 rows; rows are 128 B (eight
+// 16-byte chunks) and chunk c of row r sits at position c ^ ((r >> 1) & 7),
 // which keeps the fragment reads of 16 lanes on distinct banks.  Global -> LDS
 // copies use buffer_load_dwordx4 ... lds: lane l of a wave writes the l-th
 // 16-byte slot of a 1 KB block (8 rows), so each lane fetches the chunk that
-// belongs in its slot.  Whole 128-byte row segments per copy stream about twice as fast
-// into a CU as 64-byte ones.
+// belongs in its slot.  Whole 128-byte row segments per copy stream about
+// twice as fast into a CU as 64-byte ones.
 //
 // Per stage a wave runs four 16-deep substeps of 16 MFMAs, reading the next
-// substep's fragments while the current one multiplies.  The next stage is
-// copied during the first two substeps of the current one; one barrier per
-// stage hands it over and frees the slot just consumed.  Each substep is
+// substep's fragments while the current one multiplies.  Each substep is
 // written out as 8 fenced groups of (2 MFMAs, 1 fragment read, 1 copy): with
 // the copies spread between the MFMAs instead of issued 8 at a time, a copy
 // that cannot issue (operands missing in L2) stalls one group, not the
-// matrix core's whole queue (memory GEMM 234 -> 217 us, K/V GEMM 247 -> 236
-// us on the online-serving batch).
-template <class Epi>
-constexpr int lds_span() {
-  constexpr int kRingBytes = 2 * 2 * BM * 8 * 16;   // 2 stages x (A | B) x 256 rows x 128 B
-  return Epi::kImageBytes > kRingBytes ? Epi::kImageBytes : kRingBytes;
-}
+// matrix core's whole queue.
+//
+// Ring of five operand tiles of 32 KB (one operand of one stage: 256 rows x
+// 128 B), the whole 160 KB of LDS.  Tile q of the sequence A_0, W_0, A_1,
+// W_1, ... sits in slot q mod 5, so the A tile of stage s + 2 and the W tile
+// of stage s + 1 are in flight while stage s multiplies: 96 KB of copies
+// outstanding per CU instead of the 64 KB a two-stage ring allows, and the A
+// rows (the operand that misses in L2) get two stages to land.  The tile
+// constants wait in registers until the main loop is over and are then
+// parked at the ring's end (kCstOff), clear of the output image.
+constexpr int kHalfSlot = BM * 8;                  // u32x4 per operand tile
+constexpr int kLdsBytes = 5 * kHalfSlot * 16;      // 160 KB
+constexpr int kCstOff = kLdsBytes - kConstFloats * 4;
 
 // One output tile (or one K slice of it) in orientation TR (true: transposed,
-// the W rows are the MFMA A operand).  lds: the workgroup's operand ring, then
-// the tile constants.
+// the W rows are the MFMA A operand).  lds: the workgroup's operand ring.
 template <class Epi, bool TR>
 DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ W, int K, int nsplit, int ks,
                    int tn, const int4 T, const Epi& epi, unsigned char* lds) {
+  static_assert(Epi::kImageBytes <= kCstOff, "output image overlaps the parked constants");
   constexpr int KS = 64;
-  u32x4 (*smem)[2][BM * 8] = reinterpret_cast<u32x4 (*)[2][BM * 8]>(lds);
-  float* cst = reinterpret_cast<float*>(lds + lds_span<Epi>());
+  u32x4* ring = reinterpret_cast<u32x4*>(lds);
+  float* cst = reinterpret_cast<float*>(lds + kCstOff);
   const int kbase = ks * (K / nsplit);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;     // 2 x 2 waves, each 128 x 128
   // transposed tiles feed the W rows as the MFMA A operand: acc rows are then
   // output columns and acc columns are A rows
-  constexpr int ra_src = TR ? 1 : 0, rb_src = TR ? 0 : 1;
   const int wa = TR ? wn : wm, wb = TR ? wm : wn;
 
-  // copy sources: instruction i of wave w fills rows 8 (8 w + i) .. +8 of a stage.
+  // copy sources: instruction i of wave w fills rows 8 (8 w + i) .. +8 of a tile.
   // Buffer copies: a uniform resource per operand (its record count bounds every
   // copy to the tile's valid rows), a 32-bit byte offset per lane, the K position
   // as the scalar offset.
@@ -500,23 +503,26 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   // Block bases are multiples of 32 rows, so the swizzle depends on the lane only
   // and block i of a substep sits 256 chunks after block 0.
   const int l31 = lane & 31, hl = lane >> 5, fsw = (l31 >> 1) & 7;
-  const int fa0 = ra_src * (BM * 8) + (wa * 128 + l31) * 8;
-  const int fb0 = rb_src * (BM * 8) + (wb * 128 + l31) * 8;
-#define COPY_A(stage, k0)                                                                                      \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? aoffO : aoffE) + i * astep, ACOL(kbase + (k0)) * 2, 0, 0);
-#define COPY_B(stage, k0)                                                                                      \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                                \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + i)], 16,            \
-                                             ((i & 1) ? woffO : woffE) + i * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
-#define COPY_STAGE(stage, k0) COPY_A(stage, k0) COPY_B(stage, k0)
-#define LOAD_FRAGS(F, stage, kk)                                                 \
+  const int fa0 = (wa * 128 + l31) * 8, fb0 = (wb * 128 + l31) * 8;
+  // slot q holds the A tile of a stage, slot q + 1 (mod 5) its W tile; the
+  // MFMA A operand is the W tile in transposed tiles
+#define M5(x) ((x) >= 5 ? (x) - 5 : (x))
+#define BASE_A(q) ((TR ? M5((q) + 1) : (q)) * kHalfSlot + fa0)
+#define BASE_B(q) ((TR ? (q) : M5((q) + 1)) * kHalfSlot + fb0)
+#define CPA1(slot, k0, i)                                                                                   \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&ring[(slot) * kHalfSlot + 64 * (w * 8 + (i))], 16, \
+                                           (((i) & 1) ? aoffO : aoffE) + (i) * astep, ACOL(kbase + (k0)) * 2, 0, 0);
+#define CPB1(slot, k0, i)                                                                                   \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&ring[(slot) * kHalfSlot + 64 * (w * 8 + (i))], 16, \
+                                           (((i) & 1) ? woffO : woffE) + (i) * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
+#define COPY_A(slot, k0) _Pragma("unroll") for (int i = 0; i < 8; ++i) CPA1(slot, k0, i)
+#define COPY_B(slot, k0) _Pragma("unroll") for (int i = 0; i < 8; ++i) CPB1(slot, k0, i)
+#define LOAD_FRAGS(F, BA, BB, kk)                                                \
   {                                                                              \
-    const int ph_ = (2 * (kk) + hl) ^ fsw, sb_ = (stage) * (2 * BM * 8) + ph_;   \
+    const int ph_ = (2 * (kk) + hl) ^ fsw;                                       \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                              \
-      F##a[i] = smem[0][0][sb_ + fa0 + i * 256];                                 \
-      F##b[i] = smem[0][0][sb_ + fb0 + i * 256];                                 \
+      F##a[i] = ring[(BA) + ph_ + i * 256];                                      \
+      F##b[i] = ring[(BB) + ph_ + i * 256];                                      \
     }                                                                            \
   }
 #define MULTIPLY(F)                                                                       \
@@ -525,7 +531,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
     acc[mi][ni] = mfma32<Epi::kF16>(F##a[mi], F##b[ni], acc[mi][ni]);
 
   float kc[4];
-  epi.load_consts(T.y, tn * BN, tid, kc);   // consumed after the main loop
+  epi.load_consts(T.y, tn * BN, tid, kc);   // parked in LDS after the main loop
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -537,113 +543,113 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   u32x4 Xa[4], Xb[4], Ya[4], Yb[4];
 
   const int nk = K / nsplit / KS;        // >= 4 (K / nsplit a multiple of 128, at least 256)
-  COPY_STAGE(0, 0)
-  COPY_STAGE(1, KS)                      // nk >= 2: the second stage is in flight while the first is waited for
-  WAIT_VM(16);                           // the tile constants and the first stage have landed
+  // The prologue copies tiles A_0, W_0, A_1, W_1, A_2 and waits for the first
+  // two only.  Stage s runs four substeps; during the first it copies W_{s+1},
+  // during the second A_{s+2}, into the slots stage s - 1 freed.  The barrier
+  // before the fourth substep (whose fragments are already in registers) needs
+  // A_{s+1} and W_{s+1} landed and lets A_{s+2} stay in flight; it also frees
+  // stage s's slots.  Each substep is 8 fenced groups of (2 MFMAs of the
+  // current fragments, 1 fragment read for the next substep, 1 global->LDS copy
+  // in the first two substeps), so the compiler keeps the order.
+  COPY_A(0, 0)
+  COPY_B(1, 0)
+  COPY_A(2, KS)
+  COPY_B(3, KS)
+  COPY_A(4, 2 * KS)
+  WAIT_VM(24);                           // the tile constants, A_0 and W_0 have landed
   __builtin_amdgcn_s_barrier();
-  epi.put_consts(cst, tid, kc);          // visible to every wave after the main loop's barriers
-  LOAD_FRAGS(X, 0, 0)
-  // The prologue copies the first two stages and waits for the first only.
-  // Each stage runs four substeps; the barrier before the fourth hands the
-  // next stage over and frees the current stage's slot, into which the fourth
-  // substep already copies the A tile of the stage after next, while the B
-  // tile of the next stage is copied in the first substep.  So both operand
-  // copies get three to four substeps to land.  Needs nk >= 3 (the host keeps
-  // K / nsplit >= 256).  Each substep is 8 fenced groups of (2
-  // MFMAs of the current fragments, 1 fragment read for the next substep, 1
-  // global->LDS copy in the first two substeps), so the compiler keeps the
-  // order.  The last stage copies nothing.
+  LOAD_FRAGS(X, BASE_A(0), BASE_B(0), 0)
 #define MFMA2(F, t)                                                                         \
   acc[(t) >> 1][((t) & 1) * 2] =                                                            \
       mfma32<Epi::kF16>(F##a[(t) >> 1], F##b[((t) & 1) * 2], acc[(t) >> 1][((t) & 1) * 2]); \
   acc[(t) >> 1][((t) & 1) * 2 + 1] =                                                        \
       mfma32<Epi::kF16>(F##a[(t) >> 1], F##b[((t) & 1) * 2 + 1], acc[(t) >> 1][((t) & 1) * 2 + 1]);
-#define FRAG1(G, stage, kk, t)                                                                  \
+#define FRAG1(G, BA, BB, kk, t)                                                                 \
   {                                                                                             \
-    const int ph_ = (2 * (kk) + hl) ^ fsw, sb_ = (stage) * (2 * BM * 8) + ph_;                  \
-    if ((t) < 4) G##a[(t)] = smem[0][0][sb_ + fa0 + ((t) & 3) * 256];                           \
-    else G##b[(t) - 4] = smem[0][0][sb_ + fb0 + ((t) & 3) * 256];                               \
+    const int ph_ = (2 * (kk) + hl) ^ fsw;                                                      \
+    if ((t) < 4) G##a[(t)] = ring[(BA) + ph_ + ((t) & 3) * 256];                                \
+    else G##b[(t) - 4] = ring[(BB) + ph_ + ((t) & 3) * 256];                                    \
   }
-#define CPA1(stage, k0, i)                                                                      \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)&smem[stage][0][64 * (w * 8 + (i))], 16, \
-                                           (((i) & 1) ? aoffO : aoffE) + (i) * astep, ACOL(kbase + (k0)) * 2, 0, 0);
-#define CPB1(stage, k0, i)                                                                      \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)&smem[stage][1][64 * (w * 8 + (i))], 16, \
-                                           (((i) & 1) ? woffO : woffE) + (i) * wstep, WCOL(kbase + (k0)) * 2, 0, 0);
-#define HALF_CP(F, G, gst, gkk, CP, cst, ck0)                                                   \
+#define HALF_CP(F, G, BA, BB, gkk, CP, cslot, ck0)                                              \
   _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                               \
     MFMA2(F, t)                                                                                 \
-    FRAG1(G, gst, gkk, t)                                                                       \
-    CP(cst, ck0, t)                                                                             \
+    FRAG1(G, BA, BB, gkk, t)                                                                    \
+    CP(cslot, ck0, t)                                                                           \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
-#define HALF(F, G, gst, gkk)                                                                    \
+#define HALF(F, G, BA, BB, gkk)                                                                 \
   _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                               \
     MFMA2(F, t)                                                                                 \
-    FRAG1(G, gst, gkk, t)                                                                       \
+    FRAG1(G, BA, BB, gkk, t)                                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                          \
   }
   {
+    // stage 0: its copies were all issued by the prologue
+    const int ba = BASE_A(0), bb = BASE_B(0);
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, 0, 1)
+    HALF(X, Y, ba, bb, 1)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, 0, 2)
+    HALF(Y, X, ba, bb, 2)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, 0, 3)
+    HALF(X, Y, ba, bb, 3)
     WAIT_LDS();
-    WAIT_VM(0);
+    WAIT_VM(8);                          // A_1, W_1 landed; A_2 may be in flight
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(Y, X, 1, 0, CPA1, 0, 2 * KS)
+    HALF(Y, X, BASE_A(2), BASE_B(2), 0)
   }
+  int q = 2;                             // slot of stage kt's A tile: 2 kt mod 5
   for (int kt = 1; kt + 2 < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
+    const int ba = BASE_A(q), bb = BASE_B(q), qn = M5(q + 2);
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(X, Y, cur, 1, CPB1, nxt, (kt + 1) * KS)
+    HALF_CP(X, Y, ba, bb, 1, CPB1, M5(q + 3), (kt + 1) * KS)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, cur, 2)
+    HALF_CP(Y, X, ba, bb, 2, CPA1, M5(q + 4), (kt + 2) * KS)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, cur, 3)
+    HALF(X, Y, ba, bb, 3)
+    WAIT_LDS();
+    WAIT_VM(8);                          // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(Y, X, BASE_A(qn), BASE_B(qn), 0)
+    q = qn;
+  }
+  {
+    // stage nk - 2: copies the last W tile only
+    const int ba = BASE_A(q), bb = BASE_B(q), qn = M5(q + 2);
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF_CP(X, Y, ba, bb, 1, CPB1, M5(q + 3), (nk - 1) * KS)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(Y, X, ba, bb, 2)
+    WAIT_LDS();
+    __builtin_amdgcn_sched_barrier(0);
+    HALF(X, Y, ba, bb, 3)
     WAIT_LDS();
     WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(Y, X, nxt, 0, CPA1, cur, (kt + 2) * KS)
+    HALF(Y, X, BASE_A(qn), BASE_B(qn), 0)
+    q = qn;
   }
   {
-    const int kt = nk - 2, cur = kt & 1, nxt = cur ^ 1;
+    const int ba = BASE_A(q), bb = BASE_B(q);
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF_CP(X, Y, cur, 1, CPB1, nxt, (kt + 1) * KS)
+    HALF(X, Y, ba, bb, 1)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, cur, 2)
+    HALF(Y, X, ba, bb, 2)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, cur, 3)
-    WAIT_LDS();
-    WAIT_VM(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, nxt, 0)
-  }
-  {
-    const int cur = (nk - 1) & 1;
-    WAIT_LDS();
-    __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, cur, 1)
-    WAIT_LDS();
-    __builtin_amdgcn_sched_barrier(0);
-    HALF(Y, X, cur, 2)
-    WAIT_LDS();
-    __builtin_amdgcn_sched_barrier(0);
-    HALF(X, Y, cur, 3)
+    HALF(X, Y, ba, bb, 3)
     WAIT_LDS();
     __builtin_amdgcn_sched_barrier(0);
     MULTIPLY(Y)
@@ -651,13 +657,15 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   }
 #undef WCOL
 #undef ACOL
+#undef M5
+#undef BASE_A
+#undef BASE_B
 #undef MFMA2
 #undef FRAG1
 #undef CPA1
 #undef CPB1
 #undef HALF_CP
 #undef HALF
-#undef COPY_STAGE
 #undef COPY_A
 #undef COPY_B
 #undef LOAD_FRAGS
@@ -667,14 +675,18 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   // (finite) inputs and keep the padded part of the row space finite.
   if constexpr (Epi::kDirect) {
     epi.store_acc(acc, T.y + wb * 128, tn * BN + wa * 128, ks, lane);
-  } else if constexpr (Epi::kRegs) {
-    epi.template store_regs<TR>(acc, cst, T.y, tn * BN, wa * 128, wb * 128, lane);
   } else {
-    bf16_t* img = reinterpret_cast<bf16_t*>(lds);
     __syncthreads();                     // every wave is done with the operand ring
-    epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
+    epi.put_consts(cst, tid, kc);
     __syncthreads();
-    epi.store(img, T.y, tn * BN, tid);
+    if constexpr (Epi::kRegs) {
+      epi.template store_regs<TR>(acc, cst, T.y, tn * BN, wa * 128, wb * 128, lane);
+    } else {
+      bf16_t* img = reinterpret_cast<bf16_t*>(lds);
+      epi.stage_t(acc, cst, img, wb * 128, wa * 128, lane);
+      __syncthreads();
+      epi.store(img, T.y, tn * BN, tid);
+    }
   }
 }
 
@@ -682,9 +694,9 @@ template <class Epi>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm256(const bf16_t* __restrict__ A, int lda, const int4* __restrict__ tiles, int ntile_n,
                const bf16_t* __restrict__ W, int K, int nsplit, Epi epi) {
-  // operand ring [stage][A|B][row * 8 + swizzled chunk] (after the main loop the
-  // same bytes may hold the output image), then the tile constants
-  __shared__ __attribute__((aligned(16))) unsigned char lds[lds_span<Epi>() + kConstFloats * 4];
+  // operand ring: five tiles [row * 8 + swizzled chunk] (after the main loop
+  // the same bytes hold the output image and the tile constants)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   // nsplit > 1: workgroup b multiplies K slice b / (tiles) of length K / nsplit
   const int ntiles_mn = gridDim.x / nsplit;
   const int ks = blockIdx.x / ntiles_mn;
