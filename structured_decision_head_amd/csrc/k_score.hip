@@ -99,12 +99,17 @@ void launch_field_agg(hipStream_t st, const float* U, const int* o_off, const fl
                      fstats, eps);
 }
 
-// One block (8 waves) per question; one option per wave.  The hidden layer
-// GELU(W1 z + b1) of option k is formed here from the split-K slices of W1 z
-// (hpart, nsplit slices hstride floats apart, rows of 1024; unused when
-// joint == 0).  Softmax and first-index argmax run over the whole block.
-// jcos / mlp may be null.
-__global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, const float* __restrict__ F,
+// One block (16 waves) per question.  Each option's 1024 dims are split in
+// four quarters (a lane's float4 c = quarter c), and the waves take the
+// (option, quarter) pairs in turn, so that a question's few options still
+// spread over all its waves.  The hidden layer GELU(W1 z + b1) is formed here
+// from the split-K slices of W1 z (hpart, nsplit slices hstride floats apart,
+// rows of 1024; unused when joint == 0); each wave leaves its quarter's three
+// partial dot products (u.f, u.u, w2.h) in LDS and one thread per option adds
+// the four quarters in order.  Softmax and first-index argmax run over the
+// whole block.  jcos / mlp may be null.
+constexpr int kSW = 16, kST = kSW * 64;
+__global__ __launch_bounds__(kST) void k_score(const float* __restrict__ U, const float* __restrict__ F,
                                                const float* __restrict__ hpart, int nsplit, size_t hstride,
                                                const float* __restrict__ b1, const float* __restrict__ w2, float b2,
                                                const float* __restrict__ prior, float gate, float lam, int joint,
@@ -112,52 +117,54 @@ __global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, cons
                                                float* __restrict__ probs, int* __restrict__ amax,
                                                float* __restrict__ jcos, float* __restrict__ mlp,
                                                const int* __restrict__ q_type, AnswerOut ans) {
-  __shared__ float sm[kQW];
-  __shared__ int si[kQW];
+  __shared__ float sm[kSW];
+  __shared__ int si[kSW];
   __shared__ float sl[kMaxOptions];
+  __shared__ float sp[kMaxOptions][4][3];   // per option and quarter: u.f, u.u, w2.h
   const int q = blockIdx.x;
   const int o0 = o_off[q], no = o_off[q + 1] - o0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (joint) {
-    float4 f[4], wv[4];
     float ff = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      f[c] = ld4(F + (size_t)q * 1024 + el(lane, c));
-      wv[c] = ld4(w2 + el(lane, c));
-      ff += dot4(f[c], f[c]);
+      const float4 f = ld4(F + (size_t)q * 1024 + el(lane, c));
+      ff += dot4(f, f);
     }
     ff = wave_sum(ff);
-    for (int k = w; k < no; k += kQW) {
+    for (int i = w; i < 4 * no; i += kSW) {
+      const int k = i >> 2, c = i & 3;
       const size_t row = (size_t)(o0 + k) * 1024;
-      float uf = 0.f, uu = 0.f, r = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 u = ld4(U + row + el(lane, c));
-        float4 h = sum_slices4(hpart + row + el(lane, c), nsplit, hstride, b1 + el(lane, c));
-        h.x = gelu_erf(h.x); h.y = gelu_erf(h.y); h.z = gelu_erf(h.z); h.w = gelu_erf(h.w);
-        uf += dot4(u, f[c]);
-        uu += dot4(u, u);
-        r += dot4(wv[c], h);
-      }
-      uf = wave_sum(uf);
-      uu = wave_sum(uu);
-      r = wave_sum(r) + b2;
+      const float4 f = ld4(F + (size_t)q * 1024 + el(lane, c));
+      const float4 wv = ld4(w2 + el(lane, c));
+      const float4 u = ld4(U + row + el(lane, c));
+      float4 h = sum_slices4(hpart + row + el(lane, c), nsplit, hstride, b1 + el(lane, c));
+      h.x = gelu_erf(h.x); h.y = gelu_erf(h.y); h.z = gelu_erf(h.z); h.w = gelu_erf(h.w);
+      const float uf = wave_sum(dot4(u, f)), uu = wave_sum(dot4(u, u)), r = wave_sum(dot4(wv, h));
       if (lane == 0) {
-        const float cs = uf / (fmaxf(sqrtf(uu), 1e-8f) * fmaxf(sqrtf(ff), 1e-8f));
-        sl[k] = prior[o0 + k] + gate * (lam * cs + r);
-        if (jcos) jcos[o0 + k] = cs;
-        if (mlp) mlp[o0 + k] = r;
+        sp[k][c][0] = uf;
+        sp[k][c][1] = uu;
+        sp[k][c][2] = r;
       }
     }
+    __syncthreads();
+    for (int k = threadIdx.x; k < no; k += kST) {
+      const float uf = ((sp[k][0][0] + sp[k][1][0]) + sp[k][2][0]) + sp[k][3][0];
+      const float uu = ((sp[k][0][1] + sp[k][1][1]) + sp[k][2][1]) + sp[k][3][1];
+      const float r = (((sp[k][0][2] + sp[k][1][2]) + sp[k][2][2]) + sp[k][3][2]) + b2;
+      const float cs = uf / (fmaxf(sqrtf(uu), 1e-8f) * fmaxf(sqrtf(ff), 1e-8f));
+      sl[k] = prior[o0 + k] + gate * (lam * cs + r);
+      if (jcos) jcos[o0 + k] = cs;
+      if (mlp) mlp[o0 + k] = r;
+    }
   } else {
-    for (int k = threadIdx.x; k < no; k += kQT) sl[k] = prior[o0 + k];
+    for (int k = threadIdx.x; k < no; k += kST) sl[k] = prior[o0 + k];
   }
   __syncthreads();
   // first maximal index: larger value wins, ties go to the smaller index
   float m = -INFINITY;
   int best = 0x7fffffff;
-  for (int k = threadIdx.x; k < no; k += kQT)
+  for (int k = threadIdx.x; k < no; k += kST)
     if (sl[k] > m) { m = sl[k]; best = k; }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -170,14 +177,14 @@ __global__ __launch_bounds__(kQT) void k_score(const float* __restrict__ U, cons
   m = sm[0];
   best = si[0];
 #pragma unroll
-  for (int i = 1; i < kQW; ++i)
+  for (int i = 1; i < kSW; ++i)
     if (sm[i] > m || (sm[i] == m && si[i] < best)) { m = sm[i]; best = si[i]; }
   __syncthreads();
   float z = 0.f;
-  for (int k = threadIdx.x; k < no; k += kQT) z += expf(sl[k] - m);
-  z = block_sum<kQW>(z, sm);
+  for (int k = threadIdx.x; k < no; k += kST) z += expf(sl[k] - m);
+  z = block_sum<kSW>(z, sm);
   if (best == 0x7fffffff) best = 0;   // no comparable value: index 0
-  for (int k = threadIdx.x; k < no; k += kQT) {
+  for (int k = threadIdx.x; k < no; k += kST) {
     const float p = expf(sl[k] - m) / z;
     logits[o0 + k] = sl[k];
     probs[o0 + k] = p;
@@ -211,7 +218,7 @@ void launch_score(hipStream_t st, const float* U, const float* F, const float* h
                   const int* o_off, int NQ, float* logits, float* probs, int* amax, float* jcos, float* mlp,
                   const int* q_type, const AnswerOut& ans) {
   if (NQ == 0) return;
-  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(kQT), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
+  hipLaunchKernelGGL(k_score, dim3(NQ), dim3(kST), 0, st, U, F, hpart, nsplit, hstride, b1, w2, b2, prior, gate, lam,
                      joint, o_off, logits, probs, amax, jcos, mlp, q_type, ans);
 }
 
