@@ -51,6 +51,7 @@ struct EpiMem {          // transposed tiles; rows of out are the packed row spa
   static constexpr bool kF16 = false;                  // operands bf16
   static constexpr bool kDirect = false;               // output staged through LDS
   static constexpr bool kRegs = false;
+  static constexpr bool kBiasInit = false;
   static constexpr bool kPlain = false;                // every tile transposed
   static constexpr int kWrapW = 0;
   static constexpr int kLd = 264;                      // image row pitch (bf16): 512 B + 16 B
@@ -125,6 +126,7 @@ struct EpiKV {
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;                  // stored from the accumulators
+  static constexpr bool kBiasInit = true;              // accumulators start at the bias
   static constexpr bool kPlain = true;                 // V tiles are plain
   static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
@@ -134,8 +136,43 @@ struct EpiKV {
     const int r = col >> 11, isv = (col >> 10) & 1, h = (col >> 6) & 15;
     return kv + ((size_t)(2 * r + isv) * 16 + h) * (size_t)Tpad * 64;
   }
-  DEV void load_consts(int, int ocol0, int tid, float (&r)[4]) const { r[0] = bias[ocol0 + tid]; }
-  DEV void put_consts(float* cst, int tid, const float (&r)[4]) const { cst[tid] = r[0]; }
+  DEV void load_consts(int, int, int, float (&)[4]) const {}
+  DEV void put_consts(float*, int, const float (&)[4]) const {}
+  // The accumulators start at the bias of their output column, so the
+  // epilogue only converts and stores (accumulator layout as in store_regs):
+  // bias_regs loads the values a lane needs when the tile starts (TR tiles
+  // bq[mi][g] = columns ra0 + 32 mi + 8 g + 4 (l / 32) .. + 3; plain tiles
+  // bq[ni][0].x = column rb0 + 32 ni + l % 32), fill_acc writes them once the
+  // prologue's copies are in flight.
+  template <bool TR>
+  DEV void bias_regs(float4 (&bq)[4][4], int ocol0, int ra0, int rb0, int lane) const {
+    if constexpr (TR) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bq[mi][g] = *reinterpret_cast<const float4*>(bias + ocol0 + ra0 + mi * 32 + 8 * g + 4 * (lane >> 5));
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) bq[ni][0].x = bias[ocol0 + rb0 + ni * 32 + (lane & 31)];
+    }
+  }
+  template <bool TR>
+  DEV void fill_acc(f32x16 (&acc)[4][4], const float4 (&bq)[4][4]) const {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if constexpr (TR) {
+            const float4 b = bq[mi][e >> 2];
+            acc[mi][ni][e] = (e & 3) == 0 ? b.x : (e & 3) == 1 ? b.y : (e & 3) == 2 ? b.z : b.w;
+          } else {
+            acc[mi][ni][e] = bq[ni][0].x;
+          }
+        }
+  }
   // Every store instruction of a wave writes one contiguous 1 KB run (64
   // consecutive 16-byte chunks of a 32-row block), with the non-temporal hint:
   // K and V are read once per routing layer, so they need not sit dirty in
@@ -156,15 +193,11 @@ struct EpiKV {
   template <bool TR>
   DEV void store_regs(const f32x16 (&acc)[4][4], const float* cst, int orow0, int ocol0, int ra0, int rb0,
                       int lane) const {
-    const int hh = lane >> 5;
     if constexpr (TR) {
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int lcb = ra0 + mi * 32;
         bf16_t* hb = head_base(ocol0 + lcb) + (size_t)(64 * 2 * (mi & 1) + lane) * 8;
-        float4 b[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) b[g] = *reinterpret_cast<const float4*>(cst + lcb + 8 * g + 4 * hh);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const f32x16& a = acc[mi][ni];
@@ -172,10 +205,10 @@ struct EpiKV {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const int g0 = 2 * p, g1 = 2 * p + 1;
-            const uint32_t p0 = pack_bf16x2(a[4 * g0] + b[g0].x, a[4 * g0 + 1] + b[g0].y);
-            const uint32_t p1 = pack_bf16x2(a[4 * g0 + 2] + b[g0].z, a[4 * g0 + 3] + b[g0].w);
-            const uint32_t q0 = pack_bf16x2(a[4 * g1] + b[g1].x, a[4 * g1 + 1] + b[g1].y);
-            const uint32_t q1 = pack_bf16x2(a[4 * g1 + 2] + b[g1].z, a[4 * g1 + 3] + b[g1].w);
+            const uint32_t p0 = pack_bf16x2(a[4 * g0], a[4 * g0 + 1]);
+            const uint32_t p1 = pack_bf16x2(a[4 * g0 + 2], a[4 * g0 + 3]);
+            const uint32_t q0 = pack_bf16x2(a[4 * g1], a[4 * g1 + 1]);
+            const uint32_t q1 = pack_bf16x2(a[4 * g1 + 2], a[4 * g1 + 3]);
             const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
             store_stream(blk + p * 512, u32x4{s0[0], s1[0], s0[1], s1[1]});
@@ -186,7 +219,6 @@ struct EpiKV {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         const int lc = rb0 + ni * 32 + (lane & 31);
-        const float b = cst[lc];
         bf16_t* hb = head_base(ocol0 + rb0 + ni * 32) + (size_t)(64 * ((lc >> 5) & 1) + lane) * 8;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -195,9 +227,8 @@ struct EpiKV {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int e = 8 * q;
-            store_stream(blk + q * 1024,
-                         u32x4{pack_bf16x2(a[e] + b, a[e + 1] + b), pack_bf16x2(a[e + 2] + b, a[e + 3] + b),
-                               pack_bf16x2(a[e + 4] + b, a[e + 5] + b), pack_bf16x2(a[e + 6] + b, a[e + 7] + b)});
+            store_stream(blk + q * 1024, u32x4{pack_bf16x2(a[e], a[e + 1]), pack_bf16x2(a[e + 2], a[e + 3]),
+                                               pack_bf16x2(a[e + 4], a[e + 5]), pack_bf16x2(a[e + 6], a[e + 7])});
           }
         }
       }
@@ -240,6 +271,7 @@ struct EpiMem32 {
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
+  static constexpr bool kBiasInit = false;
   static constexpr bool kPlain = false;
   static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
@@ -313,6 +345,7 @@ struct EpiKV32 {
   static constexpr bool kF16 = false;
   static constexpr bool kDirect = false;
   static constexpr bool kRegs = true;
+  static constexpr bool kBiasInit = false;
   static constexpr bool kPlain = true;   // V tiles are plain
   static constexpr int kWrapW = 1024;    // one [N][1024] weight read three times: its 2 MB column group stays in L2
   static constexpr int kImageBytes = 0;
@@ -372,6 +405,7 @@ struct EpiPart {
   static constexpr bool kF16 = F16;
   static constexpr bool kDirect = true;
   static constexpr bool kRegs = false;
+  static constexpr bool kBiasInit = false;
   static constexpr bool kPlain = false;
   static constexpr int kWrapW = 0;
   static constexpr int kImageBytes = 0;
@@ -534,12 +568,17 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   epi.load_consts(T.y, tn * BN, tid, kc);   // parked in LDS after the main loop
 
   f32x16 acc[4][4];
+  float4 bq[4][4];                       // bias of the lane's accumulators (bias-initialized epilogues)
+  if constexpr (Epi::kBiasInit) {
+    epi.template bias_regs<TR>(bq, tn * BN, wa * 128, wb * 128, lane);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  }
   u32x4 Xa[4], Xb[4], Ya[4], Yb[4];
 
   const int nk = K / nsplit / KS;        // >= 4 (K / nsplit a multiple of 128, at least 256)
@@ -557,6 +596,7 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   COPY_B(3, KS)
   COPY_A(4, 2 * KS)
   WAIT_VM(24);                           // the tile constants, A_0 and W_0 have landed
+  if constexpr (Epi::kBiasInit) epi.template fill_acc<TR>(acc, bq);
   __builtin_amdgcn_s_barrier();
   LOAD_FRAGS(X, BASE_A(0), BASE_B(0), 0)
 #define MFMA2(F, t)                                                                         \
@@ -675,6 +715,8 @@ DEV void gemm_tile(const bf16_t* __restrict__ A, int lda, const bf16_t* __restri
   // (finite) inputs and keep the padded part of the row space finite.
   if constexpr (Epi::kDirect) {
     epi.store_acc(acc, T.y + wb * 128, tn * BN + wa * 128, ks, lane);
+  } else if constexpr (Epi::kBiasInit) {
+    epi.template store_regs<TR>(acc, cst, T.y, tn * BN, wa * 128, wb * 128, lane);
   } else {
     __syncthreads();                     // every wave is done with the operand ring
     epi.put_consts(cst, tid, kc);
